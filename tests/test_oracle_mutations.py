@@ -1,0 +1,88 @@
+"""Planted mistakes in the oracle (CPU only): each must make one of its pins fail.
+
+A pin that passes whatever the oracle does pins nothing; these tests patch a
+plausible mistake into one oracle step and check that the pin covering that
+step catches it.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention, pool
+from tests import test_oracle_attention as ta
+from tests import test_oracle_pool as tp
+
+_orig_gather = attention.gather
+
+
+def _wrong_head(cache, table_row, length, kv_head, dtype):
+    return _orig_gather(cache, table_row, length, (kv_head + 1) % cache.shape[1], dtype)
+
+
+def _wrong_row(cache, table_row, length, kv_head, dtype):
+    pos = np.arange(int(length))
+    blocks = np.asarray(table_row, dtype=np.int64)[pos // 16]
+    return attention.to_f64(cache[blocks, kv_head, (pos + 1) % 16, :], dtype)
+
+
+def _wrong_sign(q_h, K, scale):
+    x = -scale * (K @ q_h)
+    w = np.exp(x - x.max())
+    return w / w.sum()
+
+
+def _transposed(q_h, K, scale):
+    x = scale * (K[:, ::-1] @ q_h)  # operand read along the wrong axis order
+    w = np.exp(x - x.max())
+    return w / w.sum()
+
+
+def _merge_drops_rescale(parts):
+    M = max(m for m, _, _ in parts)
+    num = sum(np.exp(m - M) * acc for m, _, acc in parts)
+    den = sum(l for _, l, _ in parts)
+    return num / den
+
+
+@pytest.mark.parametrize("target,name,bad,pin", [
+    (attention, "gather", _wrong_head,
+     lambda: ta.test_paged_decode_equals_brute_force_on_contiguous_sequences("f32")),
+    (attention, "gather", _wrong_head, ta.test_constant_values_per_kv_head_pin_the_grouping),
+    (attention, "gather", _wrong_row, ta.test_needle_key_pins_the_gather),
+    (attention, "gather", _wrong_row, ta.test_paged_decode_matches_torch_sdpa_float64),
+    (attention, "softmax_weights", _wrong_sign,
+     lambda: ta.test_paged_decode_equals_brute_force_on_contiguous_sequences("bf16")),
+    (attention, "softmax_weights", _transposed, ta.test_paged_decode_matches_torch_sdpa_float64),
+    (attention, "merge", _merge_drops_rescale, lambda: ta.test_split_merge_equals_unsplit(512)),
+], ids=["head", "head-const", "row-needle", "row-sdpa", "sign", "transpose", "merge"])
+def test_planted_attention_mistake_is_caught(monkeypatch, target, name, bad, pin):
+    monkeypatch.setattr(target, name, bad)
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_planted_fifo_reuse_is_caught(monkeypatch):
+    def fifo_free(self, b):
+        b = self._check(b)
+        self.refcount[b] -= 1
+        if self.refcount[b] == 0:
+            self.free_stack.insert(0, b)  # bottom of the stack: handed out last
+    monkeypatch.setattr(pool.BlockPool, "free", fifo_free)
+    with pytest.raises(AssertionError):
+        tp.test_free_order_and_lifo_reuse()
+
+
+def test_planted_cow_without_release_is_caught(monkeypatch):
+    orig = pool.BlockPool.free
+    calls = {"n": 0}
+
+    def leaky_free(self, b):
+        # forget to drop the source's reference during copy-on-write
+        import inspect
+        if inspect.stack()[1].function == "append":
+            calls["n"] += 1
+            return
+        orig(self, b)
+    monkeypatch.setattr(pool.BlockPool, "free", leaky_free)
+    with pytest.raises(AssertionError):
+        tp.test_copy_on_write_first_writers_copy_last_writes_in_place()
+    assert calls["n"] > 0
