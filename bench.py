@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Paged-KV decode benchmark on one MI355X.
+
+A step is one pass of the whole hot path over one batch: copy-on-write block
+copies (when the workload has any), reshape_and_cache of the step's new tokens
+and paged_attention_decode (main pass + merge pass of split sequences).  The
+default workload is the Llama-3-70B-layer-shaped mixed-length batch (256
+sequences, lognormal lengths with median 300 clipped to [16, 8192], 64 query /
+8 KV heads, head_dim 128, bf16).  Inputs are resident in HBM before timing.
+Several independent copies of the KV pool (same tables) are used round-robin
+so that reads come from HBM, not from the 256 MB last-level cache.
+
+Prints one JSON line.  `value` is the step's algorithmic bytes over its wall
+time (GB/s); `roofline` is the decode main pass alone, timed with HIP events
+on its own stream; `cpu_baseline` is the oracle on a bounded sample of the same
+batch on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode achieved HBM GB/s (% of peak); attended KV tokens/s"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc", "pa_decode.hip")
+
+
+def decode_bytes(w):
+    """Algorithmic bytes of one decode call: every cached K and V element of every
+    (sequence, KV head) once, q and out once, table entries in use and lengths."""
+    import numpy as np
+    lens = np.asarray(w.context_lens, dtype=np.int64)
+    e = w.elem_bytes
+    kv = int(lens.sum()) * 2 * w.num_kv_heads * w.head_dim * e
+    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * e
+    tables = 4 * int((-(-lens // 16)).sum())
+    return kv + qo + tables + 4 * w.num_seqs
+
+
+def step_bytes(w, db):
+    """decode bytes + the step's token writes (read + write + slots) + block copies."""
+    B = db.phases[2]
+    e = w.elem_bytes
+    t = B.slots.shape[0]
+    writes = 2 * (2 * t * w.num_kv_heads * w.head_dim * e) + 8 * t
+    block = w.num_kv_heads * 16 * w.head_dim * e
+    copies = B.pairs.shape[0] * 2 * (2 * block) + 16 * B.pairs.shape[0]
+    return decode_bytes(w) + writes + copies
+
+
+def source_hash():
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """Counter-measured HBM bytes per decode launch, if taken on the current kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle (fp64 NumPy) on the first sequences of the batch, ~budget_s of work."""
+    import numpy as np
+    from oracle import attention
+    from oracle.numerics import to_f64
+    from threadpoolctl import threadpool_limits
+    limiter = threadpool_limits(1)  # the oracle is a single-threaded loop; keep BLAS at 1
+    threads = 1
+    q = to_f64(w.q, w.dtype)
+    group = w.num_q_heads // w.num_kv_heads
+    e = w.elem_bytes
+    done_tokens, done_bytes, seqs = 0, 0, 0
+    t0 = time.perf_counter()
+    for s in range(w.num_seqs):
+        kb, vb = w.sequence_kv(s)
+        K, V = to_f64(kb, w.dtype), to_f64(vb, w.dtype)
+        for g in range(w.num_kv_heads):
+            for h in range(g * group, (g + 1) * group):
+                attention.attend(q[s, h], K[:, g], V[:, g], w.scale)
+        n = int(w.context_lens[s])
+        done_tokens += n
+        done_bytes += n * 2 * w.num_kv_heads * w.head_dim * e + 2 * w.num_q_heads * w.head_dim * e
+        seqs += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    limiter.restore_original_limits()
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "tokens_per_s": round(done_tokens / dt, 1),
+            "sample": f"first {seqs} of {w.num_seqs} sequences ({done_tokens} attended tokens), "
+                      f"oracle decode (fp64 NumPy gather + softmax attention), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="3", help="workload 1..5 or 4b (default 3)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="KV pool copies used round-robin (default: enough for >= 1.5 GB)")
+    ap.add_argument("--partition", type=int, default=-1, help="-1 auto, 0 none, else tokens")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import paged_kv_cache_06_amd as pa
+    if not os.path.exists(pa.lib_path()):
+        from paged_kv_cache_06_amd import _build
+        _build.build()
+    import workloads
+    from paged_kv_cache_06_amd import runner
+
+    t_setup = time.perf_counter()
+    w = workloads.make(args.config)
+    pool_bytes = 2 * (w.num_blocks + 1) * w.num_kv_heads * 16 * w.head_dim * w.elem_bytes
+    copies = args.copies or max(1, int(np.ceil(1.5e9 / pool_bytes)))
+    db = runner.DeviceBatch(w, copies=copies)
+    db.prefill()
+    torch.cuda.synchronize()
+    print(f"# setup {time.perf_counter() - t_setup:.1f} s: workload {w.name}, "
+          f"{int(np.sum(w.context_lens))} tokens, {copies} pool copies", file=sys.stderr,
+          flush=True)
+
+    for i in range(args.warmup):
+        db.step(copy=i % copies, partition_size=args.partition)
+    torch.cuda.synchronize()
+
+    pa.timing_begin(8 * args.steps + 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        db.step(copy=i % copies, partition_size=args.partition)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = pa.timing_end()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    sbytes = step_bytes(w, db)
+    dbytes = decode_bytes(w)
+    tokens = int(np.sum(w.context_lens))
+    dec = kt["decode"]
+    dec_ms = dec["ms"] / max(1, dec["launches"])
+    achieved = dbytes / (dec_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.name)
+    ps = args.partition if args.partition != -1 else pa.decode_auto_partition(
+        w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, db.max_context_len,
+        {"f32": 0, "f16": 1, "bf16": 2}[w.dtype])
+    result = {
+        "metric": METRIC,
+        "value": round(sbytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
+                   "attended_tokens": tokens, "max_context_len": db.max_context_len,
+                   "partition_size": ps, "kv_pool_copies": copies, "parallelism": "none"},
+        "pct_of_hbm_peak": round(100 * sbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "kernels_ms_per_step": {k: round(v["ms"] / max(1, v["launches"]), 5)
+                                for k, v in kt.items() if v["launches"]},
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel" if w.dtype != "f32"
+                     else "decode_generic_kernel",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": dbytes,
+                     "avg_launch_ms": round(dec_ms, 5),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

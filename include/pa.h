@@ -1,0 +1,234 @@
+/*
+ * pa.h -- C ABI of the paged KV-cache decode library for AMD MI355X (gfx950).
+ *
+ * The KV cache of every sequence lives in fixed blocks of 16 token slots that
+ * sit anywhere in one pool; a per-sequence block table maps the sequence's
+ * logical blocks to physical ones, a block is taken only when the sequence
+ * needs it and returns to the pool when released, and blocks of a common
+ * prompt are shared by reference count and copied when one sharer writes
+ * ("PagedAttention for the professional: how vLLM serves 2.7x more requests on
+ * the same H100", sections "Beginner's example: library shelves" and "The
+ * scientific explanation"; "KV Cache and PagedAttention: why your LLM server
+ * slows down", sections "How PagedAttention fixes this" and "How does
+ * PagedAttention work?").  Each decode step attends one new query per head
+ * against the cached K/V of its sequence under grouped-query attention ("KV
+ * Cache for the intermediate: why long context eats the GPU and how to cut it
+ * 4x", sections "Precise scientific definition" and "Grouped Query Attention").
+ *
+ * Conventions
+ *   - Every call returns pa_status: 0 = PA_OK, negative = error.  Nothing
+ *     throws across this boundary.
+ *   - Pool calls are host-only and touch no device memory.  A pool is not
+ *     thread-safe; one thread owns it.
+ *   - Device calls take device pointers owned by the caller and enqueue work on
+ *     `stream` (a hipStream_t; NULL = the default stream).  They return as soon
+ *     as the work is queued.  Arguments are checked on the host before anything
+ *     is launched; an argument error launches nothing.  PA_ERR_DEVICE reports a
+ *     launch failure.
+ *   - q, caches and out share one dtype.  All arithmetic accumulates in fp32.
+ *
+ * Cache layout (per cache tensor, `num_blocks` blocks of Hkv * 16 * D elements):
+ *   K: [num_blocks][Hkv][D / X][16][X], X = 16 / element bytes (8 for bf16 and
+ *      fp16, 4 for fp32): token row r, dimension d of block b, head h is at
+ *      ((b * Hkv + h) * (D / X) + d / X) * 16 * X + r * X + d % X.
+ *   V: [num_blocks][Hkv][D][16]: at ((b * Hkv + h) * D + d) * 16 + r.
+ *   Slot s is row s % 16 of block s / 16.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+#define PA_OK 0
+#define PA_ERR_INVALID_ARG (-1)   /* bad shape, pointer, position or size */
+#define PA_ERR_OUT_OF_BLOCKS (-2) /* the pool cannot serve the request; nothing changed */
+#define PA_ERR_BAD_BLOCK (-3)     /* block id out of range or not held */
+#define PA_ERR_UNSUPPORTED (-4)   /* valid request this build does not implement */
+#define PA_ERR_DEVICE (-5)        /* HIP launch or runtime error */
+#define PA_ERR_WORKSPACE (-6)     /* workspace missing or too small */
+
+/* Storage dtype of q, the caches and out. */
+typedef int32_t pa_dtype;
+#define PA_F32 0
+#define PA_F16 1
+#define PA_BF16 2
+
+#define PA_BLOCK_SIZE 16
+
+/* partition_size values of pa_paged_attention_decode besides a positive
+ * multiple of 16 */
+#define PA_PARTITION_NONE 0   /* one pass over the whole sequence, no workspace */
+#define PA_PARTITION_AUTO (-1) /* the library picks */
+
+/* Short English text of a status code (static storage). */
+const char* pa_status_string(pa_status status);
+
+/* ---------------------------------------------------------------------------
+ * Block pool (host).  Holds block ids and reference counts only -- never device
+ * memory: the caller owns the cache tensors the ids index.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_pool pa_pool;
+
+typedef struct {
+  int32_t num_blocks;
+  int32_t num_free;   /* reference count 0 */
+  int32_t num_used;   /* reference count >= 1 */
+  int32_t num_shared; /* reference count >= 2 */
+  int64_t copies;     /* copy-on-write pairs emitted so far */
+} pa_pool_stats_t;
+
+/* New pool of `num_blocks` blocks.  `free_order` (NULL = 0, 1, 2, ...) is a
+ * permutation of [0, num_blocks): the first allocation returns free_order[0],
+ * the next free_order[1], and so on.  A block whose count drops to 0 is pushed
+ * back on top and is the next one handed out.  PA_ERR_INVALID_ARG if
+ * num_blocks <= 0 or free_order is not a permutation. */
+pa_status pa_pool_create(int32_t num_blocks, const int32_t* free_order, pa_pool** out);
+void pa_pool_destroy(pa_pool* pool);
+
+/* Take a block from the pool; its reference count becomes 1.
+ * PA_ERR_OUT_OF_BLOCKS when none is free (nothing changes). */
+pa_status pa_alloc(pa_pool* pool, int32_t* block_out);
+
+/* One more reference on a held block.  PA_ERR_BAD_BLOCK if not held. */
+pa_status pa_incref(pa_pool* pool, int32_t block);
+
+/* Drop one reference; at 0 the block returns to the pool.  PA_ERR_BAD_BLOCK on
+ * an id out of range or a block not held (double free). */
+pa_status pa_free(pa_pool* pool, int32_t block);
+
+/* One more reference on each of table[0..nblocks): a new sequence sharing
+ * these blocks.  All-or-nothing: PA_ERR_BAD_BLOCK if any id is not held. */
+pa_status pa_fork(pa_pool* pool, const int32_t* table, int32_t nblocks);
+
+/* pa_free on table[0..nblocks) in order (a finished sequence). Stops at, and
+ * returns, the first error. */
+pa_status pa_free_table(pa_pool* pool, const int32_t* table, int32_t nblocks);
+
+/* Slots for `n` new tokens at positions pos .. pos+n-1 of one sequence.
+ * table_row (host, capacity max_blocks) holds *nblocks == ceil(pos/16) blocks.
+ * If pos % 16 != 0 and the block holding pos has reference count > 1, it is
+ * copied on write: a new block is taken, the table points at it, the source
+ * loses one reference and (*cow_src, *cow_dst) name the pair to copy on the
+ * device before the tokens are written; otherwise *cow_src = *cow_dst = -1.
+ * New blocks are then taken in logical order as positions need them.
+ * slots_out[i] = table_row[p / 16] * 16 + p % 16 for p = pos + i.
+ * PA_ERR_INVALID_ARG if *nblocks != ceil(pos/16), n < 0 or the row would
+ * exceed max_blocks; PA_ERR_OUT_OF_BLOCKS if the pool is short.  Either way
+ * nothing changes. */
+pa_status pa_append_slots(pa_pool* pool, int32_t* table_row, int32_t* nblocks,
+                          int32_t max_blocks, int32_t pos, int32_t n, int64_t* slots_out,
+                          int32_t* cow_src, int32_t* cow_dst);
+
+/* Reference count of a block (-1 if the id is out of range). */
+int32_t pa_refcount(const pa_pool* pool, int32_t block);
+int32_t pa_num_free(const pa_pool* pool);
+pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
+
+/* Whole blocks whose K and V for all layers fit in `bytes`:
+ * bytes / (2 * layers * 16 * num_kv_heads * head_dim * elem_bytes), the KV_size
+ * closed form of "KV Cache for the intermediate", section "Precise scientific
+ * definition", taken per block.  -1 on a non-positive argument. */
+int64_t pa_blocks_for_bytes(int64_t bytes, int32_t num_layers, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t elem_bytes);
+
+/* ---------------------------------------------------------------------------
+ * Device calls.
+ * ------------------------------------------------------------------------- */
+
+/* Write the K and V of `num_tokens` new tokens into their slots ("KV Cache and
+ * PagedAttention: why your LLM server slows down", second article, section
+ * "What is the KV cache?": only the new token's K/V are computed and stored).
+ *   key, value   device [num_tokens][num_kv_heads][head_dim], contiguous
+ *   k_cache, v_cache  device, layout above, num_blocks blocks
+ *   slot_mapping device int64 [num_tokens]; a slot < 0 or >= num_blocks * 16 is
+ *                skipped (no write)
+ * Tokens must map to distinct slots.  head_dim: a multiple of 16 / elem bytes,
+ * at most 512. */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               pa_dtype dtype, void* stream);
+
+/* Copy whole blocks of both caches: for each pair, block dst of K and of V
+ * becomes block src ("KV Cache and PagedAttention: why your LLM server slows
+ * down", section "How PagedAttention fixes this": copy-on-write of shared
+ * prefix blocks).
+ *   block_pairs  device int64 [num_pairs][2] = (src, dst); a pair with an id
+ *                out of [0, num_blocks) is skipped
+ * The dsts must be distinct and none may also be a src (pairs run
+ * concurrently).  Enqueue it before the pa_reshape_and_cache that writes into
+ * the copies. */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                         int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, pa_dtype dtype, void* stream);
+
+/* Workspace bytes pa_paged_attention_decode needs for these sizes (0 when no
+ * sequence is split).  partition_size as for the decode call. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/* The partition size PA_PARTITION_AUTO resolves to for these sizes. */
+int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
+
+/* Decode attention over the paged cache:
+ *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_s[t]) V_s[t],
+ *   t = 0 .. context_lens[s]-1, K_s[t]/V_s[t] read through block_tables[s]
+ *   from KV head h / (num_q_heads / num_kv_heads).
+ * The textbook softmax and the argument `scale` are the reading taken; the
+ * pages name the attention dot product without a formula.
+ *   q, out        device [num_seqs][num_q_heads][head_dim], contiguous
+ *   k_cache, v_cache  device, layout above
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries at or
+ *                 after ceil(context_lens[s]/16) are never read, the others
+ *                 must be valid block ids
+ *   context_lens  device int32 [num_seqs]; counts the token being decoded
+ *                 (its K/V must already be in the cache); 0 gives out = 0;
+ *                 each must be <= max_context_len and <= 16 * max_blocks_per_seq
+ *   partition_size  PA_PARTITION_NONE, PA_PARTITION_AUTO, or a positive
+ *                 multiple of 16: sequences longer than it are split into
+ *                 partitions of that many positions whose partial results are
+ *                 merged by a second pass (running max / log-sum-exp rule)
+ *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 256-byte
+ *                 aligned; may be NULL when that is 0.  Its contents are
+ *                 scratch between calls.
+ * Supported: dtype in {F32, F16, BF16}; num_q_heads % num_kv_heads == 0;
+ * head_dim a multiple of 16 / elem bytes, at most 256 (the matrix-core path
+ * serves bf16/fp16 at head_dim 64 and 128).  Otherwise PA_ERR_UNSUPPORTED or
+ * PA_ERR_INVALID_ARG. */
+pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    float scale, void* out, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing.  Between pa_timing_begin and pa_timing_end every kernel the
+ * library launches is bracketed by HIP events on its own stream.
+ * pa_timing_end waits for those events and returns, per kernel kind, the
+ * summed milliseconds and the launch count.  At most `capacity` launches are
+ * recorded; later ones run untimed.
+ * ------------------------------------------------------------------------- */
+#define PA_KERNEL_DECODE 0          /* main pass of pa_paged_attention_decode */
+#define PA_KERNEL_DECODE_REDUCE 1   /* merge pass of split sequences */
+#define PA_KERNEL_RESHAPE_AND_CACHE 2
+#define PA_KERNEL_COPY_BLOCKS 3
+#define PA_NUM_KERNEL_KINDS 4
+
+pa_status pa_timing_begin(int32_t capacity);
+pa_status pa_timing_end(double* ms_out /* [PA_NUM_KERNEL_KINDS] */,
+                        int32_t* launches_out /* [PA_NUM_KERNEL_KINDS] */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

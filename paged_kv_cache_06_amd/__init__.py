@@ -1,0 +1,394 @@
+"""Paged KV-cache decode for AMD MI355X (gfx950): Python binding of ``libpa.so``.
+
+This module marshals arguments only.  Every step of the path runs in the
+library: the block pool (C++) and the HIP kernels.  PyTorch supplies device
+memory and the stream; nothing here computes on tensors.  When ``libpa.so`` is
+missing every call raises -- there is no fallback.
+
+The names follow the C ABI of ``include/pa.h`` without its ``pa_`` prefix:
+``reshape_and_cache``, ``copy_blocks``, ``paged_attention_decode``, the pool
+calls on :class:`Pool` (``alloc``, ``free``, ``incref``, ``fork``,
+``free_table``, ``append_slots``, ``refcount``, ``num_free``, ``stats``) and
+``blocks_for_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "BLOCK_SIZE", "PARTITION_NONE", "PARTITION_AUTO", "PAError", "load", "lib_path",
+    "Pool", "BlockManager", "blocks_for_bytes", "reshape_and_cache", "copy_blocks",
+    "paged_attention_decode", "decode_workspace_bytes", "decode_auto_partition",
+    "new_kv_cache", "logical_view", "timing_begin", "timing_end", "status_string",
+]
+
+BLOCK_SIZE = 16
+PARTITION_NONE = 0
+PARTITION_AUTO = -1
+KERNEL_KINDS = ("decode", "decode_reduce", "reshape_and_cache", "copy_blocks")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpa.so")
+_lib = None
+
+_c_i32, _c_i64, _c_sz, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                     ctypes.c_void_p, ctypes.c_float)
+_P_I32 = ctypes.POINTER(ctypes.c_int32)
+_P_I64 = ctypes.POINTER(ctypes.c_int64)
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [("num_blocks", _c_i32), ("num_free", _c_i32), ("num_used", _c_i32),
+                ("num_shared", _c_i32), ("copies", _c_i64)]
+
+
+_SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [_c_i32]),
+    "pa_pool_create": (_c_i32, [_c_i32, _P_I32, ctypes.POINTER(_c_p)]),
+    "pa_pool_destroy": (None, [_c_p]),
+    "pa_alloc": (_c_i32, [_c_p, _P_I32]),
+    "pa_incref": (_c_i32, [_c_p, _c_i32]),
+    "pa_free": (_c_i32, [_c_p, _c_i32]),
+    "pa_fork": (_c_i32, [_c_p, _P_I32, _c_i32]),
+    "pa_free_table": (_c_i32, [_c_p, _P_I32, _c_i32]),
+    "pa_append_slots": (_c_i32, [_c_p, _P_I32, _P_I32, _c_i32, _c_i32, _c_i32, _P_I64,
+                                 _P_I32, _P_I32]),
+    "pa_refcount": (_c_i32, [_c_p, _c_i32]),
+    "pa_num_free": (_c_i32, [_c_p]),
+    "pa_pool_stats": (_c_i32, [_c_p, ctypes.POINTER(_Stats)]),
+    "pa_blocks_for_bytes": (_c_i64, [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_reshape_and_cache": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                      _c_i32, _c_i32, _c_p]),
+    "pa_copy_blocks": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
+    "pa_decode_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_decode_auto_partition": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_paged_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_p, _c_i32,
+                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_p, _c_sz, _c_i32, _c_p]),
+    "pa_timing_begin": (_c_i32, [_c_i32]),
+    "pa_timing_end": (_c_i32, [ctypes.POINTER(ctypes.c_double), _P_I32]),
+}
+
+_STATUS = {0: "ok", -1: "invalid argument", -2: "out of blocks", -3: "bad block id",
+           -4: "unsupported", -5: "device error", -6: "workspace too small"}
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = int(status)
+        super().__init__(f"{call}: {_STATUS.get(self.status, 'unknown status')} ({self.status})")
+
+
+class OutOfBlocks(PAError):
+    pass
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """The loaded library; raises if libpa.so has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m paged_kv_cache_06_amd._build`"
+                " (hipcc, gfx950); there is no fallback path")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise (OutOfBlocks if status == -2 else PAError)(status, call)
+
+
+def status_string(status: int) -> str:
+    return load().pa_status_string(status).decode()
+
+
+# ---------------------------------------------------------------- host pool
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(_P_I32)
+
+
+class Pool:
+    """Block pool of ``num_blocks`` ids (C++); see ``pa_pool_create``."""
+
+    def __init__(self, num_blocks: int, free_order=None):
+        lib = load()
+        self._h = _c_p()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(free_order, dtype=np.int32)
+            if order.shape != (int(num_blocks),):
+                raise ValueError("free_order must have num_blocks entries")
+        _check(lib.pa_pool_create(int(num_blocks), None if order is None else _i32p(order),
+                                  ctypes.byref(self._h)), "pa_pool_create")
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.pa_pool_destroy(self._h)
+            self._h = None
+
+    def alloc(self) -> int:
+        b = _c_i32()
+        _check(load().pa_alloc(self._h, ctypes.byref(b)), "pa_alloc")
+        return b.value
+
+    def incref(self, block: int) -> None:
+        _check(load().pa_incref(self._h, int(block)), "pa_incref")
+
+    def free(self, block: int) -> None:
+        _check(load().pa_free(self._h, int(block)), "pa_free")
+
+    def fork(self, table) -> None:
+        t = np.ascontiguousarray(table, dtype=np.int32)
+        _check(load().pa_fork(self._h, _i32p(t), t.size), "pa_fork")
+
+    def free_table(self, table) -> None:
+        t = np.ascontiguousarray(table, dtype=np.int32)
+        _check(load().pa_free_table(self._h, _i32p(t), t.size), "pa_free_table")
+
+    def append_slots(self, row: np.ndarray, nblocks: int, pos: int, n: int):
+        """Slots of n tokens at pos.. of the sequence whose table is ``row``.
+
+        ``row`` (int32, contiguous, capacity = len(row)) is updated in place.
+        Returns (slots int64 [n], new nblocks, (src, dst) or None).
+        """
+        if row.dtype != np.int32 or not row.flags.c_contiguous:
+            raise ValueError("row must be a contiguous int32 array")
+        nb = _c_i32(int(nblocks))
+        slots = np.empty(max(int(n), 1), dtype=np.int64)
+        src, dst = _c_i32(), _c_i32()
+        _check(load().pa_append_slots(self._h, _i32p(row), ctypes.byref(nb), row.size, int(pos),
+                                      int(n), slots.ctypes.data_as(_P_I64), ctypes.byref(src),
+                                      ctypes.byref(dst)), "pa_append_slots")
+        cow = None if src.value < 0 else (src.value, dst.value)
+        return slots[:int(n)], nb.value, cow
+
+    def refcount(self, block: int) -> int:
+        return int(load().pa_refcount(self._h, int(block)))
+
+    def num_free(self) -> int:
+        return int(load().pa_num_free(self._h))
+
+    def stats(self) -> dict:
+        st = _Stats()
+        _check(load().pa_pool_stats(self._h, ctypes.byref(st)), "pa_pool_stats")
+        return {"num_blocks": st.num_blocks, "free": st.num_free, "used": st.num_used,
+                "shared": st.num_shared, "copies": st.copies}
+
+
+class BlockManager:
+    """Per-sequence block tables on top of :class:`Pool` (host side of a step).
+
+    Holds one int32 row of ``max_blocks`` entries per sequence; ``append``
+    returns the new tokens' slots and any copy-on-write pair.
+    """
+
+    def __init__(self, pool: Pool, num_seqs: int, max_blocks: int, pad: int = 0):
+        self.pool = pool
+        self.rows = np.full((int(num_seqs), int(max_blocks)), int(pad), dtype=np.int32)
+        self.nblocks = np.zeros(int(num_seqs), dtype=np.int32)
+        self.lens = np.zeros(int(num_seqs), dtype=np.int64)
+
+    def append(self, s: int, n: int):
+        row = self.rows[s]
+        slots, nb, cow = self.pool.append_slots(row, int(self.nblocks[s]), int(self.lens[s]), n)
+        self.nblocks[s] = nb
+        self.lens[s] += int(n)
+        return slots, cow
+
+    def fork(self, dst: int, src: int) -> None:
+        if self.nblocks[dst] != 0:
+            raise ValueError("fork target must be empty")
+        nb = int(self.nblocks[src])
+        self.pool.fork(self.rows[src, :nb])
+        self.rows[dst, :nb] = self.rows[src, :nb]
+        self.nblocks[dst] = nb
+        self.lens[dst] = self.lens[src]
+
+    def release(self, s: int, pad: int = 0) -> None:
+        nb = int(self.nblocks[s])
+        self.pool.free_table(self.rows[s, :nb])
+        self.rows[s, :] = pad
+        self.nblocks[s] = 0
+        self.lens[s] = 0
+
+    def table(self, s: int) -> list:
+        return self.rows[s, :int(self.nblocks[s])].tolist()
+
+
+def blocks_for_bytes(nbytes: int, num_layers: int, num_kv_heads: int, head_dim: int,
+                     elem_bytes: int) -> int:
+    return int(load().pa_blocks_for_bytes(int(nbytes), int(num_layers), int(num_kv_heads),
+                                          int(head_dim), int(elem_bytes)))
+
+
+# ------------------------------------------------------------- device calls
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def new_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda",
+                 fill: float | None = None):
+    """(k_cache, v_cache) tensors in the library's layout (see include/pa.h)."""
+    torch = _torch()
+    x = 16 // torch.tensor([], dtype=dtype).element_size()
+    _need(head_dim % x == 0, "head_dim must be a multiple of 16 bytes")
+    kshape = (num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x)
+    vshape = (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE)
+    if fill is None:
+        return (torch.empty(kshape, dtype=dtype, device=device),
+                torch.empty(vshape, dtype=dtype, device=device))
+    return (torch.full(kshape, fill, dtype=dtype, device=device),
+            torch.full(vshape, fill, dtype=dtype, device=device))
+
+
+def logical_view(k_cache, v_cache):
+    """The caches as [num_blocks, Hkv, 16, head_dim] copies (for inspection)."""
+    nb, hkv, dx, bs, x = k_cache.shape
+    k = k_cache.permute(0, 1, 3, 2, 4).reshape(nb, hkv, bs, dx * x)
+    v = v_cache.permute(0, 1, 3, 2)
+    return k.contiguous(), v.contiguous()
+
+
+def _cache_dims(k_cache, v_cache):
+    _need(k_cache.dim() == 5 and v_cache.dim() == 4, "caches must be [NB,Hkv,D/X,16,X] and "
+          "[NB,Hkv,D,16]")
+    nb, hkv, dx, bs, x = k_cache.shape
+    d = dx * x
+    _need(bs == BLOCK_SIZE and tuple(v_cache.shape) == (nb, hkv, d, BLOCK_SIZE),
+          "k_cache / v_cache shapes disagree")
+    _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    _need(k_cache.dtype == v_cache.dtype, "caches must share a dtype")
+    return nb, hkv, d
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping) -> None:
+    """Write key/value [T, Hkv, D] of new tokens into their slots (int64 [T])."""
+    torch = _torch()
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    t = key.shape[0]
+    _need(tuple(key.shape) == (t, hkv, d) and tuple(value.shape) == (t, hkv, d),
+          "key/value must be [T, Hkv, D]")
+    _need(key.is_contiguous() and value.is_contiguous(), "key/value must be contiguous")
+    _need(key.dtype == k_cache.dtype == value.dtype, "dtypes differ")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == t,
+          "slot_mapping must be int64 [T]")
+    _check(load().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(slot_mapping.contiguous()), t, nb, hkv, d,
+                                       _dtype_code(key), _stream(key)), "pa_reshape_and_cache")
+
+
+def copy_blocks(k_cache, v_cache, block_pairs) -> None:
+    """Copy whole blocks: block_pairs is int64 [n, 2] of (src, dst) on the device."""
+    torch = _torch()
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    _need(block_pairs.dtype == torch.int64 and block_pairs.dim() == 2 and
+          block_pairs.shape[1] == 2, "block_pairs must be int64 [n, 2]")
+    n = block_pairs.shape[0]
+    _check(load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs.contiguous()), n,
+                                 nb, hkv, d, _dtype_code(k_cache), _stream(k_cache)),
+           "pa_copy_blocks")
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                           partition_size=PARTITION_AUTO) -> int:
+    return int(load().pa_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(head_dim),
+                                                int(max_context_len), int(partition_size)))
+
+
+def decode_auto_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          dtype_code) -> int:
+    return int(load().pa_decode_auto_partition(int(num_seqs), int(num_q_heads),
+                                               int(num_kv_heads), int(head_dim),
+                                               int(max_context_len), int(dtype_code)))
+
+
+_workspaces = {}
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
+                           max_context_len: int | None = None,
+                           partition_size: int = PARTITION_AUTO, workspace=None) -> None:
+    """out[s, h] = softmax(scale * q[s, h] . K_s) V_s over the paged cache.
+
+    q, out: [S, Hq, D]; block_tables int32 [S, MB]; context_lens int32 [S].
+    ``max_context_len`` defaults to 16 * MB (an upper bound that needs no sync).
+    ``workspace`` (uint8 device tensor) is allocated and kept per device when
+    not given.
+    """
+    torch = _torch()
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    s, hq, dq = q.shape
+    _need(dq == d and tuple(out.shape) == (s, hq, d), "q/out must be [S, Hq, D]")
+    _need(q.is_contiguous() and out.is_contiguous(), "q/out must be contiguous")
+    _need(q.dtype == out.dtype == k_cache.dtype, "dtypes differ")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == s and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == s,
+          "context_lens must be int32 [S]")
+    mb = block_tables.shape[1]
+    mcl = mb * BLOCK_SIZE if max_context_len is None else int(max_context_len)
+    need = decode_workspace_bytes(s, hq, d, mcl, partition_size)
+    if workspace is None and need > 0:
+        key = (q.device, need)
+        workspace = _workspaces.get(key)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            _workspaces.clear()
+            _workspaces[key] = workspace
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_paged_attention_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens.contiguous()),
+        float(scale), _ptr(out), s, hq, hkv, d, mb, mcl, int(partition_size), ws_ptr, ws_bytes,
+        _dtype_code(q), _stream(q)), "pa_paged_attention_decode")
+
+
+# ------------------------------------------------------------------ timing
+def timing_begin(capacity: int = 4096) -> None:
+    _check(load().pa_timing_begin(int(capacity)), "pa_timing_begin")
+
+
+def timing_end() -> dict:
+    ms = (ctypes.c_double * 4)()
+    n = (ctypes.c_int32 * 4)()
+    _check(load().pa_timing_end(ms, n), "pa_timing_end")
+    return {k: {"ms": ms[i], "launches": n[i]} for i, k in enumerate(KERNEL_KINDS)}

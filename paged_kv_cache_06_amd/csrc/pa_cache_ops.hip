@@ -1,0 +1,146 @@
+// Cache writes and block copies.
+//
+// reshape_and_cache stores the K and V of new tokens into their slots: only the
+// new token's K/V are computed each step, everything older is read back ("KV
+// Cache and PagedAttention: why your LLM server slows down", second article,
+// section "What is the KV cache?").  copy_blocks duplicates shared blocks
+// before a sharer writes into them (same page, section "How PagedAttention
+// fixes this": shared prefix with copy-on-write).
+//
+// Both are small and memory-latency bound; every lane moves 16 bytes per
+// access.  K rows keep the 16-byte chunks of one token contiguous (layout
+// [blocks][Hkv][D/X][16][X]); V is stored transposed per block
+// ([blocks][Hkv][D][16]) so that the decode kernel can feed the 16 token
+// values of one dimension straight into the matrix cores.
+#include "pa_common.h"
+
+namespace pa {
+namespace {
+
+// One thread per (token, head, 16-byte chunk of D).
+template <typename E>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ k_cache,
+    E* __restrict__ v_cache, const int64_t* __restrict__ slots, int32_t num_tokens,
+    int64_t num_slots, int32_t hkv, int32_t head_dim) {
+  constexpr int X = 16 / sizeof(E);
+  const int chunks = head_dim / X;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(num_tokens) * hkv * chunks;
+  if (gid >= total) return;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t th = gid / chunks;  // token * hkv + head
+  const int h = static_cast<int>(th % hkv);
+  const int64_t t = th / hkv;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t b = slot / kBlock;
+  const int r = static_cast<int>(slot % kBlock);
+  const int64_t src = th * head_dim + static_cast<int64_t>(c) * X;
+  const int64_t head_base = (b * hkv + h) * static_cast<int64_t>(head_dim) * kBlock;
+
+  const uint4 kv = *reinterpret_cast<const uint4*>(key + src);
+  *reinterpret_cast<uint4*>(k_cache + head_base + (static_cast<int64_t>(c) * kBlock + r) * X) = kv;
+
+  union {
+    uint4 v;
+    E e[X];
+  } vv;
+  vv.v = *reinterpret_cast<const uint4*>(value + src);
+  E* vdst = v_cache + head_base + static_cast<int64_t>(c) * X * kBlock + r;
+#pragma unroll
+  for (int i = 0; i < X; ++i) vdst[i * kBlock] = vv.e[i];
+}
+
+// grid.x = pair * 2 + (0: K, 1: V); grid.y splits the block's bytes.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
+                                                          uint4* __restrict__ v_cache,
+                                                          const int64_t* __restrict__ pairs,
+                                                          int32_t num_blocks, int64_t vec_per_block) {
+  const int pair = blockIdx.x >> 1;
+  uint4* cache = (blockIdx.x & 1) ? v_cache : k_cache;
+  const int64_t src = pairs[2 * pair];
+  const int64_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const uint4* s = cache + src * vec_per_block;
+  uint4* d = cache + dst * vec_per_block;
+  constexpr int kPerThread = 4;
+  const int64_t base = static_cast<int64_t>(blockIdx.y) * 256 * kPerThread + threadIdx.x;
+  uint4 tmp[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int64_t j = base + i * 256;
+    if (j < vec_per_block) tmp[i] = s[j];
+  }
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int64_t j = base + i * 256;
+    if (j < vec_per_block) d[j] = tmp[i];
+  }
+}
+
+bool cache_shape_ok(int32_t num_blocks, int32_t hkv, int32_t head_dim, pa_dtype dt) {
+  if (!valid_dtype(dt) || num_blocks <= 0 || hkv <= 0 || head_dim <= 0) return false;
+  const int x = 16 / elem_bytes(dt);
+  return head_dim % x == 0 && head_dim <= 512;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               pa_dtype dtype, void* stream) {
+  using namespace pa;
+  if (num_tokens < 0 || !cache_shape_ok(num_blocks, num_kv_heads, head_dim, dtype))
+    return valid_dtype(dtype) ? PA_ERR_INVALID_ARG : PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int x = 16 / elem_bytes(dtype);
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / x);
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * kBlock;
+  const int slot = timing_start(PA_KERNEL_RESHAPE_AND_CACHE, st);
+  if (dtype == PA_F32) {
+    reshape_and_cache_kernel<float><<<dim3(grid), dim3(256), 0, st>>>(
+        static_cast<const float*>(key), static_cast<const float*>(value),
+        static_cast<float*>(k_cache), static_cast<float*>(v_cache), slot_mapping, num_tokens,
+        num_slots, num_kv_heads, head_dim);
+  } else {
+    reshape_and_cache_kernel<uint16_t><<<dim3(grid), dim3(256), 0, st>>>(
+        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
+        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), slot_mapping,
+        num_tokens, num_slots, num_kv_heads, head_dim);
+  }
+  const pa_status s = launch_status();
+  timing_stop(slot, st);
+  return s;
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                         int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, pa_dtype dtype, void* stream) {
+  using namespace pa;
+  if (num_pairs < 0 || !cache_shape_ok(num_blocks, num_kv_heads, head_dim, dtype))
+    return valid_dtype(dtype) ? PA_ERR_INVALID_ARG : PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
+  if (num_pairs > (0x7fffffff >> 1)) return PA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t bytes = static_cast<int64_t>(num_kv_heads) * kBlock * head_dim * elem_bytes(dtype);
+  const int64_t vec = bytes / 16;
+  const int64_t gy = (vec + 1023) / 1024;
+  const int slot = timing_start(PA_KERNEL_COPY_BLOCKS, st);
+  copy_blocks_kernel<<<dim3(2 * num_pairs, static_cast<uint32_t>(gy)), dim3(256), 0, st>>>(
+      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), block_pairs, num_blocks, vec);
+  const pa_status s = launch_status();
+  timing_stop(slot, st);
+  return s;
+}
+
+}  // extern "C"

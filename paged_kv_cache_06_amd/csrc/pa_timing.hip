@@ -1,0 +1,93 @@
+// Kernel timing: HIP events around each library launch while timing is on.
+//
+// Events are recorded on the launch's own stream, so the measured interval is
+// the kernel's run time on that stream (plus the event overhead, a few
+// microseconds at most).  Single-threaded use, like the rest of the library.
+#include <vector>
+
+#include "pa_common.h"
+
+namespace {
+
+struct Record {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+struct Timing {
+  bool active = false;
+  int used = 0;
+  std::vector<Record> recs;
+};
+
+Timing& state() {
+  static Timing t;
+  return t;
+}
+
+}  // namespace
+
+namespace pa {
+
+int timing_start(int kind, hipStream_t stream) {
+  Timing& t = state();
+  if (!t.active || t.used >= static_cast<int>(t.recs.size())) return -1;
+  Record& r = t.recs[t.used];
+  if (hipEventRecord(r.start, stream) != hipSuccess) return -1;
+  r.kind = kind;
+  return t.used++;
+}
+
+void timing_stop(int slot, hipStream_t stream) {
+  if (slot < 0) return;
+  Timing& t = state();
+  if (hipEventRecord(t.recs[slot].stop, stream) != hipSuccess) t.recs[slot].kind = -1;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_timing_begin(int32_t capacity) {
+  if (capacity < 0) return PA_ERR_INVALID_ARG;
+  Timing& t = state();
+  while (static_cast<int>(t.recs.size()) < capacity) {
+    Record r{-1, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess) return PA_ERR_DEVICE;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+      (void)hipEventDestroy(r.start);
+      return PA_ERR_DEVICE;
+    }
+    t.recs.push_back(r);
+  }
+  t.used = 0;
+  t.active = true;
+  return PA_OK;
+}
+
+pa_status pa_timing_end(double* ms_out, int32_t* launches_out) {
+  Timing& t = state();
+  if (!ms_out || !launches_out) return PA_ERR_INVALID_ARG;
+  for (int k = 0; k < PA_NUM_KERNEL_KINDS; ++k) {
+    ms_out[k] = 0.0;
+    launches_out[k] = 0;
+  }
+  pa_status st = PA_OK;
+  for (int i = 0; i < t.used; ++i) {
+    Record& r = t.recs[i];
+    if (r.kind < 0 || r.kind >= PA_NUM_KERNEL_KINDS) continue;
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      st = PA_ERR_DEVICE;
+      continue;
+    }
+    ms_out[r.kind] += ms;
+    launches_out[r.kind] += 1;
+  }
+  t.active = false;
+  t.used = 0;
+  return st;
+}
+
+}  // extern "C"

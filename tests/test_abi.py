@@ -1,0 +1,76 @@
+"""The C-ABI library loads on the CPU and exports every symbol include/pa.h declares."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_06_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "pa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for must in ("pa_alloc", "pa_free", "pa_incref", "pa_fork", "pa_append_slots",
+                 "pa_reshape_and_cache", "pa_copy_blocks", "pa_paged_attention_decode",
+                 "pa_decode_workspace_bytes", "pa_pool_create", "pa_pool_destroy"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pa.lib_path())
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_signatures_cover_the_header():
+    assert set(_declared()) == set(pa._SIGNATURES)
+
+
+def test_host_only_calls_and_argument_errors_without_a_gpu():
+    lib = pa.load()
+    assert pa.status_string(-2) == "out of blocks"
+    # pool sizing closed form: one block of 80 layers x 8 heads x 128 dims in fp16
+    assert pa.blocks_for_bytes(16 * 327_680, 80, 8, 128, 2) == 1
+    assert pa.blocks_for_bytes(0, 80, 8, 128, 2) == -1
+    # argument checks fail before anything is launched (no device needed)
+    st = lib.pa_paged_attention_decode(None, None, None, None, None, 1.0, None, 1, 6, 4, 128, 1,
+                                       16, 0, None, 0, 2, None)
+    assert st == -1  # 6 query heads over 4 KV heads
+    st = lib.pa_paged_attention_decode(None, None, None, None, None, 1.0, None, 1, 8, 4, 100, 1,
+                                       16, 0, None, 0, 2, None)
+    assert st == -4  # head_dim 100 is not a multiple of 8 bf16 elements
+    st = lib.pa_paged_attention_decode(None, None, None, None, None, 1.0, None, 1, 8, 4, 128, 1,
+                                       17, 0, None, 0, 2, None)
+    assert st == -1  # max_context_len beyond the table width
+    st = lib.pa_paged_attention_decode(None, None, None, None, None, 1.0, None, 1, 8, 4, 128, 1,
+                                       16, 8, None, 0, 7, None)
+    assert st == -4  # unknown dtype
+    st = lib.pa_paged_attention_decode(ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                       ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                       ctypes.c_void_p(16), 1.0, ctypes.c_void_p(16), 4, 8, 4,
+                                       128, 64, 1024, 256, None, 0, 2, None)
+    assert st == -6  # split without a workspace
+    assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 4, 2, 64, 0, None) == 0
+    assert lib.pa_reshape_and_cache(None, None, None, None, None, 1, 4, 2, 64, 0, None) == -1
+    assert lib.pa_copy_blocks(None, None, None, 0, 4, 2, 60, 2, None) == -1
+
+
+def test_workspace_size_closed_form():
+    # 4 sequences x 8 heads x ceil(1024/256) partitions, (2 + 128) fp32 each, 256-B aligned
+    parts = 4 * 8 * 4
+    want = -(-parts * 2 * 4 // 256) * 256 + -(-parts * 128 * 4 // 256) * 256
+    assert pa.decode_workspace_bytes(4, 8, 128, 1024, 256) == want
+    assert pa.decode_workspace_bytes(4, 8, 128, 1024, pa.PARTITION_NONE) == 0
+    assert pa.decode_workspace_bytes(4, 8, 128, 256, 256) == 0
+    with pytest.raises(ValueError):
+        pa.Pool(4, free_order=[0, 1])

@@ -1,0 +1,176 @@
+"""paged_attention_decode on the GPU against the oracle.
+
+Small cases compare every output with the oracle's paged decode (tables and
+cache built by the oracle itself).  The five workloads run at full size in the
+launch configuration the benchmark times; there the oracle computes sampled
+sequences one by one from their contiguous K/V, and properties that hold at any
+size (split == unsplit, run-to-run and block-relabelling invariance) cover the
+rest.
+"""
+import numpy as np
+import pytest
+
+import paged_kv_cache_06_amd as pa
+import workloads
+from oracle import attention, step
+from oracle.numerics import to_f64
+from paged_kv_cache_06_amd import runner
+from tests.helpers import NAN_BITS, assert_close, bits_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_small(w, partition_size=pa.PARTITION_AUTO):
+    ref_plan, kc, vc, ref = step.run(w, NAN_BITS[w.dtype])
+    db = runner.DeviceBatch(w)
+    db.prefill()
+    db.step(partition_size=partition_size)
+    return db, ref
+
+
+CASES = [
+    # (lens, hq, hkv, d, dtype)
+    ([1, 15, 16, 17, 33, 100, 257, 600], 8, 2, 128, "bf16"),
+    ([1, 15, 16, 17, 33, 100, 257, 600], 8, 2, 128, "f16"),
+    ([3, 64, 129, 700, 1100], 16, 2, 64, "bf16"),
+    ([5, 48, 511, 512, 513, 1025], 32, 8, 128, "bf16"),   # G = 4
+    ([7, 100, 300], 64, 8, 128, "bf16"),                    # G = 8
+    ([9, 200], 32, 1, 128, "f16"),                          # MQA, G = 32 (2 head blocks)
+    ([31, 90], 4, 4, 128, "bf16"),                          # MHA, G = 1
+    ([1, 17, 33, 100], 4, 2, 64, "f32"),                    # generic VALU path
+    ([2, 40, 700], 8, 2, 32, "bf16"),                       # generic path, D = 32
+    ([2, 40, 300], 4, 2, 256, "f16"),                       # generic path, D = 256
+    ([20, 1000], 12, 4, 96, "f32"),                         # generic path, D = 96, G = 3
+]
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d,dtype", CASES)
+@pytest.mark.parametrize("partition_size", [pa.PARTITION_AUTO, pa.PARTITION_NONE, 16, 64, 512])
+def test_small_cases_against_oracle(lens, hq, hkv, d, dtype, partition_size):
+    print(f"[gpu] decode lens={lens} hq={hq} hkv={hkv} d={d} {dtype} P={partition_size}",
+          flush=True)
+    w = workloads.make_custom(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=sum(lens) + hq)
+    db, ref = _run_small(w, partition_size)
+    assert_close(db.out_bits(), ref, dtype, f"{lens} {hq}/{hkv} d={d} {dtype}")
+
+
+def test_tiny_config_every_output():
+    print("[gpu] workload 1 (tiny fp32)", flush=True)
+    w = workloads.make(1)
+    db, ref = _run_small(w)
+    assert_close(db.out_bits(), ref, "f32", "tiny")
+
+
+def test_shared_prefix_small_against_oracle():
+    print("[gpu] shared prefix small", flush=True)
+    w = workloads.make_custom([1, 5, 20, 2, 3, 40, 7, 9], hq=8, hkv=2, d=128, dtype="bf16",
+                              seed=8, prompt_lens=[21, 32, 45], prompt_of=[0, 0, 0, 1, 1, 1, 2, 2])
+    db, ref = _run_small(w)
+    assert_close(db.out_bits(), ref, "bf16", "shared prefix")
+
+
+def test_zero_length_rows_give_zeros_and_others_unaffected():
+    import torch
+    print("[gpu] zero-length rows", flush=True)
+    w = workloads.make_custom([40, 70, 1], hq=8, hkv=2, d=128, dtype="bf16", seed=2)
+    db, ref = _run_small(w)
+    lens = db.context_lens.clone()
+    lens[1] = 0
+    out = torch.full_like(db.out, float("nan"))
+    kc, vc = db.caches[0]
+    pa.paged_attention_decode(db.q, kc, vc, db.tables, lens, w.scale, out,
+                              max_context_len=db.max_context_len)
+    got = bits_of(out)
+    assert np.all(to_f64(got[1], "bf16") == 0)
+    assert np.array_equal(got[[0, 2]], db.out_bits()[[0, 2]])
+
+
+def test_nan_in_table_padding_and_block_tails_does_not_leak():
+    # every unused table entry points at a NaN block, every unwritten slot is NaN;
+    # a clean run on a zero-filled cache must give the same bits
+    print("[gpu] poison", flush=True)
+    w = workloads.make_custom([1, 17, 35, 190], hq=16, hkv=2, d=128, dtype="f16", seed=12)
+    a = runner.DeviceBatch(w)
+    a.prefill()
+    a.step()
+    b = runner.DeviceBatch(w, fill=0.0)
+    b.prefill()
+    b.step()
+    assert np.all(np.isfinite(to_f64(a.out_bits(), "f16")))
+    assert np.array_equal(a.out_bits(), b.out_bits())
+
+
+# ---- full-size workloads, in the benchmark's launch configuration ----
+
+_FULL = {}
+
+
+def _full(config):
+    if config not in _FULL:
+        _FULL.clear()
+        import torch
+        w = workloads.make(config)
+        db = runner.DeviceBatch(w)
+        db.prefill()
+        db.step()
+        torch.cuda.synchronize()
+        _FULL[config] = (w, db)
+    return _FULL[config]
+
+
+def _sample(w, k=6):
+    lens = np.asarray(w.context_lens)
+    order = np.argsort(lens, kind="stable")
+    picks = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
+    rng = np.random.default_rng(0)
+    picks |= set(int(x) for x in rng.choice(len(lens), size=min(k, len(lens)), replace=False))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("config", [2, 3, 4, 5])
+def test_full_size_sampled_sequences_against_oracle(config):
+    print(f"[gpu] full-size workload {config}: sampled oracle check", flush=True)
+    w, db = _full(config)
+    got = db.out_bits()
+    q = to_f64(w.q, w.dtype)
+    group = w.num_q_heads // w.num_kv_heads
+    for s in _sample(w, 4 if config == 5 else 6):
+        kb, vb = w.sequence_kv(s)
+        K, V = to_f64(kb, w.dtype), to_f64(vb, w.dtype)
+        ref = np.stack([attention.attend(q[s, h], K[:, h // group], V[:, h // group], w.scale)
+                        for h in range(w.num_q_heads)])
+        info = assert_close(got[s], ref, w.dtype, f"workload {config} seq {s}")
+        print(f"  seq {s} len {int(w.context_lens[s])}: {info}", flush=True)
+
+
+@pytest.mark.parametrize("config", [3, 5])
+def test_full_size_split_equals_unsplit_and_is_deterministic(config):
+    import torch
+    print(f"[gpu] full-size workload {config}: split/unsplit/determinism", flush=True)
+    w, db = _full(config)
+    base = db.out_bits()
+    out2 = torch.empty_like(db.out)
+    db.decode(partition_size=pa.PARTITION_AUTO, out=out2)
+    assert np.array_equal(bits_of(out2), base)  # run to run
+    db.decode(partition_size=pa.PARTITION_NONE, out=out2)
+    a, b = to_f64(bits_of(out2), w.dtype), to_f64(base, w.dtype)
+    # both round to the storage dtype: one unit of its last place apart at most
+    ulp = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -10
+    assert np.all(np.abs(a - b) <= ulp * np.abs(b) + 1e-6)
+    for ps in (256, 1024):
+        db.decode(partition_size=ps, out=out2)
+        c = to_f64(bits_of(out2), w.dtype)
+        assert np.all(np.abs(c - b) <= ulp * np.abs(b) + 1e-6)
+
+
+def test_full_size_block_relabelling_is_bit_identical():
+    print("[gpu] full-size workload 3: relabelled blocks", flush=True)
+    w, db = _full(3)
+    base = db.out_bits()
+    w2 = workloads.make(3)
+    w2.free_order = np.random.default_rng(99).permutation(w2.num_blocks).astype(np.int32)
+    db2 = runner.DeviceBatch(w2)
+    db2.prefill()
+    db2.step()
+    assert not np.array_equal(db2.bm.rows, db.bm.rows)
+    assert np.array_equal(db2.out_bits(), base)
