@@ -83,27 +83,31 @@ def cpu_baseline(w, budget_s):
     q = to_f64(w.q, w.dtype)
     group = w.num_q_heads // w.num_kv_heads
     e = w.elem_bytes
-    done_tokens, done_bytes, seqs = 0, 0, 0
+    done_tokens, done_bytes, seqs, passes = 0, 0, 0, 0
     t0 = time.perf_counter()
-    for s in range(w.num_seqs):
-        kb, vb = w.sequence_kv(s)
-        K, V = to_f64(kb, w.dtype), to_f64(vb, w.dtype)
-        for g in range(w.num_kv_heads):
-            for h in range(g * group, (g + 1) * group):
-                attention.attend(q[s, h], K[:, g], V[:, g], w.scale)
-        n = int(w.context_lens[s])
-        done_tokens += n
-        done_bytes += n * 2 * w.num_kv_heads * w.head_dim * e + 2 * w.num_q_heads * w.head_dim * e
-        seqs += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    while time.perf_counter() - t0 < budget_s:  # whole passes over the batch, or a prefix
+        for s in range(w.num_seqs):
+            kb, vb = w.sequence_kv(s)
+            K, V = to_f64(kb, w.dtype), to_f64(vb, w.dtype)
+            for g in range(w.num_kv_heads):
+                for h in range(g * group, (g + 1) * group):
+                    attention.attend(q[s, h], K[:, g], V[:, g], w.scale)
+            n = int(w.context_lens[s])
+            done_tokens += n
+            done_bytes += (n * 2 * w.num_kv_heads * w.head_dim * e
+                           + 2 * w.num_q_heads * w.head_dim * e)
+            seqs += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        passes += 1
     dt = time.perf_counter() - t0
     limiter.restore_original_limits()
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "tokens_per_s": round(done_tokens / dt, 1),
-            "sample": f"first {seqs} of {w.num_seqs} sequences ({done_tokens} attended tokens), "
-                      f"oracle decode (fp64 NumPy gather + softmax attention), {dt:.1f} s"}
+            "sample": f"{seqs} sequence decodes in {passes} pass(es) over the {w.num_seqs}-sequence "
+                      f"batch ({done_tokens} attended tokens), oracle decode (fp64 NumPy "
+                      f"gather + softmax attention), {dt:.1f} s"}
 
 
 def main():
@@ -117,6 +121,9 @@ def main():
     ap.add_argument("--partition", type=int, default=-1, help="-1 auto, 0 none, else tokens")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run 3 plain device copies of MIB MiB (a known-size "
+                         "reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -201,6 +208,14 @@ def main():
                      "avg_launch_ms": round(dec_ms, 5),
                      "traffic": traffic},
     }
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = n
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

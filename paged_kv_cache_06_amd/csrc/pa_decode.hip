@@ -5,16 +5,26 @@
 // the intermediate", section "Precise scientific definition"; "PagedAttention
 // for the professional", section "The scientific explanation").  The query
 // heads of one GQA group share a KV head ("KV Cache for the intermediate",
-// section "Grouped Query Attention"), so a work-group serves the whole group
+// section "Grouped Query Attention"), so one work item serves the whole group
 // and every K/V byte is read from HBM once per step.
 //
-// Work split: one work-group (4 waves) per (sequence, KV head, partition of P
-// positions, group of up to 16 query heads).  Sequences longer than P are cut
-// into partitions whose partial results (running max m, sum l, unnormalised
-// acc) are merged by a second kernel with the running-max rule (Milakov and
-// Gimelshein 2018); a sequence with a single partition is normalised and
-// written directly.  Waves of a work-group take the partition's 16-token
-// blocks round-robin and merge their partials through LDS at the end.
+// Work items: (sequence, partition of P positions, KV head, group of up to 16
+// query heads).  Sequences longer than P are cut into partitions whose partial
+// results (running max m, sum l, unnormalised acc) are merged by a second
+// kernel with the running-max rule (Milakov and Gimelshein 2018); a sequence
+// with one partition is normalised and written directly.  A work-group of 4
+// waves serves one item at a time: the waves take the item's 16-token blocks
+// round-robin and merge their partials through LDS at the end.
+//
+// Scheduling.  Item sizes vary by two orders of magnitude in a mixed batch
+// (16 .. 8192 positions), so the persistent kernel launches as many
+// work-groups as fit on the GPU at once and each builds, in LDS, the list of
+// all items ordered largest first (full partitions, then last partitions by
+// size, found with a counting sort over their block counts).  Work-group w
+// takes ranks w, 2G-1-w, 2G+w, ... (a snake over the sorted list, G = grid
+// size), which balances the total work per work-group and leaves only small
+// items for the end.  Batches with more sequences than the LDS list holds use
+// the one-item-per-work-group kernel instead.
 //
 // Matrix-core path (bf16/fp16, head_dim 64 or 128), per 16-token block:
 //   scores[16 tok x 16 heads] = K[16 tok x D] . Q^T[D x 16 heads]
@@ -24,8 +34,9 @@
 //   acc^T[D x 16 heads] += V^T[D x 16 tok] . P^T[16 tok x 16 heads]
 //       with v_mfma_f32_16x16x16_{bf16,f16}; V is stored transposed per block,
 //       so a lane's 4 token values of one dimension are 8 contiguous bytes and
-//       each load reads 512 bytes contiguous.  P enters the matrix core in the
-//       storage dtype (bf16 or fp16); scores, exponentials, sums and the
+//       each load reads 512 bytes contiguous.  P enters the matrix core as a
+//       hi + lo pair in the storage dtype (two products), which keeps its
+//       rounding error near 2^-16 relative; scores, exponentials, sums and the
 //       accumulator stay fp32.
 // Heads beyond the group's size occupy the idle columns of the 16-wide
 // operands and are never stored.  Positions past the sequence end are masked
@@ -36,6 +47,8 @@
 // work-group per query head, VALU dot products, 256-position chunks with the
 // same online softmax and the same partial-result format.
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "pa_common.h"
 
@@ -45,6 +58,8 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxSchedSeqs = 1024;  // sequences the persistent kernel's LDS list holds
+constexpr int kMaxBuckets = 257;     // block counts 0 .. 256 (partitions up to 4096)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -71,6 +86,9 @@ struct Mfma<BF16T> {
                   static_cast<__bf16>(d)};
     return __builtin_bit_cast(uint2, v);
   }
+  // the two packed values of a 32-bit word, widened exactly
+  __device__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 };
 
 template <>
@@ -88,88 +106,63 @@ struct Mfma<F16T> {
                  static_cast<_Float16>(d)};
     return __builtin_bit_cast(uint2, v);
   }
+  __device__ static float lo(uint32_t w) { return f16_to_f32(static_cast<uint16_t>(w)); }
+  __device__ static float hi(uint32_t w) { return f16_to_f32(static_cast<uint16_t>(w >> 16)); }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Merge the per-wave partials in LDS and store the work-group's result: the
-// normalised output when the sequence has one partition, else the partial.
-template <typename Tag, int D, int H>
-__device__ __forceinline__ void store_result(const float (&sm_m)[kWaves][H],
-                                             const float (&sm_l)[kWaves][H],
-                                             const float (&sm_acc)[kWaves][H][D], int nh,
-                                             size_t row0, int p, int nparts, int np_max,
-                                             typename Tag::Bits* __restrict__ out,
-                                             float* __restrict__ ws_ml,
-                                             float* __restrict__ ws_acc) {
-  for (int e = threadIdx.x; e < nh * D; e += kThreads) {
-    const int h = e / D, d = e % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = fast_exp2(sm_m[w][h] - M);
-        L = fmaf(f, sm_l[w][h], L);
-        A = fmaf(f, sm_acc[w][h][d], A);
-      }
-    }
-    const size_t row = row0 + h;
-    if (nparts <= 1) {
-      out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
-    } else {
-      const size_t part = row * np_max + p;
-      ws_acc[part * D + d] = A;
-      if (d == 0) {
-        ws_ml[2 * part] = M;
-        ws_ml[2 * part + 1] = L;
-      }
-    }
-  }
-}
+// Arguments shared by the kernels of the matrix-core path.
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* tables;
+  const int32_t* lens;
+  uint16_t* out;
+  float* ws_ml;
+  float* ws_acc;
+  float scale_log2;
+  int num_seqs, hq_total, hkv, group, head_blocks, max_blocks, part_size, np_max;
+  int nh_max;  // query heads of the largest head group (<= 16): LDS rows per wave
+};
 
-template <typename Tag, int D>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ lens, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ ws_ml, float* __restrict__ ws_acc, int num_seqs, int hq_total, int hkv,
-    int group, int head_blocks, int max_blocks, int part_size, int np_max) {
-  constexpr int kSteps = D / 32;   // QK k-steps of 32 dims
-  constexpr int kSlices = D / 16;  // PV output slices of 16 dims
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ float sm_acc[kWaves][16][D];
-
-  int idx = blockIdx.x;
-  const int hb = idx % head_blocks;
-  idx /= head_blocks;
-  const int g = idx % hkv;
-  idx /= hkv;
-  const int s = idx % num_seqs;
-  const int p = idx / num_seqs;
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int len) {
   // lengths beyond the table width are cut to it, so a bad length cannot read
   // past the table row
-  const int len = min(max(lens[s], 0), max_blocks * kBlock);
-  const int start = p * part_size;
-  if (p > 0 && start >= len) return;
+  return min(max(len, 0), a.max_blocks * kBlock);
+}
 
+// One work item: positions [p*P, min(len, (p+1)*P)) of sequence s against KV
+// head g for query heads h0 .. h0+nh-1 of its group.  `comb` is LDS of
+// kWaves * (2 + D) * nh_max floats.  Ends with the result stored; the caller
+// must __syncthreads() before reusing `comb`.
+template <typename Tag, int D>
+__device__ void decode_item(const DecodeArgs& a, int s, int p, int g, int hb, int len,
+                            float* comb) {
+  constexpr int kSteps = D / 32;   // QK k-steps of 32 dims
+  constexpr int kSlices = D / 16;  // PV output slices of 16 dims
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int n = lane & 15;  // token row (K, scores) / head column (Q, P, acc)
-  const int kg = lane >> 4; // k-group of the MFMA operands
+  const int n = lane & 15;   // token row (K, scores) / head column (Q, P, acc)
+  const int kg = lane >> 4;  // k-group of the MFMA operands
   const int h0 = hb * 16;
-  const int nh = min(16, group - h0);
-  const int end = min(len, start + part_size);
-  const int nblk = (end - start + kBlock - 1) / kBlock;
+  const int nh = min(16, a.group - h0);
+  const int start = p * a.part_size;
+  const int end = min(len, start + a.part_size);
+  const int nblk = max(end - start + kBlock - 1, 0) / kBlock;
   const int blk0 = start / kBlock;
-  const int nparts = min((len + part_size - 1) / part_size, np_max);
+  const int nparts = min((len + a.part_size - 1) / a.part_size, a.np_max);
+  // this wave's blocks: blk0 + wave + kWaves * j, j < my_blocks
+  const int my_blocks = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+
+  // block ids of this wave, 64 at a time: lane j holds the id of its j-th block
+  const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks + blk0 + wave;
+  int ids = lane < my_blocks ? trow[kWaves * lane] : 0;
 
   uint4 qf[kSteps];
   if (n < nh) {
-    const uint16_t* qp = q + (static_cast<size_t>(s) * hq_total + g * group + h0 + n) * D;
+    const uint16_t* qp = a.q + (static_cast<size_t>(s) * a.hq_total + g * a.group + h0 + n) * D;
 #pragma unroll
     for (int j = 0; j < kSteps; ++j) qf[j] = *reinterpret_cast<const uint4*>(qp + (j * 4 + kg) * 8);
   } else {
@@ -182,16 +175,22 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < kSlices; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* trow = tables + static_cast<size_t>(s) * max_blocks + blk0;
   const size_t head_elems = static_cast<size_t>(D) * kBlock;
-  for (int i = wave; i < nblk; i += kWaves) {
-    const int phys = trow[i];
-    const size_t base = (static_cast<size_t>(phys) * hkv + g) * head_elems;
-    const uint16_t* kb = k_cache + base;
-    const uint16_t* vb = v_cache + base;
+  const uint16_t* kbase = a.k_cache + static_cast<size_t>(g) * head_elems;
+  const uint16_t* vbase = a.v_cache + static_cast<size_t>(g) * head_elems;
+  const size_t block_stride = static_cast<size_t>(a.hkv) * head_elems;
+
+  for (int j = 0; j < my_blocks; ++j) {
+    if (j > 0 && (j & 63) == 0) {  // next 64 block ids
+      const int jj = j + lane;
+      ids = jj < my_blocks ? trow[kWaves * jj] : 0;
+    }
+    const int phys = __builtin_amdgcn_readlane(ids, j & 63);
+    const uint16_t* kb = kbase + static_cast<size_t>(phys) * block_stride;
+    const uint16_t* vb = vbase + static_cast<size_t>(phys) * block_stride;
     uint4 kf[kSteps];
 #pragma unroll
-    for (int j = 0; j < kSteps; ++j) kf[j] = *reinterpret_cast<const uint4*>(kb + j * 512 + lane * 8);
+    for (int t = 0; t < kSteps; ++t) kf[t] = *reinterpret_cast<const uint4*>(kb + t * 512 + lane * 8);
     uint2 vf[kSlices];
 #pragma unroll
     for (int sl = 0; sl < kSlices; ++sl)
@@ -199,12 +198,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
 
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kSteps; ++j) sc = Mfma<Tag>::qk(kf[j], qf[j], sc);
+    for (int t = 0; t < kSteps; ++t) sc = Mfma<Tag>::qk(kf[t], qf[t], sc);
 
-    const int pos0 = (blk0 + i) * kBlock + kg * 4;  // position of this lane's first score
+    const int blk = blk0 + wave + kWaves * j;
+    const int pos0 = blk * kBlock + kg * 4;  // position of this lane's first score
     float s4[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s4[r] = (pos0 + r < end) ? sc[r] * scale_log2 : -INFINITY;
+    for (int r = 0; r < 4; ++r) s4[r] = (pos0 + r < end) ? sc[r] * a.scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
 #pragma unroll
     for (int sl = 0; sl < kSlices; ++sl) acc[sl] *= alpha;
 
-    if ((blk0 + i + 1) * kBlock > end) {  // tail block: zero V of masked positions
+    if ((blk + 1) * kBlock > end) {  // tail block: zero V of masked positions
       const uint32_t lo = (pos0 + 0 < end ? 0x0000FFFFu : 0u) | (pos0 + 1 < end ? 0xFFFF0000u : 0u);
       const uint32_t hi = (pos0 + 2 < end ? 0x0000FFFFu : 0u) | (pos0 + 3 < end ? 0xFFFF0000u : 0u);
 #pragma unroll
@@ -227,24 +227,187 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(
         vf[sl].y &= hi;
       }
     }
-    const uint2 pf = Mfma<Tag>::pack(p4[0], p4[1], p4[2], p4[3]);
+    // P as hi + lo in the storage dtype: two products, near-fp32 weights
+    const uint2 ph = Mfma<Tag>::pack(p4[0], p4[1], p4[2], p4[3]);
+    const uint2 pl = Mfma<Tag>::pack(p4[0] - Mfma<Tag>::lo(ph.x), p4[1] - Mfma<Tag>::hi(ph.x),
+                                     p4[2] - Mfma<Tag>::lo(ph.y), p4[3] - Mfma<Tag>::hi(ph.y));
 #pragma unroll
-    for (int sl = 0; sl < kSlices; ++sl) acc[sl] = Mfma<Tag>::pv(vf[sl], pf, acc[sl]);
+    for (int sl = 0; sl < kSlices; ++sl) {
+      acc[sl] = Mfma<Tag>::pv(vf[sl], ph, acc[sl]);
+      acc[sl] = Mfma<Tag>::pv(vf[sl], pl, acc[sl]);
+    }
   }
 
+  // per-wave partials to LDS: comb = [m: kWaves][nh_max] [l: kWaves][nh_max]
+  //                                  [acc: kWaves][nh_max][D]
+  const int nhm = a.nh_max;
+  float* cm = comb;
+  float* cl = comb + kWaves * nhm;
+  float* ca = comb + 2 * kWaves * nhm;
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (kg == 0) {
-    sm_m[wave][n] = m_run;
-    sm_l[wave][n] = l_tot;
-  }
+  if (n < nh) {
+    if (kg == 0) {
+      cm[wave * nhm + n] = m_run;
+      cl[wave * nhm + n] = l_tot;
+    }
 #pragma unroll
-  for (int sl = 0; sl < kSlices; ++sl)
-    *reinterpret_cast<f32x4_t*>(&sm_acc[wave][n][sl * 16 + kg * 4]) = acc[sl];
+    for (int sl = 0; sl < kSlices; ++sl)
+      *reinterpret_cast<f32x4_t*>(&ca[(wave * nhm + n) * D + sl * 16 + kg * 4]) = acc[sl];
+  }
   __syncthreads();
 
-  const size_t row0 = static_cast<size_t>(s) * hq_total + g * group + h0;
-  store_result<Tag, D, 16>(sm_m, sm_l, sm_acc, nh, row0, p, nparts, np_max, out, ws_ml, ws_acc);
+  const size_t row0 = static_cast<size_t>(s) * a.hq_total + g * a.group + h0;
+  for (int e = threadIdx.x; e < nh * D; e += kThreads) {
+    const int h = e / D, d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * nhm + h]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = fast_exp2(cm[w * nhm + h] - M);
+        L = fmaf(f, cl[w * nhm + h], L);
+        A = fmaf(f, ca[(w * nhm + h) * D + d], A);
+      }
+    }
+    const size_t row = row0 + h;
+    if (nparts <= 1) {
+      a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
+    } else {
+      const size_t part = row * a.np_max + p;
+      a.ws_acc[part * D + d] = A;
+      if (d == 0) {
+        a.ws_ml[2 * part] = M;
+        a.ws_ml[2 * part + 1] = L;
+      }
+    }
+  }
+}
+
+__host__ __device__ inline size_t comb_floats(int nh_max, int head_dim) {
+  return static_cast<size_t>(kWaves) * nh_max * (2 + head_dim);
+}
+
+// One item per work-group, partition-major order (p, s, g, hb).  Work-groups
+// of partitions a sequence does not have return at once.
+template <typename Tag, int D>
+__global__ __launch_bounds__(kThreads, 4) void decode_grid_kernel(DecodeArgs a) {
+  extern __shared__ float comb[];
+  int idx = blockIdx.x;
+  const int hb = idx % a.head_blocks;
+  idx /= a.head_blocks;
+  const int g = idx % a.hkv;
+  idx /= a.hkv;
+  const int s = idx % a.num_seqs;
+  const int p = idx / a.num_seqs;
+  const int len = clamp_len(a, a.lens[s]);
+  if (p > 0 && p * a.part_size >= len) return;
+  decode_item<Tag, D>(a, s, p, g, hb, len, comb);
+}
+
+// Exclusive prefix sum of v[0..n) in place (LDS), all threads of the block.
+// `scratch` holds kWaves ints.  Returns the total.
+__device__ int block_exclusive_scan(int* v, int n, int* scratch) {
+  const int per = (n + kThreads - 1) / kThreads;
+  const int b = threadIdx.x * per;
+  const int e = min(n, b + per);
+  int local = 0;
+  for (int i = b; i < e; ++i) local += v[i];
+  // inclusive scan of the per-thread sums within the wave, then across waves
+  const int lane = threadIdx.x & (kWave - 1);
+  int x = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) scratch[threadIdx.x / kWave] = x;
+  __syncthreads();
+  int wave_off = 0;
+  for (int w = 0; w < static_cast<int>(threadIdx.x / kWave); ++w) wave_off += scratch[w];
+  int total = 0;
+  for (int w = 0; w < kWaves; ++w) total += scratch[w];
+  int run = wave_off + x - local;
+  for (int i = b; i < e; ++i) {
+    const int t = v[i];
+    v[i] = run;
+    run += t;
+  }
+  __syncthreads();
+  return total;
+}
+
+// Persistent kernel: every work-group builds the largest-first item list in
+// LDS and walks it in a snake over the grid (see the file header).
+template <typename Tag, int D>
+__global__ __launch_bounds__(kThreads, 4) void decode_persistent_kernel(DecodeArgs a) {
+  extern __shared__ float comb[];
+  const int S = a.num_seqs;
+  const int nbk = a.part_size / kBlock + 1;  // bucket = blocks of a last partition
+  // Every work-group must derive the same list, so everything below is
+  // deterministic (no order-dependent atomics).
+  int* s_len = reinterpret_cast<int*>(comb + comb_floats(a.nh_max, D));
+  int* s_full = s_len + S;              // [S + 1] exclusive prefix of full partitions
+  int* s_order = s_full + S + 1;        // [S]     last partitions, largest first
+  int* s_key = s_order + S;             // [S]     bucket of each last partition
+  int* s_bucket = s_key + S;            // [nbk]
+  int* s_scratch = s_bucket + nbk;      // [kWaves]
+
+  for (int i = threadIdx.x; i < nbk; i += kThreads) s_bucket[i] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < S; i += kThreads) {
+    const int len = clamp_len(a, a.lens[i]);
+    const int np = min((len + a.part_size - 1) / a.part_size, a.np_max);
+    s_len[i] = len;
+    s_full[i] = max(np - 1, 0);
+    const int last = np > 0 ? min((len - (np - 1) * a.part_size + kBlock - 1) / kBlock, nbk - 1)
+                            : 0;
+    s_key[i] = nbk - 1 - last;  // bucket 0 = most blocks
+    atomicAdd(&s_bucket[nbk - 1 - last], 1);  // counts only: order-independent
+  }
+  __syncthreads();
+  const int num_full = block_exclusive_scan(s_full, S, s_scratch);
+  if (threadIdx.x == 0) s_full[S] = num_full;
+  block_exclusive_scan(s_bucket, nbk, s_scratch);
+  // stable placement: one thread per bucket walks the sequences in order
+  for (int b = threadIdx.x; b < nbk; b += kThreads) {
+    int pos = s_bucket[b];
+    for (int i = 0; i < S; ++i)
+      if (s_key[i] == b) s_order[pos++] = i;
+  }
+  __syncthreads();
+
+  // the host bounds (partitions x sequences x heads) below 2^31
+  const int heads = a.hkv * a.head_blocks;
+  const int total = (num_full + S) * heads;
+  const int G = gridDim.x;
+  const int w = blockIdx.x;
+  for (int base = 0; base < total; base += 2 * G) {
+    for (int half = 0; half < 2; ++half) {
+    const int rank = base + (half ? G + (G - 1 - w) : w);
+    if (rank >= total) break;
+    const int u = rank / heads;
+    const int gh = rank % heads;
+    int s, p;
+    if (u < num_full) {  // full partition: s with s_full[s] <= u < s_full[s + 1]
+      int lo = 0, hi = S - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_full[mid] <= u) lo = mid; else hi = mid - 1;
+      }
+      s = lo;
+      p = u - s_full[s];
+    } else {  // last partition of a sequence
+      s = s_order[u - num_full];
+      const int len = s_len[s];
+      p = max(min((len + a.part_size - 1) / a.part_size, a.np_max) - 1, 0);
+    }
+    decode_item<Tag, D>(a, s, p, gh / a.head_blocks, gh % a.head_blocks, s_len[s], comb);
+    __syncthreads();  // comb is reused by the next item
+    }
+  }
 }
 
 // ---- generic VALU path ----
@@ -364,6 +527,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
 
 // Merge the partitions of one (sequence, query head): M = max m_p,
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p   (m in log2 units).
+// One wave per row; lanes take the partitions 64 at a time, so the loads of
+// all partitions are in flight together.
 template <typename Tag>
 __global__ __launch_bounds__(kWave) void decode_reduce_kernel(
     const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
@@ -373,16 +538,31 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(
   const int len = min(max(lens[row / hq_total], 0), max_blocks * kBlock);
   const int np = min((len + part_size - 1) / part_size, np_max);
   if (np <= 1) return;
+  const int lane = threadIdx.x;
   const float* ml = ws_ml + row * np_max * 2;
   float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, ml[2 * i]);
+  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[2 * i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float L = 0.f;
-  for (int i = 0; i < np; ++i) L = fmaf(fast_exp2(ml[2 * i] - M), ml[2 * i + 1], L);
+  for (int i = lane; i < np; i += kWave) L = fmaf(fast_exp2(ml[2 * i] - M), ml[2 * i + 1], L);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+  const float inv = 1.f / L;
   const float* acc = ws_acc + row * np_max * head_dim;
-  for (int d = threadIdx.x; d < head_dim; d += kWave) {
+  for (int d0 = 0; d0 < head_dim; d0 += kWave) {
+    const int d = d0 + lane;
     float A = 0.f;
-    for (int i = 0; i < np; ++i) A = fmaf(fast_exp2(ml[2 * i] - M), acc[i * head_dim + d], A);
-    out[row * head_dim + d] = Tag::from_f32(A / L);
+    for (int c = 0; c < np; c += kWave) {
+      const float wl = c + lane < np ? fast_exp2(ml[2 * (c + lane)] - M) : 0.f;
+      const int cnt = min(kWave, np - c);
+#pragma unroll 8
+      for (int k = 0; k < cnt; ++k) {
+        const float wk = __shfl(wl, k);
+        if (d < head_dim) A = fmaf(wk, acc[(c + k) * head_dim + d], A);
+      }
+    }
+    if (d < head_dim) out[row * head_dim + d] = Tag::from_f32(A * inv);
   }
 }
 
@@ -421,6 +601,54 @@ bool mfma_path(pa_dtype dt, int head_dim) {
   return (dt == PA_BF16 || dt == PA_F16) && (head_dim == 64 || head_dim == 128);
 }
 
+// Work-groups of `kern` resident on the current device at once (cached per
+// device, kernel and LDS size).
+int resident_groups(const void* kern, size_t lds_bytes) {
+  struct Entry {
+    int dev;
+    const void* kern;
+    size_t lds;
+    int groups;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.dev == dev && e.kern == kern && e.lds == lds_bytes) return e.groups;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds_bytes) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int n = max(per_cu, 0) * max(cus, 0);
+  cache.push_back({dev, kern, lds_bytes, n});
+  return n;
+}
+
+template <typename Tag, int D>
+pa_status launch_mfma(const DecodeArgs& a, hipStream_t st) {
+  const int heads = a.hkv * a.head_blocks;
+  const int64_t upper = static_cast<int64_t>(a.np_max) * a.num_seqs * heads;
+  const size_t comb = comb_floats(a.nh_max, D) * sizeof(float);
+  if (a.num_seqs <= kMaxSchedSeqs && a.part_size / kBlock + 1 <= kMaxBuckets &&
+      upper <= 0x7fffffff) {
+    const size_t lds = comb + sizeof(int) * (4 * static_cast<size_t>(a.num_seqs) + 1 +
+                                             a.part_size / kBlock + 1 + kWaves);
+    const void* kern = reinterpret_cast<const void*>(&decode_persistent_kernel<Tag, D>);
+    const int resident = resident_groups(kern, lds);
+    if (resident > 0) {
+      const int grid = static_cast<int>(std::min<int64_t>(resident, upper));
+      decode_persistent_kernel<Tag, D><<<dim3(grid), dim3(kThreads), lds, st>>>(a);
+      return launch_status();
+    }
+  }
+  if (upper > 0x7fffffff) return PA_ERR_INVALID_ARG;
+  decode_grid_kernel<Tag, D><<<dim3(static_cast<uint32_t>(upper)), dim3(kThreads), comb, st>>>(a);
+  return launch_status();
+}
+
 template <typename Tag>
 pa_status launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
                  const int32_t* lens, float scale_log2, void* out, int num_seqs, int hq, int hkv,
@@ -428,34 +656,41 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
                  bool use_mfma, hipStream_t st) {
   using E = typename Tag::Bits;
   const int group = hq / hkv;
-  const int head_blocks = use_mfma ? (group + 15) / 16 : 1;
-  const int64_t grid = use_mfma ? static_cast<int64_t>(sp.np) * num_seqs * hkv * head_blocks
-                                : static_cast<int64_t>(sp.np) * num_seqs * hq;
-  if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
-  const dim3 grid3(static_cast<uint32_t>(grid)), block3(kThreads);
+  if (!use_mfma && static_cast<int64_t>(sp.np) * num_seqs * hq > 0x7fffffff)
+    return PA_ERR_INVALID_ARG;
   int slot = timing_start(PA_KERNEL_DECODE, st);
+  pa_status status = PA_OK;
   if (use_mfma) {
     if constexpr (sizeof(E) == 2) {
-      if (head_dim == 128)
-        decode_mfma_kernel<Tag, 128><<<grid3, block3, 0, st>>>(
-            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-            static_cast<const uint16_t*>(v_cache), tables, lens, scale_log2,
-            static_cast<uint16_t*>(out), ws_ml, ws_acc, num_seqs, hq, hkv, group, head_blocks,
-            max_blocks, sp.part, sp.np);
-      else
-        decode_mfma_kernel<Tag, 64><<<grid3, block3, 0, st>>>(
-            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-            static_cast<const uint16_t*>(v_cache), tables, lens, scale_log2,
-            static_cast<uint16_t*>(out), ws_ml, ws_acc, num_seqs, hq, hkv, group, head_blocks,
-            max_blocks, sp.part, sp.np);
+      DecodeArgs a;
+      a.q = static_cast<const uint16_t*>(q);
+      a.k_cache = static_cast<const uint16_t*>(k_cache);
+      a.v_cache = static_cast<const uint16_t*>(v_cache);
+      a.tables = tables;
+      a.lens = lens;
+      a.out = static_cast<uint16_t*>(out);
+      a.ws_ml = ws_ml;
+      a.ws_acc = ws_acc;
+      a.scale_log2 = scale_log2;
+      a.num_seqs = num_seqs;
+      a.hq_total = hq;
+      a.hkv = hkv;
+      a.group = group;
+      a.head_blocks = (group + 15) / 16;
+      a.max_blocks = max_blocks;
+      a.part_size = sp.part;
+      a.np_max = sp.np;
+      a.nh_max = std::min(16, group);
+      status = head_dim == 128 ? launch_mfma<Tag, 128>(a, st) : launch_mfma<Tag, 64>(a, st);
     }
   } else {
-    decode_generic_kernel<Tag><<<grid3, block3, 0, st>>>(
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(sp.np) * num_seqs * hq));
+    decode_generic_kernel<Tag><<<grid, dim3(kThreads), 0, st>>>(
         static_cast<const E*>(q), static_cast<const E*>(k_cache), static_cast<const E*>(v_cache),
         tables, lens, scale_log2, static_cast<E*>(out), ws_ml, ws_acc, num_seqs, hq, hkv, group,
         head_dim, max_blocks, sp.part, sp.np);
+    status = launch_status();
   }
-  pa_status status = launch_status();
   timing_stop(slot, st);
   if (status != PA_OK || sp.np <= 1) return status;
   slot = timing_start(PA_KERNEL_DECODE_REDUCE, st);

@@ -85,6 +85,15 @@ def test_zero_length_rows_give_zeros_and_others_unaffected():
     assert np.array_equal(got[[0, 2]], db.out_bits()[[0, 2]])
 
 
+def test_more_sequences_than_the_persistent_schedule_holds():
+    # 1100 short sequences take the one-item-per-work-group kernel
+    print("[gpu] 1100 sequences", flush=True)
+    lens = (np.arange(1100) % 45) + 1
+    w = workloads.make_custom(lens, hq=8, hkv=2, d=64, dtype="bf16", seed=5)
+    db, ref = _run_small(w, 16)
+    assert_close(db.out_bits(), ref, "bf16", "1100 sequences")
+
+
 def test_nan_in_table_padding_and_block_tails_does_not_leak():
     # every unused table entry points at a NaN block, every unwritten slot is NaN;
     # a clean run on a zero-filled cache must give the same bits
@@ -152,15 +161,15 @@ def test_full_size_split_equals_unsplit_and_is_deterministic(config):
     out2 = torch.empty_like(db.out)
     db.decode(partition_size=pa.PARTITION_AUTO, out=out2)
     assert np.array_equal(bits_of(out2), base)  # run to run
-    db.decode(partition_size=pa.PARTITION_NONE, out=out2)
-    a, b = to_f64(bits_of(out2), w.dtype), to_f64(base, w.dtype)
-    # both round to the storage dtype: one unit of its last place apart at most
+    b = to_f64(base, w.dtype)
+    # the fp32 results differ only in summation order; after rounding to the
+    # storage dtype they are at most one unit in its last place apart
     ulp = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -10
-    assert np.all(np.abs(a - b) <= ulp * np.abs(b) + 1e-6)
-    for ps in (256, 1024):
+    for ps in (pa.PARTITION_NONE, 256, 1024):
         db.decode(partition_size=ps, out=out2)
         c = to_f64(bits_of(out2), w.dtype)
-        assert np.all(np.abs(c - b) <= ulp * np.abs(b) + 1e-6)
+        ratio = np.abs(c - b) / (ulp * np.abs(b) + 1e-6)
+        assert ratio.max() <= 1.0, f"partition {ps}: {ratio.max():.2f} ulp"
 
 
 def test_full_size_block_relabelling_is_bit_identical():
