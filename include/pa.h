@@ -63,7 +63,7 @@ typedef int32_t pa_dtype;
 
 /* partition_size values of pa_paged_attention_decode besides a positive
  * multiple of 16 */
-#define PA_PARTITION_NONE 0   /* one pass over the whole sequence, no workspace */
+#define PA_PARTITION_NONE 0    /* one pass over each whole sequence, no partials */
 #define PA_PARTITION_AUTO (-1) /* the library picks */
 
 /* Short English text of a status code (static storage). */
@@ -168,8 +168,11 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
                          int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
                          int32_t head_dim, pa_dtype dtype, void* stream);
 
-/* Workspace bytes pa_paged_attention_decode needs for these sizes (0 when no
- * sequence is split).  partition_size as for the decode call. */
+/* Workspace bytes pa_paged_attention_decode needs for these sizes: the work
+ * list of the call (16 bytes per sequence and partition, 4 per sequence) plus,
+ * when some sequence is split, the partial results (4 * (2 + head_dim) bytes
+ * per sequence, query head and partition).  partition_size as for the decode
+ * call.  0 on invalid sizes. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size);
 
@@ -196,8 +199,9 @@ int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 partitions of that many positions whose partial results are
  *                 merged by a second pass (running max / log-sum-exp rule)
  *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 256-byte
- *                 aligned; may be NULL when that is 0.  Its contents are
- *                 scratch between calls.
+ *                 aligned; scratch that each call rewrites before reading.
+ *                 Calls that share a workspace must not overlap (same stream,
+ *                 or ordered by events).
  * Supported: dtype in {F32, F16, BF16}; num_q_heads % num_kv_heads == 0;
  * head_dim a multiple of 16 / elem bytes, at most 256 (the matrix-core path
  * serves bf16/fp16 at head_dim 64 and 128).  Otherwise PA_ERR_UNSUPPORTED or
@@ -221,7 +225,8 @@ pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const vo
 #define PA_KERNEL_DECODE_REDUCE 1   /* merge pass of split sequences */
 #define PA_KERNEL_RESHAPE_AND_CACHE 2
 #define PA_KERNEL_COPY_BLOCKS 3
-#define PA_NUM_KERNEL_KINDS 4
+#define PA_KERNEL_DECODE_PLAN 4     /* work list of pa_paged_attention_decode */
+#define PA_NUM_KERNEL_KINDS 5
 
 pa_status pa_timing_begin(int32_t capacity);
 pa_status pa_timing_end(double* ms_out /* [PA_NUM_KERNEL_KINDS] */,

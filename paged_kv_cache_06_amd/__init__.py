@@ -28,7 +28,7 @@ __all__ = [
 BLOCK_SIZE = 16
 PARTITION_NONE = 0
 PARTITION_AUTO = -1
-KERNEL_KINDS = ("decode", "decode_reduce", "reshape_and_cache", "copy_blocks")
+KERNEL_KINDS = ("decode", "decode_reduce", "reshape_and_cache", "copy_blocks", "decode_plan")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -351,7 +351,7 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     q, out: [S, Hq, D]; block_tables int32 [S, MB]; context_lens int32 [S].
     ``max_context_len`` defaults to 16 * MB (an upper bound that needs no sync).
     ``workspace`` (uint8 device tensor) is allocated and kept per device when
-    not given.
+    not given; calls sharing a workspace must not overlap.
     """
     torch = _torch()
     nb, hkv, d = _cache_dims(k_cache, v_cache)
@@ -388,7 +388,7 @@ def timing_begin(capacity: int = 4096) -> None:
 
 
 def timing_end() -> dict:
-    ms = (ctypes.c_double * 4)()
-    n = (ctypes.c_int32 * 4)()
+    ms = (ctypes.c_double * len(KERNEL_KINDS))()
+    n = (ctypes.c_int32 * len(KERNEL_KINDS))()
     _check(load().pa_timing_end(ms, n), "pa_timing_end")
     return {k: {"ms": ms[i], "launches": n[i]} for i, k in enumerate(KERNEL_KINDS)}

@@ -13,18 +13,18 @@
 // results (running max m, sum l, unnormalised acc) are merged by a second
 // kernel with the running-max rule (Milakov and Gimelshein 2018); a sequence
 // with one partition is normalised and written directly.  A work-group of 4
-// waves serves one item at a time: the waves take the item's 16-token blocks
+// waves serves one item: the waves take the item's 16-token blocks
 // round-robin and merge their partials through LDS at the end.
 //
 // Scheduling.  Item sizes vary by two orders of magnitude in a mixed batch
-// (16 .. 8192 positions), so the persistent kernel launches as many
-// work-groups as fit on the GPU at once and each builds, in LDS, the list of
-// all items ordered largest first (full partitions, then last partitions by
-// size, found with a counting sort over their block counts).  Work-group w
-// takes ranks w, 2G-1-w, 2G+w, ... (a snake over the sorted list, G = grid
-// size), which balances the total work per work-group and leaves only small
-// items for the end.  Batches with more sequences than the LDS list holds use
-// the one-item-per-work-group kernel instead.
+// (16 .. 8192 positions).  A one-work-group plan kernel turns the lengths into
+// an item list ordered largest first -- every full partition, then the last
+// partition of every sequence by size class -- plus the list of split
+// sequences.  Work-group i of the decode kernel serves item i / (heads) of
+// that list, so the hardware dispatcher hands out big items first and the
+// last ones to start are the smallest: a short tail with no atomics and no
+// idle work-groups besides the trailing ones past the list's end, which exit
+// at once.  The merge kernel walks only the split sequences.
 //
 // Matrix-core path (bf16/fp16, head_dim 64 or 128), per 16-token block:
 //   scores[16 tok x 16 heads] = K[16 tok x D] . Q^T[D x 16 heads]
@@ -46,9 +46,8 @@
 // Generic path (any supported dtype/head_dim, fp32 in particular): one
 // work-group per query head, VALU dot products, 256-position chunks with the
 // same online softmax and the same partial-result format.
+#include <algorithm>
 #include <cmath>
-#include <mutex>
-#include <vector>
 
 #include "pa_common.h"
 
@@ -58,8 +57,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kMaxSchedSeqs = 1024;  // sequences the persistent kernel's LDS list holds
-constexpr int kMaxBuckets = 257;     // block counts 0 .. 256 (partitions up to 4096)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -290,124 +287,123 @@ __host__ __device__ inline size_t comb_floats(int nh_max, int head_dim) {
   return static_cast<size_t>(kWaves) * nh_max * (2 + head_dim);
 }
 
-// One item per work-group, partition-major order (p, s, g, hb).  Work-groups
-// of partitions a sequence does not have return at once.
-template <typename Tag, int D>
-__global__ __launch_bounds__(kThreads, 4) void decode_grid_kernel(DecodeArgs a) {
-  extern __shared__ float comb[];
-  int idx = blockIdx.x;
-  const int hb = idx % a.head_blocks;
-  idx /= a.head_blocks;
-  const int g = idx % a.hkv;
-  idx /= a.hkv;
-  const int s = idx % a.num_seqs;
-  const int p = idx / a.num_seqs;
-  const int len = clamp_len(a, a.lens[s]);
-  if (p > 0 && p * a.part_size >= len) return;
-  decode_item<Tag, D>(a, s, p, g, hb, len, comb);
+// Size class of a last partition: 0 (the largest) .. kClasses - 1 (an empty
+// sequence).  Classes 0..5 are sixths of a partition, largest first; class 6
+// holds slivers below 1/64 of a partition.
+constexpr int kClasses = 8;
+__device__ __forceinline__ int size_class(int tokens, int part_size) {
+  if (tokens <= 0) return kClasses - 1;
+  if (tokens * 64 < part_size) return kClasses - 2;
+  return 6 - (tokens * 6 + part_size - 1) / part_size;
 }
 
-// Exclusive prefix sum of v[0..n) in place (LDS), all threads of the block.
-// `scratch` holds kWaves ints.  Returns the total.
-__device__ int block_exclusive_scan(int* v, int n, int* scratch) {
-  const int per = (n + kThreads - 1) / kThreads;
-  const int b = threadIdx.x * per;
-  const int e = min(n, b + per);
-  int local = 0;
-  for (int i = b; i < e; ++i) local += v[i];
-  // inclusive scan of the per-thread sums within the wave, then across waves
-  const int lane = threadIdx.x & (kWave - 1);
-  int x = local;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == kWave - 1) scratch[threadIdx.x / kWave] = x;
-  __syncthreads();
-  int wave_off = 0;
-  for (int w = 0; w < static_cast<int>(threadIdx.x / kWave); ++w) wave_off += scratch[w];
-  int total = 0;
-  for (int w = 0; w < kWaves; ++w) total += scratch[w];
-  int run = wave_off + x - local;
-  for (int i = b; i < e; ++i) {
-    const int t = v[i];
-    v[i] = run;
-    run += t;
-  }
-  __syncthreads();
-  return total;
+struct PlanArgs {
+  const int32_t* lens;
+  int4* items;  // [num_seqs * np_max] (sequence, partition, length, 0); sequence -1 past the end
+  int* split;   // [num_seqs] sequences with more than one partition, then -1
+  int* meta;    // [0] items, [1] split sequences
+  int num_seqs, max_blocks, part_size, np_max;
+};
+
+__device__ __forceinline__ int plan_len(const PlanArgs& a, int i) {
+  return min(max(a.lens[i], 0), a.max_blocks * kBlock);
+}
+__device__ __forceinline__ int plan_parts(const PlanArgs& a, int len) {
+  return min((len + a.part_size - 1) / a.part_size, a.np_max);
 }
 
-// Persistent kernel: every work-group builds the largest-first item list in
-// LDS and walks it in a snake over the grid (see the file header).
-template <typename Tag, int D>
-__global__ __launch_bounds__(kThreads, 4) void decode_persistent_kernel(DecodeArgs a) {
-  extern __shared__ float comb[];
+// The item list, largest first (see the file header).  One work-group; each
+// thread takes a run of consecutive sequences, so one exclusive scan of its
+// per-class counts places every item, in sequence order within a class.
+__global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
+  constexpr int kVals = kClasses + 2;  // classes, full partitions, split sequences
+  __shared__ int wave_tot[kWaves][kVals];
   const int S = a.num_seqs;
-  const int nbk = a.part_size / kBlock + 1;  // bucket = blocks of a last partition
-  // Every work-group must derive the same list, so everything below is
-  // deterministic (no order-dependent atomics).
-  int* s_len = reinterpret_cast<int*>(comb + comb_floats(a.nh_max, D));
-  int* s_full = s_len + S;              // [S + 1] exclusive prefix of full partitions
-  int* s_order = s_full + S + 1;        // [S]     last partitions, largest first
-  int* s_key = s_order + S;             // [S]     bucket of each last partition
-  int* s_bucket = s_key + S;            // [nbk]
-  int* s_scratch = s_bucket + nbk;      // [kWaves]
-
-  for (int i = threadIdx.x; i < nbk; i += kThreads) s_bucket[i] = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < S; i += kThreads) {
-    const int len = clamp_len(a, a.lens[i]);
-    const int np = min((len + a.part_size - 1) / a.part_size, a.np_max);
-    s_len[i] = len;
-    s_full[i] = max(np - 1, 0);
-    const int last = np > 0 ? min((len - (np - 1) * a.part_size + kBlock - 1) / kBlock, nbk - 1)
-                            : 0;
-    s_key[i] = nbk - 1 - last;  // bucket 0 = most blocks
-    atomicAdd(&s_bucket[nbk - 1 - last], 1);  // counts only: order-independent
+  const int per = (S + kThreads - 1) / kThreads;
+  const int i0 = threadIdx.x * per;
+  const int i1 = min(S, i0 + per);
+  int cnt[kVals];
+#pragma unroll
+  for (int c = 0; c < kVals; ++c) cnt[c] = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int len = plan_len(a, i);
+    const int np = plan_parts(a, len);
+    const int cls = size_class(np > 0 ? len - (np - 1) * a.part_size : 0, a.part_size);
+#pragma unroll
+    for (int c = 0; c < kClasses; ++c) cnt[c] += cls == c;
+    cnt[kClasses] += max(np - 1, 0);
+    cnt[kClasses + 1] += np > 1;
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  int excl[kVals];
+#pragma unroll
+  for (int c = 0; c < kVals; ++c) {
+    int x = cnt[c];
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    excl[c] = x - cnt[c];
+    if (lane == kWave - 1) wave_tot[wv][c] = x;
   }
   __syncthreads();
-  const int num_full = block_exclusive_scan(s_full, S, s_scratch);
-  if (threadIdx.x == 0) s_full[S] = num_full;
-  block_exclusive_scan(s_bucket, nbk, s_scratch);
-  // stable placement: one thread per bucket walks the sequences in order
-  for (int b = threadIdx.x; b < nbk; b += kThreads) {
-    int pos = s_bucket[b];
-    for (int i = 0; i < S; ++i)
-      if (s_key[i] == b) s_order[pos++] = i;
+  int all[kVals];
+#pragma unroll
+  for (int c = 0; c < kVals; ++c) {
+    int before = 0, sum = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      before += w < wv ? wave_tot[w][c] : 0;
+      sum += wave_tot[w][c];
+    }
+    excl[c] += before;
+    all[c] = sum;
   }
-  __syncthreads();
+  // item positions: full partitions from 0, then classes in order
+  const int num_full = all[kClasses];
+  int pos[kClasses];
+  int run = num_full;
+#pragma unroll
+  for (int c = 0; c < kClasses; ++c) {
+    pos[c] = run + excl[c];
+    run += all[c];
+  }
+  int full_pos = excl[kClasses];
+  int split_pos = excl[kClasses + 1];
+  for (int i = i0; i < i1; ++i) {
+    const int len = plan_len(a, i);
+    const int np = plan_parts(a, len);
+    for (int p = 0; p + 1 < np; ++p) a.items[full_pos++] = make_int4(i, p, len, 0);
+    const int cls = size_class(np > 0 ? len - (np - 1) * a.part_size : 0, a.part_size);
+    int at = 0;
+#pragma unroll
+    for (int c = 0; c < kClasses; ++c)
+      if (cls == c) at = pos[c]++;
+    a.items[at] = make_int4(i, max(np - 1, 0), len, 0);
+    if (np > 1) a.split[split_pos++] = i;
+  }
+  const int total = num_full + S;
+  const int cap = S * a.np_max;
+  for (int u = total + threadIdx.x; u < cap; u += kThreads) a.items[u] = make_int4(-1, 0, 0, 0);
+  for (int i = all[kClasses + 1] + threadIdx.x; i < S; i += kThreads) a.split[i] = -1;
+  if (threadIdx.x == 0) {
+    a.meta[0] = total;
+    a.meta[1] = all[kClasses + 1];
+  }
+}
 
-  // the host bounds (partitions x sequences x heads) below 2^31
+// Work-group i serves item i / heads of the plan (heads = KV heads x query
+// head groups); work-groups past the list's end exit at once.
+template <typename Tag, int D>
+__global__ __launch_bounds__(kThreads, 4) void decode_items_kernel(DecodeArgs a,
+                                                                   const int4* __restrict__ items) {
+  extern __shared__ float comb[];
   const int heads = a.hkv * a.head_blocks;
-  const int total = (num_full + S) * heads;
-  const int G = gridDim.x;
-  const int w = blockIdx.x;
-  for (int base = 0; base < total; base += 2 * G) {
-    for (int half = 0; half < 2; ++half) {
-    const int rank = base + (half ? G + (G - 1 - w) : w);
-    if (rank >= total) break;
-    const int u = rank / heads;
-    const int gh = rank % heads;
-    int s, p;
-    if (u < num_full) {  // full partition: s with s_full[s] <= u < s_full[s + 1]
-      int lo = 0, hi = S - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_full[mid] <= u) lo = mid; else hi = mid - 1;
-      }
-      s = lo;
-      p = u - s_full[s];
-    } else {  // last partition of a sequence
-      s = s_order[u - num_full];
-      const int len = s_len[s];
-      p = max(min((len + a.part_size - 1) / a.part_size, a.np_max) - 1, 0);
-    }
-    decode_item<Tag, D>(a, s, p, gh / a.head_blocks, gh % a.head_blocks, s_len[s], comb);
-    __syncthreads();  // comb is reused by the next item
-    }
-  }
+  const int4 it = items[blockIdx.x / heads];
+  if (it.x < 0) return;
+  const int gh = blockIdx.x % heads;
+  decode_item<Tag, D>(a, it.x, it.y, gh / a.head_blocks, gh % a.head_blocks, it.z, comb);
 }
 
 // ---- generic VALU path ----
@@ -527,42 +523,66 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
 
 // Merge the partitions of one (sequence, query head): M = max m_p,
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p   (m in log2 units).
-// One wave per row; lanes take the partitions 64 at a time, so the loads of
-// all partitions are in flight together.
+// Work-groups walk the rows of the split sequences of the plan.  Within a row,
+// thread t reads 16-byte pieces d4 = t % (D/4) of the partitions
+// p = t / (D/4) + k * (256 / (D/4)), so the row's loads are in flight
+// together; the per-thread sums are merged through LDS.
 template <typename Tag>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(
+__global__ __launch_bounds__(kThreads) void decode_reduce_kernel(
     const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+    const int* __restrict__ split, const int* __restrict__ meta,
     const int32_t* __restrict__ lens, typename Tag::Bits* __restrict__ out, int hq_total,
     int head_dim, int max_blocks, int part_size, int np_max) {
-  const size_t row = blockIdx.x;
-  const int len = min(max(lens[row / hq_total], 0), max_blocks * kBlock);
-  const int np = min((len + part_size - 1) / part_size, np_max);
-  if (np <= 1) return;
-  const int lane = threadIdx.x;
-  const float* ml = ws_ml + row * np_max * 2;
-  float M = -INFINITY;
-  for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[2 * i]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float L = 0.f;
-  for (int i = lane; i < np; i += kWave) L = fmaf(fast_exp2(ml[2 * i] - M), ml[2 * i + 1], L);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-  const float inv = 1.f / L;
-  const float* acc = ws_acc + row * np_max * head_dim;
-  for (int d0 = 0; d0 < head_dim; d0 += kWave) {
-    const int d = d0 + lane;
-    float A = 0.f;
-    for (int c = 0; c < np; c += kWave) {
-      const float wl = c + lane < np ? fast_exp2(ml[2 * (c + lane)] - M) : 0.f;
-      const int cnt = min(kWave, np - c);
-#pragma unroll 8
-      for (int k = 0; k < cnt; ++k) {
-        const float wk = __shfl(wl, k);
-        if (d < head_dim) A = fmaf(wk, acc[(c + k) * head_dim + d], A);
+  __shared__ float red[kWaves];
+  __shared__ float4 part_sum[kThreads];
+  const int rows = meta[1] * hq_total;
+  const int tid = threadIdx.x;
+  const int q4 = head_dim / 4;  // float4 pieces per row
+  const int lanes_per_part = kThreads / q4;
+  const int d4 = tid % q4, pr = tid / q4;
+  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+    const int s = split[r / hq_total];
+    const size_t row = static_cast<size_t>(s) * hq_total + r % hq_total;
+    const int len = min(max(lens[s], 0), max_blocks * kBlock);
+    const int np = min((len + part_size - 1) / part_size, np_max);
+    const float* ml = ws_ml + row * np_max * 2;
+    float M = -INFINITY;
+    for (int i = tid; i < np; i += kThreads) M = fmaxf(M, ml[2 * i]);
+    M = block_reduce_max(M, red);
+    float L = 0.f;
+    for (int i = tid; i < np; i += kThreads) L = fmaf(fast_exp2(ml[2 * i] - M), ml[2 * i + 1], L);
+    L = block_reduce_sum(L, red);
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (pr < lanes_per_part) {
+      const float4* acc = reinterpret_cast<const float4*>(ws_acc + row * np_max * head_dim);
+      for (int i = pr; i < np; i += lanes_per_part) {
+        const float wgt = fast_exp2(ml[2 * i] - M);
+        const float4 v = acc[static_cast<size_t>(i) * q4 + d4];
+        A.x = fmaf(wgt, v.x, A.x);
+        A.y = fmaf(wgt, v.y, A.y);
+        A.z = fmaf(wgt, v.z, A.z);
+        A.w = fmaf(wgt, v.w, A.w);
       }
     }
-    if (d < head_dim) out[row * head_dim + d] = Tag::from_f32(A * inv);
+    part_sum[tid] = A;
+    __syncthreads();
+    if (tid < q4) {
+      float4 t = part_sum[tid];
+      for (int k = 1; k < lanes_per_part; ++k) {
+        const float4 u = part_sum[k * q4 + tid];
+        t.x += u.x;
+        t.y += u.y;
+        t.z += u.z;
+        t.w += u.w;
+      }
+      const float inv = 1.f / L;
+      typename Tag::Bits* o = out + row * head_dim + 4 * tid;
+      o[0] = Tag::from_f32(t.x * inv);
+      o[1] = Tag::from_f32(t.y * inv);
+      o[2] = Tag::from_f32(t.z * inv);
+      o[3] = Tag::from_f32(t.w * inv);
+    }
+    __syncthreads();  // part_sum is reused by the next row
   }
 }
 
@@ -591,73 +611,59 @@ bool resolve_split(int partition_size, int num_seqs, int hkv, int max_len, Split
   return true;
 }
 
-size_t workspace_bytes(int num_seqs, int hq, int head_dim, const Split& sp) {
-  if (sp.np <= 1) return 0;
-  const size_t parts = static_cast<size_t>(num_seqs) * hq * sp.np;
-  return align_up(parts * 2 * sizeof(float)) + align_up(parts * head_dim * sizeof(float));
+// Workspace: [plan: meta (256 B), items, split list] [m, l of every partial]
+// [acc of every partial]; the partial areas exist only when some sequence is
+// split.  Every call rewrites what it reads.
+struct Layout {
+  size_t meta, items, split, ml, acc, total;
+};
+
+Layout workspace_layout(int num_seqs, int hq, int head_dim, const Split& sp) {
+  Layout l;
+  const size_t cap = static_cast<size_t>(num_seqs) * sp.np;
+  l.meta = 0;
+  l.items = kAlign;
+  l.split = l.items + align_up(cap * sizeof(int4));
+  l.ml = l.split + align_up(static_cast<size_t>(num_seqs) * sizeof(int));
+  l.acc = l.ml;
+  l.total = l.ml;
+  if (sp.np > 1) {
+    const size_t parts = cap * hq;
+    l.acc = l.ml + align_up(parts * 2 * sizeof(float));
+    l.total = l.acc + align_up(parts * head_dim * sizeof(float));
+  }
+  return l;
 }
 
 bool mfma_path(pa_dtype dt, int head_dim) {
   return (dt == PA_BF16 || dt == PA_F16) && (head_dim == 64 || head_dim == 128);
 }
 
-// Work-groups of `kern` resident on the current device at once (cached per
-// device, kernel and LDS size).
-int resident_groups(const void* kern, size_t lds_bytes) {
-  struct Entry {
-    int dev;
-    const void* kern;
-    size_t lds;
-    int groups;
-  };
-  static std::mutex mu;
-  static std::vector<Entry> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  for (const Entry& e : cache)
-    if (e.dev == dev && e.kern == kern && e.lds == lds_bytes) return e.groups;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds_bytes) !=
-          hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  const int n = max(per_cu, 0) * max(cus, 0);
-  cache.push_back({dev, kern, lds_bytes, n});
-  return n;
-}
-
-template <typename Tag, int D>
-pa_status launch_mfma(const DecodeArgs& a, hipStream_t st) {
-  const int heads = a.hkv * a.head_blocks;
-  const int64_t upper = static_cast<int64_t>(a.np_max) * a.num_seqs * heads;
-  const size_t comb = comb_floats(a.nh_max, D) * sizeof(float);
-  if (a.num_seqs <= kMaxSchedSeqs && a.part_size / kBlock + 1 <= kMaxBuckets &&
-      upper <= 0x7fffffff) {
-    const size_t lds = comb + sizeof(int) * (4 * static_cast<size_t>(a.num_seqs) + 1 +
-                                             a.part_size / kBlock + 1 + kWaves);
-    const void* kern = reinterpret_cast<const void*>(&decode_persistent_kernel<Tag, D>);
-    const int resident = resident_groups(kern, lds);
-    if (resident > 0) {
-      const int grid = static_cast<int>(std::min<int64_t>(resident, upper));
-      decode_persistent_kernel<Tag, D><<<dim3(grid), dim3(kThreads), lds, st>>>(a);
-      return launch_status();
-    }
-  }
-  if (upper > 0x7fffffff) return PA_ERR_INVALID_ARG;
-  decode_grid_kernel<Tag, D><<<dim3(static_cast<uint32_t>(upper)), dim3(kThreads), comb, st>>>(a);
-  return launch_status();
-}
-
 template <typename Tag>
 pa_status launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
                  const int32_t* lens, float scale_log2, void* out, int num_seqs, int hq, int hkv,
-                 int head_dim, int max_blocks, const Split& sp, float* ws_ml, float* ws_acc,
-                 bool use_mfma, hipStream_t st) {
+                 int head_dim, int max_blocks, const Split& sp, char* ws, bool use_mfma,
+                 hipStream_t st) {
   using E = typename Tag::Bits;
   const int group = hq / hkv;
-  if (!use_mfma && static_cast<int64_t>(sp.np) * num_seqs * hq > 0x7fffffff)
-    return PA_ERR_INVALID_ARG;
+  const int head_blocks = use_mfma ? (group + 15) / 16 : 1;
+  const int64_t grid = use_mfma ? static_cast<int64_t>(sp.np) * num_seqs * hkv * head_blocks
+                                : static_cast<int64_t>(sp.np) * num_seqs * hq;
+  if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
+  const Layout lay = workspace_layout(num_seqs, hq, head_dim, sp);
+  int* meta = reinterpret_cast<int*>(ws + lay.meta);
+  int4* items = reinterpret_cast<int4*>(ws + lay.items);
+  int* split = reinterpret_cast<int*>(ws + lay.split);
+  float* ws_ml = reinterpret_cast<float*>(ws + lay.ml);
+  float* ws_acc = reinterpret_cast<float*>(ws + lay.acc);
+  if (use_mfma || sp.np > 1) {
+    PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np};
+    const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);
+    decode_plan_kernel<<<dim3(1), dim3(kThreads), 0, st>>>(pa);
+    const pa_status ps = launch_status();
+    timing_stop(pslot, st);
+    if (ps != PA_OK) return ps;
+  }
   int slot = timing_start(PA_KERNEL_DECODE, st);
   pa_status status = PA_OK;
   if (use_mfma) {
@@ -676,16 +682,21 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
       a.hq_total = hq;
       a.hkv = hkv;
       a.group = group;
-      a.head_blocks = (group + 15) / 16;
+      a.head_blocks = head_blocks;
       a.max_blocks = max_blocks;
       a.part_size = sp.part;
       a.np_max = sp.np;
       a.nh_max = std::min(16, group);
-      status = head_dim == 128 ? launch_mfma<Tag, 128>(a, st) : launch_mfma<Tag, 64>(a, st);
+      const size_t lds = comb_floats(a.nh_max, head_dim) * sizeof(float);
+      const dim3 g3(static_cast<uint32_t>(grid)), b3(kThreads);
+      if (head_dim == 128)
+        decode_items_kernel<Tag, 128><<<g3, b3, lds, st>>>(a, items);
+      else
+        decode_items_kernel<Tag, 64><<<g3, b3, lds, st>>>(a, items);
+      status = launch_status();
     }
   } else {
-    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(sp.np) * num_seqs * hq));
-    decode_generic_kernel<Tag><<<grid, dim3(kThreads), 0, st>>>(
+    decode_generic_kernel<Tag><<<dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, st>>>(
         static_cast<const E*>(q), static_cast<const E*>(k_cache), static_cast<const E*>(v_cache),
         tables, lens, scale_log2, static_cast<E*>(out), ws_ml, ws_acc, num_seqs, hq, hkv, group,
         head_dim, max_blocks, sp.part, sp.np);
@@ -694,8 +705,10 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   timing_stop(slot, st);
   if (status != PA_OK || sp.np <= 1) return status;
   slot = timing_start(PA_KERNEL_DECODE_REDUCE, st);
-  decode_reduce_kernel<Tag><<<dim3(static_cast<uint32_t>(num_seqs * hq)), dim3(kWave), 0, st>>>(
-      ws_ml, ws_acc, lens, static_cast<E*>(out), hq, head_dim, max_blocks, sp.part, sp.np);
+  const int rows = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(num_seqs) * hq, 2048));
+  decode_reduce_kernel<Tag><<<dim3(rows), dim3(kThreads), 0, st>>>(
+      ws_ml, ws_acc, split, meta, lens, static_cast<E*>(out), hq, head_dim, max_blocks, sp.part,
+      sp.np);
   status = launch_status();
   timing_stop(slot, st);
   return status;
@@ -720,7 +733,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
   // the auto choice does not depend on the KV head count today; pass 1
   if (!pa::resolve_split(partition_size, num_seqs, 1, max_context_len, &sp)) return 0;
-  return pa::workspace_bytes(num_seqs, num_q_heads, head_dim, sp);
+  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
 }
 
 pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -746,17 +759,10 @@ pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const vo
   Split sp;
   if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp))
     return PA_ERR_INVALID_ARG;
-  const size_t need = pa::workspace_bytes(num_seqs, num_q_heads, head_dim, sp);
-  if (need > 0 && (!workspace || workspace_bytes < need ||
-                   reinterpret_cast<uintptr_t>(workspace) % kAlign != 0))
+  const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
     return PA_ERR_WORKSPACE;
-  float* ws_ml = static_cast<float*>(workspace);
-  float* ws_acc = nullptr;
-  if (need > 0) {
-    const size_t parts = static_cast<size_t>(num_seqs) * num_q_heads * sp.np;
-    ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      align_up(parts * 2 * sizeof(float)));
-  }
+  char* ws = static_cast<char*>(workspace);
   const float scale_log2 = scale * kLog2e;
   const bool use_mfma = mfma_path(dtype, head_dim);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -764,15 +770,15 @@ pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const vo
     case PA_BF16:
       return launch<BF16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                            num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
-                           ws_ml, ws_acc, use_mfma, st);
+                           ws, use_mfma, st);
     case PA_F16:
       return launch<F16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
-                          ws_ml, ws_acc, use_mfma, st);
+                          ws, use_mfma, st);
     default:
       return launch<F32T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
-                          ws_ml, ws_acc, false, st);
+                          ws, false, st);
   }
 }
 

@@ -59,18 +59,27 @@ def test_host_only_calls_and_argument_errors_without_a_gpu():
                                        ctypes.c_void_p(16), ctypes.c_void_p(16),
                                        ctypes.c_void_p(16), 1.0, ctypes.c_void_p(16), 4, 8, 4,
                                        128, 64, 1024, 256, None, 0, 2, None)
-    assert st == -6  # split without a workspace
+    assert st == -6  # no workspace
+    st = lib.pa_paged_attention_decode(ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                       ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                       ctypes.c_void_p(16), 1.0, ctypes.c_void_p(16), 4, 8, 4,
+                                       128, 64, 1024, 256, ctypes.c_void_p(256), 1024, 2, None)
+    assert st == -6  # workspace without room for the partials
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 4, 2, 64, 0, None) == 0
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 1, 4, 2, 64, 0, None) == -1
     assert lib.pa_copy_blocks(None, None, None, 0, 4, 2, 60, 2, None) == -1
 
 
 def test_workspace_size_closed_form():
-    # 4 sequences x 8 heads x ceil(1024/256) partitions, (2 + 128) fp32 each, 256-B aligned
-    parts = 4 * 8 * 4
-    want = -(-parts * 2 * 4 // 256) * 256 + -(-parts * 128 * 4 // 256) * 256
-    assert pa.decode_workspace_bytes(4, 8, 128, 1024, 256) == want
-    assert pa.decode_workspace_bytes(4, 8, 128, 1024, pa.PARTITION_NONE) == 0
-    assert pa.decode_workspace_bytes(4, 8, 128, 256, 256) == 0
+    # plan (256-byte meta, 16 B per sequence and partition, 4 B per sequence),
+    # then m, l and acc of every (sequence, query head, partition), each 256-B aligned
+    def up(x):
+        return -(-x // 256) * 256
+    s, hq, d, np_ = 4, 8, 128, 4
+    plan = 256 + up(16 * s * np_) + up(4 * s)
+    parts = s * hq * np_
+    assert pa.decode_workspace_bytes(s, hq, d, 1024, 256) == plan + up(8 * parts) + up(4 * d * parts)
+    assert pa.decode_workspace_bytes(s, hq, d, 1024, pa.PARTITION_NONE) == 256 + up(16 * s) + up(4 * s)
+    assert pa.decode_workspace_bytes(s, hq, d, 256, 256) == 256 + up(16 * s) + up(4 * s)
     with pytest.raises(ValueError):
         pa.Pool(4, free_order=[0, 1])

@@ -85,13 +85,31 @@ def test_zero_length_rows_give_zeros_and_others_unaffected():
     assert np.array_equal(got[[0, 2]], db.out_bits()[[0, 2]])
 
 
-def test_more_sequences_than_the_persistent_schedule_holds():
-    # 1100 short sequences take the one-item-per-work-group kernel
+def test_many_sequences():
+    # more sequences than threads of the plan kernel: several per thread
     print("[gpu] 1100 sequences", flush=True)
     lens = (np.arange(1100) % 45) + 1
     w = workloads.make_custom(lens, hq=8, hkv=2, d=64, dtype="bf16", seed=5)
     db, ref = _run_small(w, 16)
     assert_close(db.out_bits(), ref, "bf16", "1100 sequences")
+
+
+def test_stale_workspace_does_not_matter():
+    # the workspace is scratch: a NaN-filled one and a reused one give the same bits
+    import torch
+    print("[gpu] stale workspace", flush=True)
+    w = workloads.make_custom([5, 300, 1000, 2], hq=8, hkv=2, d=128, dtype="bf16", seed=3)
+    db, ref = _run_small(w, 64)
+    kc, vc = db.caches[0]
+    need = pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim, db.max_context_len, 64)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
+    for _ in range(3):
+        out = torch.empty_like(db.out)
+        pa.paged_attention_decode(db.q, kc, vc, db.tables, db.context_lens, w.scale, out,
+                                  max_context_len=db.max_context_len, partition_size=64,
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(out), db.out_bits())
 
 
 def test_nan_in_table_padding_and_block_tails_does_not_leak():
