@@ -12,8 +12,8 @@ so that reads come from HBM, not from the 256 MB last-level cache.
 
 Prints one JSON line.  `value` is the step's algorithmic bytes over its wall
 time (GB/s); `roofline` is the decode main pass alone, timed with HIP events
-on its own stream; `cpu_baseline` is the oracle on a bounded sample of the same
-batch on the host cores.
+on its own stream in a second pass of the same steps; `cpu_baseline` is the
+oracle on a bounded sample of the same batch on the host cores.
 """
 import argparse
 import hashlib
@@ -72,6 +72,45 @@ def load_traffic(workload):
     return t.get("bytes_per_launch")
 
 
+def pmc_summary(fetch_dir, write_dir, workload, out_path=TRAFFIC_FILE):
+    """HBM bytes per decode launch from two rocprofv3 --pmc runs of this bench
+    (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch), each scaled by
+    what the same counter reads for the run's plain 1 GiB device copy."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, counter):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                out += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+        if not out:
+            raise SystemExit(f"no {counter} rows under {d}")
+        return out
+
+    result = {"workload": workload, "source_sha256_16": source_hash()}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rs = rows(d, counter)
+        copies = [r for r in rs if "copyBuffer" in r["Kernel_Name"]]
+        big = max(int(r["Grid_Size"]) for r in copies)
+        cal = statistics.median(float(r["Counter_Value"]) for r in copies
+                                if int(r["Grid_Size"]) == big)
+        factor = (1 << 30) / 1024.0 / cal  # the copy moves 1 GiB each way
+        dec = [float(r["Counter_Value"]) for r in rs if "decode_items_kernel" in r["Kernel_Name"]
+               or "decode_generic_kernel" in r["Kernel_Name"]]
+        kib = statistics.median(dec)
+        result[counter] = {"kib_per_dispatch_raw": kib, "calibration_factor": round(factor, 4),
+                           "bytes_per_launch": int(kib * 1024 * factor),
+                           "dispatches": len(dec)}
+    result["bytes_per_launch"] = (result["FETCH_SIZE"]["bytes_per_launch"]
+                                  + result["WRITE_SIZE"]["bytes_per_launch"])
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
+        json.dump(result, f, indent=1)
+    print(json.dumps(result))
+
+
 def cpu_baseline(w, budget_s):
     """The oracle (fp64 NumPy) on the first sequences of the batch, ~budget_s of work."""
     import numpy as np
@@ -124,7 +163,17 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 plain device copies of MIB MiB (a known-size "
                          "reference for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "bench, taken with --calibrate-copy 1024, into " + TRAFFIC_FILE)
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        import workloads
+        pmc_summary(*args.pmc_summary, workloads.CONFIG_NAMES[int(args.config)
+                                                               if args.config.isdigit()
+                                                               else args.config])
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -159,13 +208,20 @@ def main():
         db.step(copy=i % copies, partition_size=args.partition)
     torch.cuda.synchronize()
 
-    pa.timing_begin(8 * args.steps + 16)
+    # timed region: K steps, nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         db.step(copy=i % copies, partition_size=args.partition)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # the same K steps again with HIP events around every library kernel, on
+    # the stream it runs on (events add a few microseconds per launch, so they
+    # stay out of the region above)
+    pa.timing_begin(8 * args.steps + 16)
+    for i in range(args.steps):
+        db.step(copy=i % copies, partition_size=args.partition)
+    torch.cuda.synchronize()
     kt = pa.timing_end()
 
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -200,7 +256,7 @@ def main():
         "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "kernels_ms_per_step": {k: round(v["ms"] / max(1, v["launches"]), 5)
                                 for k, v in kt.items() if v["launches"]},
-        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel" if w.dtype != "f32"
+        "roofline": {"bound": "hbm", "kernel": "decode_items_kernel" if w.dtype != "f32"
                      else "decode_generic_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -17,7 +17,8 @@ of n=1).
 Readings where the pages leave a step open (listed in the design doc):
 * the pool is a stack seeded from ``free_order``: the first ``alloc`` returns
   ``free_order[0]``; a block whose count drops to 0 is pushed back and is the
-  next one handed out (the page's "someone else takes it immediately");
+  next one handed out (in the shelves example a returned shelf is reused
+  right away);
 * blocks of one append are taken in logical order; a copy-on-write destination
   is taken before any fresh block of the same append;
 * a write into a block whose reference count is above 1 copies it first, the

@@ -595,10 +595,17 @@ struct Split {
   int np;
 };
 
+// Partitions of 1024 positions keep split overhead (partials, merge) near 1 %
+// of the K/V bytes; shorter ones are used only when the batch would otherwise
+// give fewer than ~2048 work items (a few long sequences), so that every CU
+// has work.  Batches whose longest sequence fits one partition are not split.
 int auto_partition(int num_seqs, int hkv, int max_len) {
-  (void)num_seqs;
-  (void)hkv;
-  return max_len <= 512 ? 0 : 512;
+  if (max_len <= 1024) return PA_PARTITION_NONE;
+  int ps = 1024;
+  while (ps > 256 &&
+         static_cast<int64_t>(num_seqs) * ((max_len + ps - 1) / ps) * hkv < 2048)
+    ps /= 2;
+  return ps;
 }
 
 bool resolve_split(int partition_size, int num_seqs, int hkv, int max_len, Split* out) {
@@ -731,7 +738,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t max_context_len, int32_t partition_size) {
   pa::Split sp;
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-  // the auto choice does not depend on the KV head count today; pass 1
+  // the automatic choice shrinks partitions for fewer KV heads, so sizing with
+  // one KV head covers every head count
   if (!pa::resolve_split(partition_size, num_seqs, 1, max_context_len, &sp)) return 0;
   return pa::workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
 }
