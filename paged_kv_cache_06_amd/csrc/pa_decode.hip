@@ -130,15 +130,58 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int len) {
   return min(max(len, 0), a.max_blocks * kBlock);
 }
 
+// The loads that start a work item (its block ids and its q rows), issued
+// before the item runs so that they can overlap earlier work.
+template <int D>
+struct ItemPrep {
+  int s, p, g, hb, len;
+  int ids;              // lane j: id of this wave's j-th block (first 64)
+  uint4 qf[D / 32];     // B operand of the QK products: head lane%16, k-group lane/16
+};
+
+template <typename Tag, int D, int W>
+__device__ __forceinline__ void prep_item(const DecodeArgs& a, int s, int p, int g, int hb,
+                                          int len, ItemPrep<D>& it) {
+  constexpr int kSteps = D / 32;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int n = lane & 15;
+  const int kg = lane >> 4;
+  it.s = s;
+  it.p = p;
+  it.g = g;
+  it.hb = hb;
+  it.len = len;
+  const int h0 = hb * 16;
+  const int nh = min(16, a.group - h0);
+  const int start = p * a.part_size;
+  const int end = min(len, start + a.part_size);
+  const int nblk = max(end - start + kBlock - 1, 0) / kBlock;
+  const int my_blocks = nblk > wave ? (nblk - wave + W - 1) / W : 0;
+  const int32_t* trow =
+      a.tables + static_cast<size_t>(s) * a.max_blocks + start / kBlock + wave;
+  it.ids = lane < my_blocks ? trow[W * lane] : 0;
+  if (n < nh) {
+    const uint16_t* qp = a.q + (static_cast<size_t>(s) * a.hq_total + g * a.group + h0 + n) * D;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j)
+      it.qf[j] = *reinterpret_cast<const uint4*>(qp + (j * 4 + kg) * 8);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) it.qf[j] = make_uint4(0, 0, 0, 0);
+  }
+}
+
 // One work item: positions [p*P, min(len, (p+1)*P)) of sequence s against KV
-// head g for query heads h0 .. h0+nh-1 of its group.  `comb` is LDS of
-// kWaves * (2 + D) * nh_max floats.  Ends with the result stored; the caller
-// must __syncthreads() before reusing `comb`.
-template <typename Tag, int D>
-__device__ void decode_item(const DecodeArgs& a, int s, int p, int g, int hb, int len,
-                            float* comb) {
+// head g for query heads h0 .. h0+nh-1 of its group, served by W waves; each
+// wave issues the loads of B of its blocks before using any of them.  `comb`
+// is LDS of comb_floats(W, nh_max, D) floats.  Ends with the result stored;
+// the caller must __syncthreads() before reusing `comb`.
+template <typename Tag, int D, int W, int B>
+__device__ void run_item(const DecodeArgs& a, const ItemPrep<D>& it, float* comb) {
   constexpr int kSteps = D / 32;   // QK k-steps of 32 dims
   constexpr int kSlices = D / 16;  // PV output slices of 16 dims
+  const int s = it.s, p = it.p, g = it.g, hb = it.hb, len = it.len;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n = lane & 15;   // token row (K, scores) / head column (Q, P, acc)
@@ -150,22 +193,11 @@ __device__ void decode_item(const DecodeArgs& a, int s, int p, int g, int hb, in
   const int nblk = max(end - start + kBlock - 1, 0) / kBlock;
   const int blk0 = start / kBlock;
   const int nparts = min((len + a.part_size - 1) / a.part_size, a.np_max);
-  // this wave's blocks: blk0 + wave + kWaves * j, j < my_blocks
-  const int my_blocks = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
-
-  // block ids of this wave, 64 at a time: lane j holds the id of its j-th block
+  // this wave's blocks: blk0 + wave + W * j, j < my_blocks
+  const int my_blocks = nblk > wave ? (nblk - wave + W - 1) / W : 0;
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks + blk0 + wave;
-  int ids = lane < my_blocks ? trow[kWaves * lane] : 0;
-
-  uint4 qf[kSteps];
-  if (n < nh) {
-    const uint16_t* qp = a.q + (static_cast<size_t>(s) * a.hq_total + g * a.group + h0 + n) * D;
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) qf[j] = *reinterpret_cast<const uint4*>(qp + (j * 4 + kg) * 8);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) qf[j] = make_uint4(0, 0, 0, 0);
-  }
+  int ids = it.ids;
+  const uint4* qf = it.qf;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4_t acc[kSlices];
@@ -177,70 +209,80 @@ __device__ void decode_item(const DecodeArgs& a, int s, int p, int g, int hb, in
   const uint16_t* vbase = a.v_cache + static_cast<size_t>(g) * head_elems;
   const size_t block_stride = static_cast<size_t>(a.hkv) * head_elems;
 
-  for (int j = 0; j < my_blocks; ++j) {
-    if (j > 0 && (j & 63) == 0) {  // next 64 block ids
-      const int jj = j + lane;
-      ids = jj < my_blocks ? trow[kWaves * jj] : 0;
+  for (int j0 = 0; j0 < my_blocks; j0 += B) {
+    if (j0 > 0 && (j0 & 63) < B) {  // the batch starts in the next 64 block ids
+      const int jj = (j0 & ~63) + lane;
+      ids = jj < my_blocks ? trow[W * jj] : 0;
     }
-    const int phys = __builtin_amdgcn_readlane(ids, j & 63);
-    const uint16_t* kb = kbase + static_cast<size_t>(phys) * block_stride;
-    const uint16_t* vb = vbase + static_cast<size_t>(phys) * block_stride;
-    uint4 kf[kSteps];
+    uint4 kf[B][kSteps];
+    uint2 vf[B][kSlices];
 #pragma unroll
-    for (int t = 0; t < kSteps; ++t) kf[t] = *reinterpret_cast<const uint4*>(kb + t * 512 + lane * 8);
-    uint2 vf[kSlices];
+    for (int b = 0; b < B; ++b) {
+      if (j0 + b < my_blocks) {
+        const int phys = __builtin_amdgcn_readlane(ids, (j0 + b) & 63);
+        const uint16_t* kb = kbase + static_cast<size_t>(phys) * block_stride;
+        const uint16_t* vb = vbase + static_cast<size_t>(phys) * block_stride;
 #pragma unroll
-    for (int sl = 0; sl < kSlices; ++sl)
-      vf[sl] = *reinterpret_cast<const uint2*>(vb + (sl * 16 + n) * kBlock + kg * 4);
-
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < kSteps; ++t)
+          kf[b][t] = *reinterpret_cast<const uint4*>(kb + t * 512 + lane * 8);
 #pragma unroll
-    for (int t = 0; t < kSteps; ++t) sc = Mfma<Tag>::qk(kf[t], qf[t], sc);
-
-    const int blk = blk0 + wave + kWaves * j;
-    const int pos0 = blk * kBlock + kg * 4;  // position of this lane's first score
-    float s4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s4[r] = (pos0 + r < end) ? sc[r] * a.scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    float p4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p4[r] = fast_exp2(s4[r] - m_new);
-    l_run = fmaf(l_run, alpha, (p4[0] + p4[1]) + (p4[2] + p4[3]));
-    m_run = m_new;
-#pragma unroll
-    for (int sl = 0; sl < kSlices; ++sl) acc[sl] *= alpha;
-
-    if ((blk + 1) * kBlock > end) {  // tail block: zero V of masked positions
-      const uint32_t lo = (pos0 + 0 < end ? 0x0000FFFFu : 0u) | (pos0 + 1 < end ? 0xFFFF0000u : 0u);
-      const uint32_t hi = (pos0 + 2 < end ? 0x0000FFFFu : 0u) | (pos0 + 3 < end ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int sl = 0; sl < kSlices; ++sl) {
-        vf[sl].x &= lo;
-        vf[sl].y &= hi;
+        for (int sl = 0; sl < kSlices; ++sl)
+          vf[b][sl] = *reinterpret_cast<const uint2*>(vb + (sl * 16 + n) * kBlock + kg * 4);
       }
     }
-    // P as hi + lo in the storage dtype: two products, near-fp32 weights
-    const uint2 ph = Mfma<Tag>::pack(p4[0], p4[1], p4[2], p4[3]);
-    const uint2 pl = Mfma<Tag>::pack(p4[0] - Mfma<Tag>::lo(ph.x), p4[1] - Mfma<Tag>::hi(ph.x),
-                                     p4[2] - Mfma<Tag>::lo(ph.y), p4[3] - Mfma<Tag>::hi(ph.y));
 #pragma unroll
-    for (int sl = 0; sl < kSlices; ++sl) {
-      acc[sl] = Mfma<Tag>::pv(vf[sl], ph, acc[sl]);
-      acc[sl] = Mfma<Tag>::pv(vf[sl], pl, acc[sl]);
+    for (int b = 0; b < B; ++b) {
+      if (j0 + b >= my_blocks) break;
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < kSteps; ++t) sc = Mfma<Tag>::qk(kf[b][t], qf[t], sc);
+
+      const int blk = blk0 + wave + W * (j0 + b);
+      const int pos0 = blk * kBlock + kg * 4;  // position of this lane's first score
+      float s4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s4[r] = (pos0 + r < end) ? sc[r] * a.scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      float p4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p4[r] = fast_exp2(s4[r] - m_new);
+      l_run = fmaf(l_run, alpha, (p4[0] + p4[1]) + (p4[2] + p4[3]));
+      m_run = m_new;
+#pragma unroll
+      for (int sl = 0; sl < kSlices; ++sl) acc[sl] *= alpha;
+
+      if ((blk + 1) * kBlock > end) {  // tail block: zero V of masked positions
+        const uint32_t lo =
+            (pos0 + 0 < end ? 0x0000FFFFu : 0u) | (pos0 + 1 < end ? 0xFFFF0000u : 0u);
+        const uint32_t hi =
+            (pos0 + 2 < end ? 0x0000FFFFu : 0u) | (pos0 + 3 < end ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int sl = 0; sl < kSlices; ++sl) {
+          vf[b][sl].x &= lo;
+          vf[b][sl].y &= hi;
+        }
+      }
+      // P as hi + lo in the storage dtype: two products, near-fp32 weights
+      const uint2 ph = Mfma<Tag>::pack(p4[0], p4[1], p4[2], p4[3]);
+      const uint2 pl = Mfma<Tag>::pack(p4[0] - Mfma<Tag>::lo(ph.x), p4[1] - Mfma<Tag>::hi(ph.x),
+                                       p4[2] - Mfma<Tag>::lo(ph.y), p4[3] - Mfma<Tag>::hi(ph.y));
+#pragma unroll
+      for (int sl = 0; sl < kSlices; ++sl) {
+        acc[sl] = Mfma<Tag>::pv(vf[b][sl], ph, acc[sl]);
+        acc[sl] = Mfma<Tag>::pv(vf[b][sl], pl, acc[sl]);
+      }
     }
   }
 
-  // per-wave partials to LDS: comb = [m: kWaves][nh_max] [l: kWaves][nh_max]
-  //                                  [acc: kWaves][nh_max][D]
+  // per-wave partials to LDS: comb = [m: W][nh_max] [l: W][nh_max] [acc: W][nh_max][D]
   const int nhm = a.nh_max;
   float* cm = comb;
-  float* cl = comb + kWaves * nhm;
-  float* ca = comb + 2 * kWaves * nhm;
+  float* cl = comb + W * nhm;
+  float* ca = comb + 2 * W * nhm;
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (n < nh) {
@@ -255,15 +297,15 @@ __device__ void decode_item(const DecodeArgs& a, int s, int p, int g, int hb, in
   __syncthreads();
 
   const size_t row0 = static_cast<size_t>(s) * a.hq_total + g * a.group + h0;
-  for (int e = threadIdx.x; e < nh * D; e += kThreads) {
+  for (int e = threadIdx.x; e < nh * D; e += W * kWave) {
     const int h = e / D, d = e % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * nhm + h]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, cm[w * nhm + h]);
     float L = 0.f, A = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float f = fast_exp2(cm[w * nhm + h] - M);
         L = fmaf(f, cl[w * nhm + h], L);
         A = fmaf(f, ca[(w * nhm + h) * D + d], A);
@@ -283,9 +325,24 @@ __device__ void decode_item(const DecodeArgs& a, int s, int p, int g, int hb, in
   }
 }
 
-__host__ __device__ inline size_t comb_floats(int nh_max, int head_dim) {
-  return static_cast<size_t>(kWaves) * nh_max * (2 + head_dim);
+__host__ __device__ inline size_t comb_floats(int waves, int nh_max, int head_dim) {
+  return static_cast<size_t>(waves) * nh_max * (2 + head_dim);
 }
+
+// Waves per decode work-group and blocks each wave loads together.
+#ifndef PA_ITEM_WAVES
+#define PA_ITEM_WAVES 4
+#endif
+#ifndef PA_ITEM_BATCH
+#define PA_ITEM_BATCH 1
+#endif
+#ifndef PA_ITEMS_PER_GROUP
+#define PA_ITEMS_PER_GROUP 1
+#endif
+constexpr int kItemWaves = PA_ITEM_WAVES;
+constexpr int kItemBatch = PA_ITEM_BATCH;
+constexpr int kItemsPerGroup = PA_ITEMS_PER_GROUP;  // work items per work-group
+constexpr int kItemThreads = kItemWaves * kWave;
 
 // Size class of a last partition: 0 (the largest) .. kClasses - 1 (an empty
 // sequence).  Classes 0..5 are sixths of a partition, largest first; class 6
@@ -295,6 +352,13 @@ __device__ __forceinline__ int size_class(int tokens, int part_size) {
   if (tokens <= 0) return kClasses - 1;
   if (tokens * 64 < part_size) return kClasses - 2;
   return 6 - (tokens * 6 + part_size - 1) / part_size;
+}
+
+// Entries of the item list: every (sequence, partition), rounded up to a
+// multiple of 32 (a whole number of work-groups' items) and padded with end
+// markers.
+__host__ __device__ inline int plan_capacity(int num_seqs, int np_max) {
+  return (num_seqs * np_max + 31) / 32 * 32;
 }
 
 struct PlanArgs {
@@ -384,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
     if (np > 1) a.split[split_pos++] = i;
   }
   const int total = num_full + S;
-  const int cap = S * a.np_max;
+  const int cap = plan_capacity(S, a.np_max);
   for (int u = total + threadIdx.x; u < cap; u += kThreads) a.items[u] = make_int4(-1, 0, 0, 0);
   for (int i = all[kClasses + 1] + threadIdx.x; i < S; i += kThreads) a.split[i] = -1;
   if (threadIdx.x == 0) {
@@ -396,14 +460,31 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
 // Work-group i serves item i / heads of the plan (heads = KV heads x query
 // head groups); work-groups past the list's end exit at once.
 template <typename Tag, int D>
-__global__ __launch_bounds__(kThreads, 4) void decode_items_kernel(DecodeArgs a,
-                                                                   const int4* __restrict__ items) {
+__global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_kernel(
+    DecodeArgs a, const int4* __restrict__ items) {
   extern __shared__ float comb[];
   const int heads = a.hkv * a.head_blocks;
-  const int4 it = items[blockIdx.x / heads];
-  if (it.x < 0) return;
+  // items u0 .. u0 + kItemsPerGroup - 1 (neighbours in the list, so of similar
+  // size), all for head gh; the later items' block ids and q are loaded
+  // up front so their start overlaps the earlier items
+  const int u0 = (blockIdx.x / heads) * kItemsPerGroup;
   const int gh = blockIdx.x % heads;
-  decode_item<Tag, D>(a, it.x, it.y, gh / a.head_blocks, gh % a.head_blocks, it.z, comb);
+  ItemPrep<D> prep[kItemsPerGroup];
+  int valid = 0;
+#pragma unroll
+  for (int k = 0; k < kItemsPerGroup; ++k) {
+    const int4 it = items[u0 + k];
+    if (it.x < 0) break;
+    prep_item<Tag, D, kItemWaves>(a, it.x, it.y, gh / a.head_blocks, gh % a.head_blocks, it.z,
+                                  prep[k]);
+    ++valid;
+  }
+#pragma unroll
+  for (int k = 0; k < kItemsPerGroup; ++k) {
+    if (k >= valid) break;
+    if (k > 0) __syncthreads();  // comb is reused
+    run_item<Tag, D, kItemWaves, kItemBatch>(a, prep[k], comb);
+  }
 }
 
 // ---- generic VALU path ----
@@ -627,7 +708,7 @@ struct Layout {
 
 Layout workspace_layout(int num_seqs, int hq, int head_dim, const Split& sp) {
   Layout l;
-  const size_t cap = static_cast<size_t>(num_seqs) * sp.np;
+  const size_t cap = static_cast<size_t>(plan_capacity(num_seqs, sp.np));
   l.meta = 0;
   l.items = kAlign;
   l.split = l.items + align_up(cap * sizeof(int4));
@@ -635,7 +716,7 @@ Layout workspace_layout(int num_seqs, int hq, int head_dim, const Split& sp) {
   l.acc = l.ml;
   l.total = l.ml;
   if (sp.np > 1) {
-    const size_t parts = cap * hq;
+    const size_t parts = static_cast<size_t>(num_seqs) * sp.np * hq;
     l.acc = l.ml + align_up(parts * 2 * sizeof(float));
     l.total = l.acc + align_up(parts * head_dim * sizeof(float));
   }
@@ -654,9 +735,10 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   using E = typename Tag::Bits;
   const int group = hq / hkv;
   const int head_blocks = use_mfma ? (group + 15) / 16 : 1;
-  const int64_t grid = use_mfma ? static_cast<int64_t>(sp.np) * num_seqs * hkv * head_blocks
+  if (static_cast<int64_t>(sp.np) * num_seqs * hq > 0x7fffffff / 2) return PA_ERR_INVALID_ARG;
+  const int64_t grid = use_mfma ? static_cast<int64_t>(plan_capacity(num_seqs, sp.np)) /
+                                      kItemsPerGroup * hkv * head_blocks
                                 : static_cast<int64_t>(sp.np) * num_seqs * hq;
-  if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
   const Layout lay = workspace_layout(num_seqs, hq, head_dim, sp);
   int* meta = reinterpret_cast<int*>(ws + lay.meta);
   int4* items = reinterpret_cast<int4*>(ws + lay.items);
@@ -694,8 +776,8 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
       a.part_size = sp.part;
       a.np_max = sp.np;
       a.nh_max = std::min(16, group);
-      const size_t lds = comb_floats(a.nh_max, head_dim) * sizeof(float);
-      const dim3 g3(static_cast<uint32_t>(grid)), b3(kThreads);
+      const size_t lds = comb_floats(kItemWaves, a.nh_max, head_dim) * sizeof(float);
+      const dim3 g3(static_cast<uint32_t>(grid)), b3(kItemThreads);
       if (head_dim == 128)
         decode_items_kernel<Tag, 128><<<g3, b3, lds, st>>>(a, items);
       else
