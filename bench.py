@@ -30,6 +30,8 @@ METRIC = "paged-attn decode achieved HBM GB/s (% of peak); attended KV tokens/s"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc", "pa_decode.hip")
+# main-pass kernels of a decode call: balanced split, fixed partitions, VALU path
+DECODE_KERNELS = ("decode_balanced_kernel", "decode_items_kernel", "decode_generic_kernel")
 
 
 def decode_bytes(w):
@@ -97,8 +99,8 @@ def pmc_summary(fetch_dir, write_dir, workload, out_path=TRAFFIC_FILE):
         cal = statistics.median(float(r["Counter_Value"]) for r in copies
                                 if int(r["Grid_Size"]) == big)
         factor = (1 << 30) / 1024.0 / cal  # the copy moves 1 GiB each way
-        dec = [float(r["Counter_Value"]) for r in rs if "decode_items_kernel" in r["Kernel_Name"]
-               or "decode_generic_kernel" in r["Kernel_Name"]]
+        dec = [float(r["Counter_Value"]) for r in rs
+               if any(k in r["Kernel_Name"] for k in DECODE_KERNELS)]
         kib = statistics.median(dec)
         result[counter] = {"kib_per_dispatch_raw": kib, "calibration_factor": round(factor, 4),
                            "bytes_per_launch": int(kib * 1024 * factor),
@@ -157,7 +159,7 @@ def main():
     ap.add_argument("--config", default="3", help="workload 1..5 or 4b (default 3)")
     ap.add_argument("--copies", type=int, default=0,
                     help="KV pool copies used round-robin (default: enough for >= 1.5 GB)")
-    ap.add_argument("--partition", type=int, default=-1, help="-1 auto, 0 none, else tokens")
+    ap.add_argument("--partition", type=int, default=-1, help="-1 auto, -2 balanced split, 0 none, else tokens")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -235,6 +237,12 @@ def main():
     ps = args.partition if args.partition != -1 else pa.decode_auto_partition(
         w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, db.max_context_len,
         {"f32": 0, "f16": 1, "bf16": 2}[w.dtype])
+    if ps == pa.PARTITION_BALANCED:
+        main_kernel = "decode_balanced_kernel"
+    elif w.dtype != "f32" and w.head_dim in (64, 128):
+        main_kernel = "decode_items_kernel"
+    else:
+        main_kernel = "decode_generic_kernel"
     result = {
         "metric": METRIC,
         "value": round(sbytes / (ms_step * 1e-3) / 1e9, 2),
@@ -256,8 +264,7 @@ def main():
         "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "kernels_ms_per_step": {k: round(v["ms"] / max(1, v["launches"]), 5)
                                 for k, v in kt.items() if v["launches"]},
-        "roofline": {"bound": "hbm", "kernel": "decode_items_kernel" if w.dtype != "f32"
-                     else "decode_generic_kernel",
+        "roofline": {"bound": "hbm", "kernel": main_kernel,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": dbytes,

@@ -65,6 +65,7 @@ typedef int32_t pa_dtype;
  * multiple of 16 */
 #define PA_PARTITION_NONE 0    /* one pass over each whole sequence, no partials */
 #define PA_PARTITION_AUTO (-1) /* the library picks */
+#define PA_PARTITION_BALANCED (-2) /* equal K/V blocks per work-group (matrix-core path) */
 
 /* Short English text of a status code (static storage). */
 const char* pa_status_string(pa_status status);
@@ -168,17 +169,29 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
                          int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
                          int32_t head_dim, pa_dtype dtype, void* stream);
 
-/* Workspace bytes pa_paged_attention_decode needs for these sizes: the work
- * list of the call (16 bytes per sequence and partition, 4 per sequence) plus,
- * when some sequence is split, the partial results (4 * (2 + head_dim) bytes
- * per sequence, query head and partition).  partition_size as for the decode
- * call.  0 on invalid sizes. */
+/* Workspace bytes pa_paged_attention_decode needs for these sizes.
+ * Fixed partitions (NONE or a positive size): the work list of the call (16
+ * bytes per sequence and partition, rounded up to 32 entries, and 4 per
+ * sequence) plus, when some sequence is split, the partial results
+ * (4 * (2 + head_dim) bytes per sequence, query head and partition).
+ * PA_PARTITION_BALANCED: 16 bytes per range start and two partial slots of
+ * min(16, num_q_heads) rows per work-group, for up to 2048 work-groups,
+ * whatever the lengths.  PA_PARTITION_AUTO: as for the partition size it
+ * resolves to.  Each area is 256-byte aligned after a 256-byte header.  0 on
+ * invalid sizes. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size);
 
-/* The partition size PA_PARTITION_AUTO resolves to for these sizes. */
+/* The partition size PA_PARTITION_AUTO resolves to for these sizes
+ * (PA_PARTITION_NONE or a positive multiple of 16). */
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
+
+/* Caps the work-groups of the balanced split at max_groups (0: no cap; the
+ * default is the number the device holds resident at once).  For sharing the
+ * GPU with concurrent work, and for tests.  Library-wide, not thread-safe
+ * against concurrent decode calls.  PA_ERR_INVALID_ARG if negative. */
+pa_status pa_decode_set_max_groups(int32_t max_groups);
 
 /* Decode attention over the paged cache:
  *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_s[t]) V_s[t],
@@ -194,10 +207,18 @@ int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   context_lens  device int32 [num_seqs]; counts the token being decoded
  *                 (its K/V must already be in the cache); 0 gives out = 0;
  *                 each must be <= max_context_len and <= 16 * max_blocks_per_seq
- *   partition_size  PA_PARTITION_NONE, PA_PARTITION_AUTO, or a positive
- *                 multiple of 16: sequences longer than it are split into
- *                 partitions of that many positions whose partial results are
- *                 merged by a second pass (running max / log-sum-exp rule)
+ *   partition_size  how the work is split:
+ *                 PA_PARTITION_BALANCED (matrix-core path only): the blocks
+ *                 of all (sequence, KV head) pairs are cut into one range of
+ *                 equal length per resident work-group; a pair cut by range
+ *                 boundaries is merged by a second pass (running max /
+ *                 log-sum-exp rule);
+ *                 a positive multiple of 16: sequences longer than it are
+ *                 split into partitions of that many positions, merged the
+ *                 same way;
+ *                 PA_PARTITION_NONE: one pass over each whole sequence;
+ *                 PA_PARTITION_AUTO: the partition size
+ *                 pa_decode_auto_partition gives
  *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 256-byte
  *                 aligned; scratch that each call rewrites before reading.
  *                 Calls that share a workspace must not overlap (same stream,

@@ -65,21 +65,47 @@ def test_host_only_calls_and_argument_errors_without_a_gpu():
                                        ctypes.c_void_p(16), 1.0, ctypes.c_void_p(16), 4, 8, 4,
                                        128, 64, 1024, 256, ctypes.c_void_p(256), 1024, 2, None)
     assert st == -6  # workspace without room for the partials
+    # the balanced split exists only on the matrix-core path (bf16/fp16, D 64/128)
+    st = lib.pa_paged_attention_decode(None, None, None, None, None, 1.0, None, 1, 8, 4, 128, 1,
+                                       16, pa.PARTITION_BALANCED, None, 0, 0, None)
+    assert st == -4
+    assert pa.decode_auto_partition(4, 8, 4, 128, 4096, 2) > 0
+    assert pa.decode_auto_partition(4, 8, 4, 96, 512, 2) == pa.PARTITION_NONE
+    assert lib.pa_decode_set_max_groups(-1) == -1
+    assert lib.pa_decode_set_max_groups(0) == 0
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 4, 2, 64, 0, None) == 0
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 1, 4, 2, 64, 0, None) == -1
     assert lib.pa_copy_blocks(None, None, None, 0, 4, 2, 60, 2, None) == -1
 
 
 def test_workspace_size_closed_form():
-    # plan (256-byte meta, 16 B per sequence and partition, 4 B per sequence),
-    # then m, l and acc of every (sequence, query head, partition), each 256-B aligned
+    # fixed partitions: plan (256-byte meta, 16 B per list entry -- sequences x
+    # partitions rounded up to 32 entries -- and 4 B per sequence), then m, l
+    # and acc of every (sequence, query head, partition), each 256-B aligned
     def up(x):
         return -(-x // 256) * 256
+
+    def entries(n):
+        return -(-n // 32) * 32
     s, hq, d, np_ = 4, 8, 128, 4
-    plan = 256 + up(16 * s * np_) + up(4 * s)
+    plan = 256 + up(16 * entries(s * np_)) + up(4 * s)
     parts = s * hq * np_
     assert pa.decode_workspace_bytes(s, hq, d, 1024, 256) == plan + up(8 * parts) + up(4 * d * parts)
-    assert pa.decode_workspace_bytes(s, hq, d, 1024, pa.PARTITION_NONE) == 256 + up(16 * s) + up(4 * s)
-    assert pa.decode_workspace_bytes(s, hq, d, 256, 256) == 256 + up(16 * s) + up(4 * s)
+    fixed_none = 256 + up(16 * entries(s)) + up(4 * s)
+    assert pa.decode_workspace_bytes(s, hq, d, 1024, pa.PARTITION_NONE) == fixed_none
+    assert pa.decode_workspace_bytes(s, hq, d, 256, 256) == fixed_none
+    # balanced split: meta, 2049 range starts of 16 B, two partial slots of
+    # min(16, hq) rows (rounded up to a power of two) per range; independent
+    # of the lengths
+    for hq_, d_, r in ((8, 128, 8), (64, 64, 16), (2, 128, 2), (3, 128, 4), (12, 64, 16)):
+        rows = 2048 * 2 * r
+        bal = 256 + up(16 * 2049) + up(8 * rows) + up(4 * d_ * rows)
+        for max_len in (0, 100, 100000):
+            assert pa.decode_workspace_bytes(s, hq_, d_, max_len, pa.PARTITION_BALANCED) == bal
+    # automatic: the fixed partition it resolves to
+    auto_p = pa.decode_auto_partition(s, hq, 1, 64, 4096, 2)
+    assert auto_p > 0
+    assert (pa.decode_workspace_bytes(s, hq, d, 4096, pa.PARTITION_AUTO)
+            == pa.decode_workspace_bytes(s, hq, d, 4096, auto_p))
     with pytest.raises(ValueError):
         pa.Pool(4, free_order=[0, 1])

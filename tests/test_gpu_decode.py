@@ -37,6 +37,8 @@ CASES = [
     ([7, 100, 300], 64, 8, 128, "bf16"),                    # G = 8
     ([9, 200], 32, 1, 128, "f16"),                          # MQA, G = 32 (2 head blocks)
     ([31, 90], 4, 4, 128, "bf16"),                          # MHA, G = 1
+    ([5, 77, 400], 4, 2, 64, "f16"),                        # G = 2
+    ([20, 300, 1000], 12, 4, 128, "bf16"),                  # G = 3 (4-row head group)
     ([1, 17, 33, 100], 4, 2, 64, "f32"),                    # generic VALU path
     ([2, 40, 700], 8, 2, 32, "bf16"),                       # generic path, D = 32
     ([2, 40, 300], 4, 2, 256, "f16"),                       # generic path, D = 256
@@ -52,6 +54,38 @@ def test_small_cases_against_oracle(lens, hq, hkv, d, dtype, partition_size):
     w = workloads.make_custom(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=sum(lens) + hq)
     db, ref = _run_small(w, partition_size)
     assert_close(db.out_bits(), ref, dtype, f"{lens} {hq}/{hkv} d={d} {dtype}")
+
+
+@pytest.mark.parametrize("groups", [1, 2, 3, 7, 64, 0])
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(16, 2, 128, "bf16"), (8, 8, 64, "f16"),
+                                            (64, 2, 128, "f16")])
+def test_balanced_split_on_any_grid(groups, hq, hkv, d, dtype):
+    # the range cuts move with the grid: one range (no cut) up to units cut
+    # into many pieces; then two sequences emptied, whose single empty block
+    # still goes through the schedule and must give zeros
+    import torch
+    lens = [1, 15, 16, 17, 33, 100, 257, 600, 3, 2000, 5]
+    print(f"[gpu] balanced split groups={groups} hq={hq} hkv={hkv} d={d} {dtype}", flush=True)
+    w = workloads.make_custom(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=groups + hq)
+    pa.decode_set_max_groups(groups)
+    try:
+        db, ref = _run_small(w, pa.PARTITION_BALANCED)
+        assert_close(db.out_bits(), ref, dtype, f"balanced groups={groups}")
+        cut = db.context_lens.clone()
+        cut[0] = 0
+        cut[8] = 0
+        out = torch.full_like(db.out, float("nan"))
+        kc, vc = db.caches[0]
+        pa.paged_attention_decode(db.q, kc, vc, db.tables, cut, w.scale, out,
+                                  max_context_len=db.max_context_len,
+                                  partition_size=pa.PARTITION_BALANCED)
+        torch.cuda.synchronize()
+    finally:
+        pa.decode_set_max_groups(0)
+    got = bits_of(out)
+    assert not got[[0, 8]].any()
+    keep = [i for i in range(len(lens)) if i not in (0, 8)]
+    assert_close(got[keep], ref[keep], dtype, f"balanced groups={groups}, two rows emptied")
 
 
 def test_tiny_config_every_output():
@@ -183,7 +217,7 @@ def test_full_size_split_equals_unsplit_and_is_deterministic(config):
     # the fp32 results differ only in summation order; after rounding to the
     # storage dtype they are at most one unit in its last place apart
     ulp = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -10
-    for ps in (pa.PARTITION_NONE, 256, 1024):
+    for ps in (pa.PARTITION_NONE, 256, 1024, pa.PARTITION_BALANCED):
         db.decode(partition_size=ps, out=out2)
         c = to_f64(bits_of(out2), w.dtype)
         ratio = np.abs(c - b) / (ulp * np.abs(b) + 1e-6)
