@@ -29,9 +29,14 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode achieved HBM GB/s (% of peak); attended KV tokens/s"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc", "pa_decode.hip")
-# main-pass kernels of a decode call: balanced split, fixed partitions, VALU path
-DECODE_KERNELS = ("decode_balanced_kernel", "decode_items_kernel", "decode_generic_kernel")
+CSRC = os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc")
+# main-pass kernels of a decode call (balanced split, fixed partitions, VALU
+# path) and the sources each is built from
+DECODE_KERNELS = {
+    "decode_stream_kernel": ("pa_decode_balanced.hip", "pa_decode_common.h"),
+    "decode_items_kernel": ("pa_decode.hip", "pa_decode_common.h"),
+    "decode_generic_kernel": ("pa_decode.hip", "pa_decode_common.h"),
+}
 
 
 def decode_bytes(w):
@@ -57,24 +62,28 @@ def step_bytes(w, db):
     return decode_bytes(w) + writes + copies
 
 
-def source_hash():
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for name in DECODE_KERNELS[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """Counter-measured HBM bytes per decode launch, if taken on the current kernel."""
+def load_traffic(workload, kernel):
+    """Counter-measured HBM bytes per launch of `kernel`, if taken on its current source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != source_hash() or t.get("workload") != workload:
+    if (t.get("kernel") != kernel or t.get("source_sha256_16") != source_hash(kernel)
+            or t.get("workload") != workload):
         return None
     return t.get("bytes_per_launch")
 
 
-def pmc_summary(fetch_dir, write_dir, workload, out_path=TRAFFIC_FILE):
+def pmc_summary(fetch_dir, write_dir, workload, kernel, out_path=TRAFFIC_FILE):
     """HBM bytes per decode launch from two rocprofv3 --pmc runs of this bench
     (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch), each scaled by
     what the same counter reads for the run's plain 1 GiB device copy."""
@@ -91,7 +100,7 @@ def pmc_summary(fetch_dir, write_dir, workload, out_path=TRAFFIC_FILE):
             raise SystemExit(f"no {counter} rows under {d}")
         return out
 
-    result = {"workload": workload, "source_sha256_16": source_hash()}
+    result = {"workload": workload, "kernel": kernel, "source_sha256_16": source_hash(kernel)}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rs = rows(d, counter)
         copies = [r for r in rs if "copyBuffer" in r["Kernel_Name"]]
@@ -99,8 +108,7 @@ def pmc_summary(fetch_dir, write_dir, workload, out_path=TRAFFIC_FILE):
         cal = statistics.median(float(r["Counter_Value"]) for r in copies
                                 if int(r["Grid_Size"]) == big)
         factor = (1 << 30) / 1024.0 / cal  # the copy moves 1 GiB each way
-        dec = [float(r["Counter_Value"]) for r in rs
-               if any(k in r["Kernel_Name"] for k in DECODE_KERNELS)]
+        dec = [float(r["Counter_Value"]) for r in rs if kernel in r["Kernel_Name"]]
         kib = statistics.median(dec)
         result[counter] = {"kib_per_dispatch_raw": kib, "calibration_factor": round(factor, 4),
                            "bytes_per_launch": int(kib * 1024 * factor),
@@ -165,6 +173,8 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 plain device copies of MIB MiB (a known-size "
                          "reference for HBM byte counters)")
+    ap.add_argument("--kernel", default="decode_items_kernel", choices=sorted(DECODE_KERNELS),
+                    help="main decode kernel the --pmc-summary counters belong to")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench, taken with --calibrate-copy 1024, into " + TRAFFIC_FILE)
@@ -174,7 +184,8 @@ def main():
         import workloads
         pmc_summary(*args.pmc_summary, workloads.CONFIG_NAMES[int(args.config)
                                                                if args.config.isdigit()
-                                                               else args.config])
+                                                               else args.config],
+                    args.kernel)
         return
 
     if args.gpus != 1:
@@ -233,16 +244,16 @@ def main():
     dec = kt["decode"]
     dec_ms = dec["ms"] / max(1, dec["launches"])
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.name)
     ps = args.partition if args.partition != -1 else pa.decode_auto_partition(
         w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, db.max_context_len,
         {"f32": 0, "f16": 1, "bf16": 2}[w.dtype])
     if ps == pa.PARTITION_BALANCED:
-        main_kernel = "decode_balanced_kernel"
+        main_kernel = "decode_stream_kernel"
     elif w.dtype != "f32" and w.head_dim in (64, 128):
         main_kernel = "decode_items_kernel"
     else:
         main_kernel = "decode_generic_kernel"
+    traffic = load_traffic(w.name, main_kernel)
     result = {
         "metric": METRIC,
         "value": round(sbytes / (ms_step * 1e-3) / 1e9, 2),

@@ -65,7 +65,7 @@ typedef int32_t pa_dtype;
  * multiple of 16 */
 #define PA_PARTITION_NONE 0    /* one pass over each whole sequence, no partials */
 #define PA_PARTITION_AUTO (-1) /* the library picks */
-#define PA_PARTITION_BALANCED (-2) /* equal K/V blocks per work-group (matrix-core path) */
+#define PA_PARTITION_BALANCED (-2) /* equal K/V work per wave (matrix-core path) */
 
 /* Short English text of a status code (static storage). */
 const char* pa_status_string(pa_status status);
@@ -174,11 +174,13 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
  * bytes per sequence and partition, rounded up to 32 entries, and 4 per
  * sequence) plus, when some sequence is split, the partial results
  * (4 * (2 + head_dim) bytes per sequence, query head and partition).
- * PA_PARTITION_BALANCED: 16 bytes per range start and two partial slots of
- * min(16, num_q_heads) rows per work-group, for up to 2048 work-groups,
- * whatever the lengths.  PA_PARTITION_AUTO: as for the partition size it
- * resolves to.  Each area is 256-byte aligned after a 256-byte header.  0 on
- * invalid sizes. */
+ * PA_PARTITION_BALANCED: 16 bytes per range start (one more than ranges) and
+ * two partial slots per range of min(16, num_q_heads) rows, rounded up to a
+ * power of two, of 4 * (2 + head_dim) bytes each; ranges = 2048, or
+ * ceil(num_seqs * num_q_heads * (2 + ceil(max_context_len / 16)) / 512) when
+ * that is larger.  PA_PARTITION_AUTO: as for the partition size it resolves
+ * to.  Each area is 256-byte aligned after a 256-byte header.  0 on invalid
+ * sizes. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size);
 
@@ -187,10 +189,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
 
-/* Caps the work-groups of the balanced split at max_groups (0: no cap; the
- * default is the number the device holds resident at once).  For sharing the
- * GPU with concurrent work, and for tests.  Library-wide, not thread-safe
- * against concurrent decode calls.  PA_ERR_INVALID_ARG if negative. */
+/* Caps the work-groups of the balanced split at max_groups, four waves (four
+ * ranges) each (0: no cap; the default is the number the device holds
+ * resident at once).  For sharing the GPU with concurrent work, and for
+ * tests.  Library-wide, not thread-safe against concurrent decode calls.
+ * PA_ERR_INVALID_ARG if negative. */
 pa_status pa_decode_set_max_groups(int32_t max_groups);
 
 /* Decode attention over the paged cache:
@@ -209,10 +212,10 @@ pa_status pa_decode_set_max_groups(int32_t max_groups);
  *                 each must be <= max_context_len and <= 16 * max_blocks_per_seq
  *   partition_size  how the work is split:
  *                 PA_PARTITION_BALANCED (matrix-core path only): the blocks
- *                 of all (sequence, KV head) pairs are cut into one range of
- *                 equal length per resident work-group; a pair cut by range
- *                 boundaries is merged by a second pass (running max /
- *                 log-sum-exp rule);
+ *                 of all (sequence, KV head) pairs are cut into ranges of
+ *                 equal cost, one per resident wave (at most 512 blocks
+ *                 each); a pair cut by range boundaries is merged by a
+ *                 second pass (running max / log-sum-exp rule);
  *                 a positive multiple of 16: sequences longer than it are
  *                 split into partitions of that many positions, merged the
  *                 same way;

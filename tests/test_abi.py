@@ -94,13 +94,15 @@ def test_workspace_size_closed_form():
     fixed_none = 256 + up(16 * entries(s)) + up(4 * s)
     assert pa.decode_workspace_bytes(s, hq, d, 1024, pa.PARTITION_NONE) == fixed_none
     assert pa.decode_workspace_bytes(s, hq, d, 256, 256) == fixed_none
-    # balanced split: meta, 2049 range starts of 16 B, two partial slots of
-    # min(16, hq) rows (rounded up to a power of two) per range; independent
-    # of the lengths
+    # balanced split: meta, one range start more than ranges (16 B each), two
+    # partial slots of min(16, hq) rows (rounded up to a power of two) per
+    # range; ranges = 2048, or more when ranges of at most 512 blocks plus 2
+    # per unit are needed to cover num_seqs x hq units of the longest length
     for hq_, d_, r in ((8, 128, 8), (64, 64, 16), (2, 128, 2), (3, 128, 4), (12, 64, 16)):
-        rows = 2048 * 2 * r
-        bal = 256 + up(16 * 2049) + up(8 * rows) + up(4 * d_ * rows)
         for max_len in (0, 100, 100000):
+            ranges = max(2048, -(-(s * hq_ * (2 + max(1, -(-max_len // 16)))) // 512))
+            rows = ranges * 2 * r
+            bal = 256 + up(16 * (ranges + 1)) + up(8 * rows) + up(4 * d_ * rows)
             assert pa.decode_workspace_bytes(s, hq_, d_, max_len, pa.PARTITION_BALANCED) == bal
     # automatic: the fixed partition it resolves to
     auto_p = pa.decode_auto_partition(s, hq, 1, 64, 4096, 2)

@@ -56,20 +56,22 @@ def test_small_cases_against_oracle(lens, hq, hkv, d, dtype, partition_size):
     assert_close(db.out_bits(), ref, dtype, f"{lens} {hq}/{hkv} d={d} {dtype}")
 
 
+@pytest.mark.parametrize("mode", [pa.PARTITION_BALANCED])
 @pytest.mark.parametrize("groups", [1, 2, 3, 7, 64, 0])
 @pytest.mark.parametrize("hq,hkv,d,dtype", [(16, 2, 128, "bf16"), (8, 8, 64, "f16"),
-                                            (64, 2, 128, "f16")])
-def test_balanced_split_on_any_grid(groups, hq, hkv, d, dtype):
+                                            (64, 2, 128, "f16"), (32, 1, 128, "bf16")])
+def test_balanced_split_on_any_grid(mode, groups, hq, hkv, d, dtype):
     # the range cuts move with the grid: one range (no cut) up to units cut
     # into many pieces; then two sequences emptied, whose single empty block
     # still goes through the schedule and must give zeros
     import torch
     lens = [1, 15, 16, 17, 33, 100, 257, 600, 3, 2000, 5]
-    print(f"[gpu] balanced split groups={groups} hq={hq} hkv={hkv} d={d} {dtype}", flush=True)
+    print(f"[gpu] balanced split mode={mode} groups={groups} hq={hq} hkv={hkv} d={d} {dtype}",
+          flush=True)
     w = workloads.make_custom(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=groups + hq)
     pa.decode_set_max_groups(groups)
     try:
-        db, ref = _run_small(w, pa.PARTITION_BALANCED)
+        db, ref = _run_small(w, mode)
         assert_close(db.out_bits(), ref, dtype, f"balanced groups={groups}")
         cut = db.context_lens.clone()
         cut[0] = 0
@@ -77,8 +79,7 @@ def test_balanced_split_on_any_grid(groups, hq, hkv, d, dtype):
         out = torch.full_like(db.out, float("nan"))
         kc, vc = db.caches[0]
         pa.paged_attention_decode(db.q, kc, vc, db.tables, cut, w.scale, out,
-                                  max_context_len=db.max_context_len,
-                                  partition_size=pa.PARTITION_BALANCED)
+                                  max_context_len=db.max_context_len, partition_size=mode)
         torch.cuda.synchronize()
     finally:
         pa.decode_set_max_groups(0)
@@ -214,13 +215,17 @@ def test_full_size_split_equals_unsplit_and_is_deterministic(config):
     db.decode(partition_size=pa.PARTITION_AUTO, out=out2)
     assert np.array_equal(bits_of(out2), base)  # run to run
     b = to_f64(base, w.dtype)
-    # the fp32 results differ only in summation order; after rounding to the
-    # storage dtype they are at most one unit in its last place apart
+    # the splits differ in summation order and in the running maxima the
+    # weights are taken against; a weight enters the matrix core as a hi + lo
+    # pair in the storage dtype, exact to about 2^-16 of itself, so outputs
+    # that nearly cancel can move by ~1e-6 in absolute terms.  After rounding
+    # to the storage dtype the results are at most one unit in its last place
+    # apart, or 1e-5 where the output is that small.
     ulp = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -10
     for ps in (pa.PARTITION_NONE, 256, 1024, pa.PARTITION_BALANCED):
         db.decode(partition_size=ps, out=out2)
         c = to_f64(bits_of(out2), w.dtype)
-        ratio = np.abs(c - b) / (ulp * np.abs(b) + 1e-6)
+        ratio = np.abs(c - b) / (ulp * np.abs(b) + 1e-5)
         assert ratio.max() <= 1.0, f"partition {ps}: {ratio.max():.2f} ulp"
 
 
