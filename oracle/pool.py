@@ -25,11 +25,34 @@ Readings where the pages leave a step open (listed in the design doc):
   writer gets the copy and the source loses one reference; a block at count 1
   is written in place (so of n sharers, the first n-1 writers copy).
 
+Prefix caching: blocks are reused when several requests start with the same
+tokens, e.g. one system prompt ("PagedAttention for the professional", the
+serve-command section on --enable-prefix-caching), and the cached blocks
+consume room in the pool (same page, trade-offs section).  Readings:
+* only full blocks are cached; a block's key is (the serial number of the
+  entry of the block before it, or 0 for the first block; its 16 token ids).
+  Serial numbers are never reused, so a key names a whole token prefix
+  exactly -- no hashing, no collisions -- and an entry whose parent was
+  evicted simply becomes unreachable;
+* ``register`` enters the full blocks of a sequence's table; a block whose key
+  is already cached under another block is left out (the chain continues
+  through the cached entry, which holds the same prefix);
+* ``match_prefix`` walks the key chain of a token list from the first block
+  and takes one reference on every cached block it finds, stopping at the
+  first miss;
+* a cached block whose count drops to 0 stays cached and joins the end of an
+  eviction list; allocation takes an uncached free block first (LIFO as
+  above) and only then evicts the least recently released cached block.
+
 Pins (tests/test_oracle_pool.py): the pages' worked examples (token 17 -> second
 block; 300 of a 4096 reservation idle), block count = ceil(len/16) with waste
 below 16 slots per sequence, reference-count conservation against the tables
 after random operation sequences, LIFO reuse, all-or-nothing failure, and the
-shared-prefix workload's closed-form copy count and block count.
+shared-prefix workload's closed-form copy count and block count.  Prefix
+caching (tests/test_oracle_prefix.py): matched blocks = floor(common prefix /
+16) by brute force over random token lists, cached blocks outliving their
+sequences, eviction order, no false hit through a reused block id, and the
+shared-prompt block count in closed form.
 """
 from __future__ import annotations
 
@@ -69,10 +92,18 @@ class BlockPool:
         self.refcount = [0] * num_blocks
         self.free_stack = list(reversed(order))  # top of the stack = order[0]
         self.copies_made = 0
+        # prefix cache
+        self.cache = {}        # key -> block
+        self.key_of = {}       # block -> key
+        self.serial_of = {}    # block -> serial number of its entry
+        self.next_serial = 1
+        self.lru = []          # cached blocks at count 0, least recently released first
+        self.prefix_hits = 0
 
     # -- single-block calls --
     def num_free(self) -> int:
-        return len(self.free_stack)
+        """Blocks an allocation can take: uncached free ones and evictable ones."""
+        return len(self.free_stack) + len(self.lru)
 
     def _check(self, b: int) -> int:
         b = int(b)
@@ -81,11 +112,24 @@ class BlockPool:
         return b
 
     def alloc(self) -> int:
-        if not self.free_stack:
+        if self.free_stack:
+            b = self.free_stack.pop()
+        elif self.lru:
+            b = self.lru.pop(0)
+            self._uncache(b)
+        else:
             raise OutOfBlocks("pool is empty")
-        b = self.free_stack.pop()
         self.refcount[b] = 1
         return b
+
+    def _chain_id(self, b: int) -> int:
+        """What the key of the block after cached block ``b`` names as its
+        parent: the serial number of b's entry."""
+        return self.serial_of[b]
+
+    def _uncache(self, b: int) -> None:
+        del self.cache[self.key_of.pop(b)]
+        del self.serial_of[b]
 
     def incref(self, b: int) -> None:
         b = self._check(b)
@@ -96,7 +140,10 @@ class BlockPool:
         b = self._check(b)
         self.refcount[b] -= 1
         if self.refcount[b] == 0:
-            self.free_stack.append(b)
+            if b in self.key_of:
+                self.lru.append(b)
+            else:
+                self.free_stack.append(b)
 
     # -- whole-table calls --
     def fork(self, table) -> list:
@@ -147,9 +194,64 @@ class BlockPool:
             slots.append(table[p // BLOCK_SIZE] * BLOCK_SIZE + p % BLOCK_SIZE)
         return slots, cow
 
+    # -- prefix cache --
+    @staticmethod
+    def _full_blocks(tokens):
+        tokens = [int(t) for t in tokens]
+        return [tuple(tokens[i:i + BLOCK_SIZE])
+                for i in range(0, len(tokens) - BLOCK_SIZE + 1, BLOCK_SIZE)]
+
+    def match_prefix(self, tokens) -> list:
+        """Cached blocks holding the longest run of whole leading blocks of
+        ``tokens``; each gets one more reference (the caller's new table)."""
+        found = []
+        parent = 0
+        for chunk in self._full_blocks(tokens):
+            b = self.cache.get((parent, chunk))
+            if b is None:
+                break
+            found.append(b)
+            parent = self._chain_id(b)
+        for b in found:
+            if self.refcount[b] == 0:
+                self.lru.remove(b)
+            self.refcount[b] += 1
+        self.prefix_hits += len(found)
+        return found
+
+    def register(self, table, tokens) -> int:
+        """Cache the full blocks of a sequence whose first tokens are
+        ``tokens`` and whose blocks are ``table``.  Returns how many blocks
+        were entered.  All-or-nothing: every block must be held and a block
+        already cached must hold the same 16 tokens."""
+        chunks = self._full_blocks(tokens)
+        if len(chunks) > len(table):
+            raise InvalidArg("more full blocks of tokens than table entries")
+        for i, chunk in enumerate(chunks):
+            b = self._check(table[i])
+            if b in self.key_of and self.key_of[b][1] != chunk:
+                raise InvalidArg(f"block {b} is cached with other tokens")
+        added = 0
+        parent = 0
+        for i, chunk in enumerate(chunks):
+            b = int(table[i])
+            if b not in self.key_of:
+                other = self.cache.get((parent, chunk))
+                if other is not None:
+                    parent = self._chain_id(other)
+                    continue
+                self.cache[(parent, chunk)] = b
+                self.key_of[b] = (parent, chunk)
+                self.serial_of[b] = self.next_serial
+                self.next_serial += 1
+                added += 1
+            parent = self._chain_id(b)
+        return added
+
     # -- accounting --
     def stats(self) -> dict:
         used = sum(1 for r in self.refcount if r > 0)
         shared = sum(1 for r in self.refcount if r > 1)
         return {"num_blocks": self.num_blocks, "free": self.num_free(), "used": used,
-                "shared": shared, "copies": self.copies_made}
+                "shared": shared, "copies": self.copies_made, "cached": len(self.key_of),
+                "evictable": len(self.lru), "prefix_hits": self.prefix_hits}

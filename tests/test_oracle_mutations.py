@@ -86,3 +86,45 @@ def test_planted_cow_without_release_is_caught(monkeypatch):
     with pytest.raises(AssertionError):
         tp.test_copy_on_write_first_writers_copy_last_writes_in_place()
     assert calls["n"] > 0
+
+
+from tests import test_oracle_prefix as tpre  # noqa: E402
+
+
+def test_planted_block_id_keys_are_caught(monkeypatch):
+    """Keying a cached block on its parent's block id (reused after eviction)
+    instead of a never-reused serial number gives false hits."""
+    monkeypatch.setattr(pool.BlockPool, "_chain_id", lambda self, b: b + 1)
+    with pytest.raises(AssertionError):
+        tpre.test_no_false_hit_through_a_reused_block_id()
+
+
+def test_planted_mru_eviction_is_caught(monkeypatch):
+    orig_alloc = pool.BlockPool.alloc
+
+    def mru_alloc(self):
+        if not self.free_stack and self.lru:
+            self.lru.reverse()
+            try:
+                return orig_alloc(self)
+            finally:
+                self.lru.reverse()
+        return orig_alloc(self)
+    monkeypatch.setattr(pool.BlockPool, "alloc", mru_alloc)
+    with pytest.raises(AssertionError):
+        tpre.test_uncached_blocks_go_first_then_least_recently_released()
+
+
+def test_planted_match_without_reference_is_caught(monkeypatch):
+    orig_match = pool.BlockPool.match_prefix
+
+    def match_no_ref(self, tokens):
+        found = orig_match(self, tokens)
+        for b in found:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.lru.append(b)
+        return found
+    monkeypatch.setattr(pool.BlockPool, "match_prefix", match_no_ref)
+    with pytest.raises((AssertionError, pool.PoolError)):  # a count check, or a later call on an unheld block
+        tpre.test_cached_blocks_outlive_their_sequence()

@@ -25,7 +25,7 @@ def _conservation(pool, tables):
             counts[b] += 1
     assert counts == pool.refcount
     assert pool.num_free() + sum(1 for c in counts if c > 0) == pool.num_blocks
-    assert sorted(pool.free_stack) == [b for b in range(pool.num_blocks) if counts[b] == 0]
+    assert sorted(pool.free_stack + pool.lru) == [b for b in range(pool.num_blocks) if counts[b] == 0]
 
 
 def test_token_17_opens_the_second_block():
