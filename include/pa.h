@@ -52,6 +52,7 @@ typedef int32_t pa_status;
 #define PA_ERR_UNSUPPORTED (-4)   /* valid request this build does not implement */
 #define PA_ERR_DEVICE (-5)        /* HIP launch or runtime error */
 #define PA_ERR_WORKSPACE (-6)     /* workspace missing or too small */
+#define PA_ERR_HOST_MEMORY (-7)   /* a host allocation failed; nothing changed */
 
 /* Storage dtype of q, the caches and out. */
 typedef int32_t pa_dtype;
@@ -82,12 +83,18 @@ typedef struct {
   int32_t num_used;   /* reference count >= 1 */
   int32_t num_shared; /* reference count >= 2 */
   int64_t copies;     /* copy-on-write pairs emitted so far */
+  int32_t num_cached;    /* blocks entered in the prefix cache (held or not) */
+  int32_t num_evictable; /* cached blocks at count 0 (counted in num_free) */
+  int64_t prefix_hits;   /* blocks handed out by pa_prefix_match so far */
 } pa_pool_stats_t;
 
 /* New pool of `num_blocks` blocks.  `free_order` (NULL = 0, 1, 2, ...) is a
  * permutation of [0, num_blocks): the first allocation returns free_order[0],
  * the next free_order[1], and so on.  A block whose count drops to 0 is pushed
- * back on top and is the next one handed out.  PA_ERR_INVALID_ARG if
+ * back on top and is the next one handed out -- unless it is in the prefix
+ * cache (below): then it stays cached and joins the end of an eviction list,
+ * and an allocation takes it (dropping it from the cache) only when no
+ * uncached block is free, oldest release first.  PA_ERR_INVALID_ARG if
  * num_blocks <= 0 or free_order is not a permutation. */
 pa_status pa_pool_create(int32_t num_blocks, const int32_t* free_order, pa_pool** out);
 void pa_pool_destroy(pa_pool* pool);
@@ -126,8 +133,41 @@ pa_status pa_append_slots(pa_pool* pool, int32_t* table_row, int32_t* nblocks,
                           int32_t max_blocks, int32_t pos, int32_t n, int64_t* slots_out,
                           int32_t* cow_src, int32_t* cow_dst);
 
+/* Prefix cache ("PagedAttention for the professional", serve-command section:
+ * requests that begin with the same tokens, such as one system prompt, reuse
+ * the blocks holding them).  Only full blocks are cached.  A block's key is
+ * (serial number of the cache entry of the block before it, 0 for the first
+ * block of a sequence; its 16 token ids); serial numbers are never reused, so
+ * a key stands for one exact token prefix and entries below an evicted block
+ * can no longer be reached.  Calls that never register leave the pool
+ * behaving exactly as without a cache.
+ *
+ * pa_prefix_match: the cached blocks holding the longest run of whole
+ * leading blocks of tokens[0..num_tokens) (at most max_blocks), written to
+ * table_out (host) in logical order; each gets one more reference (one for
+ * the new sequence's table; an evictable block leaves the eviction list).
+ * *num_matched = their number (0 when nothing is cached).  The new sequence
+ * continues with pa_append_slots at pos = 16 * *num_matched.
+ * PA_ERR_INVALID_ARG on a NULL pointer or negative size. */
+pa_status pa_prefix_match(pa_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                          int32_t* table_out, int32_t max_blocks, int32_t* num_matched);
+
+/* pa_prefix_register: enter the full blocks of a sequence whose blocks are
+ * table_row[0..nblocks) and whose first num_tokens token ids are `tokens`:
+ * block i holds tokens[16i .. 16i+16) for i < num_tokens / 16.  Call it once
+ * those blocks' K/V are written (or enqueued on the stream that later
+ * readers use).  A block already cached stays as it is; a block whose key is
+ * already cached under another block is not entered (the chain continues
+ * through that entry).  *num_added (may be NULL) = blocks entered.
+ * All-or-nothing: PA_ERR_INVALID_ARG if num_tokens / 16 > nblocks or a
+ * cached block holds other tokens, PA_ERR_BAD_BLOCK if a block is not held,
+ * PA_ERR_HOST_MEMORY if the index cannot grow. */
+pa_status pa_prefix_register(pa_pool* pool, const int32_t* table_row, int32_t nblocks,
+                             const int32_t* tokens, int32_t num_tokens, int32_t* num_added);
+
 /* Reference count of a block (-1 if the id is out of range). */
 int32_t pa_refcount(const pa_pool* pool, int32_t block);
+/* Blocks an allocation can take: uncached free ones plus evictable cached ones. */
 int32_t pa_num_free(const pa_pool* pool);
 pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
 

@@ -13,6 +13,12 @@ Order of a batch (the reading taken of the pages' serving story):
 Each phase yields its copy-on-write pairs and the slots of the tokens it
 appends; its effect on the cache is "copy the pairs, then write the tokens".
 Then every sequence decodes its last token over all ``len`` cached positions.
+
+With ``prefix_cache=True``, A1 runs through the pool's prefix cache instead of
+forking: every sequence of a prompt looks the prompt's token ids up, takes the
+cached whole blocks, allocates and writes the rest itself, and enters its full
+blocks in the cache ("PagedAttention for the professional", serve-command
+section on prefix caching).
 """
 from __future__ import annotations
 
@@ -21,6 +27,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import attention, cache_ops
+from .pool import BLOCK_SIZE as pool_block
 from .pool import BlockPool
 
 
@@ -57,7 +64,7 @@ def _phase(pairs, slots, keys, values, hkv, d, bits):
                  np.asarray(slots, dtype=np.int64), k, v)
 
 
-def plan(w) -> Plan:
+def plan(w, prefix_cache: bool = False) -> Plan:
     pool = BlockPool(w.num_blocks, w.free_order)
     S, hkv, d = w.num_seqs, w.num_kv_heads, w.head_dim
     bits = w.q.dtype
@@ -71,7 +78,17 @@ def plan(w) -> Plan:
         p = int(w.prompt_of[s])
         if p < 0:
             continue
-        if p not in owner:
+        if prefix_cache:
+            toks = w.prompt_tokens(p)
+            tables[s] = pool.match_prefix(toks)
+            i0 = len(tables[s]) * pool_block
+            sl, cow = pool.append(tables[s], i0, len(toks) - i0)
+            assert cow is None
+            slots += sl
+            ks.append(w.k_prompt[poff[p] + i0:poff[p + 1]])
+            vs.append(w.v_prompt[poff[p] + i0:poff[p + 1]])
+            pool.register(tables[s], toks)
+        elif p not in owner:
             owner[p] = s
             n = int(w.prompt_lens[p])
             sl, cow = pool.append(tables[s], 0, n)
@@ -118,9 +135,9 @@ def apply_phase(phase: Phase, k_cache, v_cache) -> None:
     cache_ops.reshape_and_cache(phase.key, phase.value, k_cache, v_cache, phase.slots)
 
 
-def run(w, fill_bits, phases=None):
+def run(w, fill_bits, phases=None, prefix_cache: bool = False):
     """Plan, build the cache and decode.  Returns (plan, k_cache, v_cache, out)."""
-    pl = plan(w)
+    pl = plan(w, prefix_cache)
     k_cache, v_cache = empty_cache(w, fill_bits)
     for ph in (pl.phases if phases is None else [pl.phases[i] for i in phases]):
         apply_phase(ph, k_cache, v_cache)

@@ -8,8 +8,8 @@ missing every call raises -- there is no fallback.
 The names follow the C ABI of ``include/pa.h`` without its ``pa_`` prefix:
 ``reshape_and_cache``, ``copy_blocks``, ``paged_attention_decode``, the pool
 calls on :class:`Pool` (``alloc``, ``free``, ``incref``, ``fork``,
-``free_table``, ``append_slots``, ``refcount``, ``num_free``, ``stats``) and
-``blocks_for_bytes``.
+``free_table``, ``append_slots``, ``prefix_match``, ``prefix_register``,
+``refcount``, ``num_free``, ``stats``) and ``blocks_for_bytes``.
 """
 from __future__ import annotations
 
@@ -44,7 +44,8 @@ _P_I64 = ctypes.POINTER(ctypes.c_int64)
 
 class _Stats(ctypes.Structure):
     _fields_ = [("num_blocks", _c_i32), ("num_free", _c_i32), ("num_used", _c_i32),
-                ("num_shared", _c_i32), ("copies", _c_i64)]
+                ("num_shared", _c_i32), ("copies", _c_i64), ("num_cached", _c_i32),
+                ("num_evictable", _c_i32), ("prefix_hits", _c_i64)]
 
 
 _SIGNATURES = {
@@ -61,6 +62,8 @@ _SIGNATURES = {
     "pa_refcount": (_c_i32, [_c_p, _c_i32]),
     "pa_num_free": (_c_i32, [_c_p]),
     "pa_pool_stats": (_c_i32, [_c_p, ctypes.POINTER(_Stats)]),
+    "pa_prefix_match": (_c_i32, [_c_p, _P_I32, _c_i32, _P_I32, _c_i32, _P_I32]),
+    "pa_prefix_register": (_c_i32, [_c_p, _P_I32, _c_i32, _P_I32, _c_i32, _P_I32]),
     "pa_blocks_for_bytes": (_c_i64, [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_reshape_and_cache": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _c_p]),
@@ -76,7 +79,8 @@ _SIGNATURES = {
 }
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "out of blocks", -3: "bad block id",
-           -4: "unsupported", -5: "device error", -6: "workspace too small"}
+           -4: "unsupported", -5: "device error", -6: "workspace too small",
+           -7: "host memory allocation failed"}
 
 
 class PAError(RuntimeError):
@@ -190,7 +194,29 @@ class Pool:
         st = _Stats()
         _check(load().pa_pool_stats(self._h, ctypes.byref(st)), "pa_pool_stats")
         return {"num_blocks": st.num_blocks, "free": st.num_free, "used": st.num_used,
-                "shared": st.num_shared, "copies": st.copies}
+                "shared": st.num_shared, "copies": st.copies, "cached": st.num_cached,
+                "evictable": st.num_evictable, "prefix_hits": st.prefix_hits}
+
+    def prefix_match(self, tokens, max_blocks: int | None = None) -> np.ndarray:
+        """Cached blocks of the longest whole-block prefix of ``tokens`` (each
+        gets one reference); int32 array in logical order."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        cap = t.size // BLOCK_SIZE if max_blocks is None else int(max_blocks)
+        out = np.empty(max(cap, 1), dtype=np.int32)
+        n = _c_i32()
+        _check(load().pa_prefix_match(self._h, _i32p(t), t.size, _i32p(out), cap,
+                                      ctypes.byref(n)), "pa_prefix_match")
+        return out[:n.value]
+
+    def prefix_register(self, table, tokens) -> int:
+        """Enter the full blocks of a sequence (blocks ``table``, first tokens
+        ``tokens``) in the prefix cache; returns how many were entered."""
+        t = np.ascontiguousarray(table, dtype=np.int32)
+        k = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = _c_i32()
+        _check(load().pa_prefix_register(self._h, _i32p(t), t.size, _i32p(k), k.size,
+                                         ctypes.byref(n)), "pa_prefix_register")
+        return n.value
 
 
 class BlockManager:
@@ -212,6 +238,21 @@ class BlockManager:
         self.nblocks[s] = nb
         self.lens[s] += int(n)
         return slots, cow
+
+    def match(self, s: int, tokens) -> int:
+        """Start empty sequence ``s`` with the cached whole blocks of
+        ``tokens``; returns the positions they cover."""
+        if self.nblocks[s] != 0:
+            raise ValueError("match target must be empty")
+        got = self.pool.prefix_match(tokens, self.rows.shape[1])
+        self.rows[s, :got.size] = got
+        self.nblocks[s] = got.size
+        self.lens[s] = got.size * BLOCK_SIZE
+        return int(self.lens[s])
+
+    def register(self, s: int, tokens) -> int:
+        """Enter sequence ``s``'s full blocks, holding ``tokens``, in the cache."""
+        return self.pool.prefix_register(self.rows[s, :int(self.nblocks[s])], tokens)
 
     def fork(self, dst: int, src: int) -> None:
         if self.nblocks[dst] != 0:

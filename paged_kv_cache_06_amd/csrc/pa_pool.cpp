@@ -8,12 +8,52 @@
 // down", section "How PagedAttention fixes this").
 //
 // The free list is a stack in a flat array: pushes and pops are O(1), a freed
-// block is the next one handed out.  No call allocates after pa_pool_create.
+// block is the next one handed out.
+//
+// Prefix cache: requests that start with the same tokens (one system prompt)
+// reuse the blocks that hold them ("PagedAttention for the professional", the
+// serve-command section on prefix caching), and cached blocks keep room in the
+// pool until it is needed (same page, trade-offs section).  A full block is
+// entered under the key (serial number of the entry of the block before it, 0
+// for a sequence's first block; its 16 token ids).  Serial numbers are never
+// reused, so a key stands for one exact token prefix -- the map compares whole
+// keys, nothing is hashed away -- and the entries below an evicted block become
+// unreachable instead of wrong.  A cached block whose count drops to 0 joins the
+// tail of an intrusive LRU list; allocation pops the uncached stack first and
+// then evicts the list's head.  Only registering allocates (hash-map nodes).
+#include <array>
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <unordered_map>
 
 #include "pa.h"
+
+namespace {
+
+struct Key {
+  uint64_t parent;
+  std::array<int32_t, PA_BLOCK_SIZE> tokens;
+  bool operator==(const Key& o) const { return parent == o.parent && tokens == o.tokens; }
+};
+
+struct KeyHash {
+  size_t operator()(const Key& k) const {
+    // FNV-1a over the parent serial and the token ids (bucket choice only)
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&h](uint64_t v) {
+      for (int i = 0; i < 8; ++i) {
+        h ^= (v >> (8 * i)) & 0xff;
+        h *= 1099511628211ull;
+      }
+    };
+    mix(k.parent);
+    for (int32_t t : k.tokens) mix(static_cast<uint32_t>(t));
+    return static_cast<size_t>(h);
+  }
+};
+
+}  // namespace
 
 struct pa_pool {
   int32_t num_blocks;
@@ -21,6 +61,16 @@ struct pa_pool {
   int64_t copies;
   int32_t* free_stack; // free_stack[top-1] is handed out next
   int32_t* refcount;
+  // prefix cache
+  uint64_t* serial;    // serial number of the block's cache entry, 0 = not cached
+  Key* key;            // the block's key while cached
+  int32_t* lru_prev;   // LRU list of cached blocks at count 0 (head = oldest)
+  int32_t* lru_next;
+  int32_t lru_head, lru_tail, lru_len;
+  int32_t cached;
+  uint64_t next_serial;
+  int64_t prefix_hits;
+  std::unordered_map<Key, int32_t, KeyHash>* index;
 };
 
 namespace {
@@ -31,14 +81,61 @@ inline bool held(const pa_pool* p, int32_t b) {
   return b >= 0 && b < p->num_blocks && p->refcount[b] > 0;
 }
 
-inline int32_t pop(pa_pool* p) {
-  int32_t b = p->free_stack[--p->top];
+void lru_unlink(pa_pool* p, int32_t b) {
+  const int32_t pr = p->lru_prev[b], nx = p->lru_next[b];
+  if (pr >= 0) p->lru_next[pr] = nx; else p->lru_head = nx;
+  if (nx >= 0) p->lru_prev[nx] = pr; else p->lru_tail = pr;
+  p->lru_prev[b] = p->lru_next[b] = -1;
+  --p->lru_len;
+}
+
+void lru_push_back(pa_pool* p, int32_t b) {
+  p->lru_prev[b] = p->lru_tail;
+  p->lru_next[b] = -1;
+  if (p->lru_tail >= 0) p->lru_next[p->lru_tail] = b; else p->lru_head = b;
+  p->lru_tail = b;
+  ++p->lru_len;
+}
+
+void uncache(pa_pool* p, int32_t b) {
+  p->index->erase(p->key[b]);
+  p->serial[b] = 0;
+  --p->cached;
+}
+
+inline int32_t available(const pa_pool* p) { return p->top + p->lru_len; }
+
+// caller has checked available(p) > 0
+int32_t pop(pa_pool* p) {
+  int32_t b;
+  if (p->top > 0) {
+    b = p->free_stack[--p->top];
+  } else {
+    b = p->lru_head;
+    lru_unlink(p, b);
+    uncache(p, b);
+  }
   p->refcount[b] = 1;
   return b;
 }
 
 inline void drop(pa_pool* p, int32_t b) {
-  if (--p->refcount[b] == 0) p->free_stack[p->top++] = b;
+  if (--p->refcount[b] == 0) {
+    if (p->serial[b] != 0) lru_push_back(p, b);
+    else p->free_stack[p->top++] = b;
+  }
+}
+
+inline void take_ref(pa_pool* p, int32_t b) {
+  if (p->refcount[b] == 0) lru_unlink(p, b);
+  ++p->refcount[b];
+}
+
+Key make_key(uint64_t parent, const int32_t* tokens) {
+  Key k;
+  k.parent = parent;
+  std::memcpy(k.tokens.data(), tokens, sizeof(int32_t) * PA_BLOCK_SIZE);
+  return k;
 }
 
 }  // namespace
@@ -54,6 +151,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported";
     case PA_ERR_DEVICE: return "device error";
     case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_HOST_MEMORY: return "host memory allocation failed";
     default: return "unknown status";
   }
 }
@@ -63,11 +161,23 @@ pa_status pa_pool_create(int32_t num_blocks, const int32_t* free_order, pa_pool*
   *out = nullptr;
   pa_pool* p = new (std::nothrow) pa_pool;
   if (!p) return PA_ERR_INVALID_ARG;
+  const size_t nb = static_cast<size_t>(num_blocks);
   p->num_blocks = num_blocks;
   p->copies = 0;
-  p->free_stack = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * (size_t)num_blocks));
-  p->refcount = static_cast<int32_t*>(std::calloc((size_t)num_blocks, sizeof(int32_t)));
-  if (!p->free_stack || !p->refcount) {
+  p->free_stack = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * nb));
+  p->refcount = static_cast<int32_t*>(std::calloc(nb, sizeof(int32_t)));
+  p->serial = static_cast<uint64_t*>(std::calloc(nb, sizeof(uint64_t)));
+  p->key = static_cast<Key*>(std::malloc(sizeof(Key) * nb));
+  p->lru_prev = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * nb));
+  p->lru_next = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * nb));
+  p->lru_head = p->lru_tail = -1;
+  p->lru_len = 0;
+  p->cached = 0;
+  p->next_serial = 1;
+  p->prefix_hits = 0;
+  p->index = new (std::nothrow) std::unordered_map<Key, int32_t, KeyHash>();
+  if (!p->free_stack || !p->refcount || !p->serial || !p->key || !p->lru_prev || !p->lru_next ||
+      !p->index) {
     pa_pool_destroy(p);
     return PA_ERR_INVALID_ARG;
   }
@@ -81,7 +191,8 @@ pa_status pa_pool_create(int32_t num_blocks, const int32_t* free_order, pa_pool*
     p->refcount[b] = -1;  // seen marker
     p->free_stack[num_blocks - 1 - i] = b;
   }
-  std::memset(p->refcount, 0, sizeof(int32_t) * (size_t)num_blocks);
+  std::memset(p->refcount, 0, sizeof(int32_t) * nb);
+  for (size_t b = 0; b < nb; ++b) p->lru_prev[b] = p->lru_next[b] = -1;
   p->top = num_blocks;
   *out = p;
   return PA_OK;
@@ -91,12 +202,17 @@ void pa_pool_destroy(pa_pool* p) {
   if (!p) return;
   std::free(p->free_stack);
   std::free(p->refcount);
+  std::free(p->serial);
+  std::free(p->key);
+  std::free(p->lru_prev);
+  std::free(p->lru_next);
+  delete p->index;
   delete p;
 }
 
 pa_status pa_alloc(pa_pool* p, int32_t* block_out) {
   if (!p || !block_out) return PA_ERR_INVALID_ARG;
-  if (p->top == 0) return PA_ERR_OUT_OF_BLOCKS;
+  if (available(p) == 0) return PA_ERR_OUT_OF_BLOCKS;
   *block_out = pop(p);
   return PA_OK;
 }
@@ -147,7 +263,7 @@ pa_status pa_append_slots(pa_pool* p, int32_t* row, int32_t* nblocks, int32_t ma
   const int32_t cur = pos / PA_BLOCK_SIZE;
   if (pos % PA_BLOCK_SIZE != 0 && !held(p, row[cur])) return PA_ERR_BAD_BLOCK;
   const bool cow = (pos % PA_BLOCK_SIZE) != 0 && p->refcount[row[cur]] > 1;
-  if (p->top < fresh + (cow ? 1 : 0)) return PA_ERR_OUT_OF_BLOCKS;
+  if (available(p) < fresh + (cow ? 1 : 0)) return PA_ERR_OUT_OF_BLOCKS;
   if (cow) {
     const int32_t src = row[cur];
     const int32_t dst = pop(p);
@@ -170,7 +286,7 @@ int32_t pa_refcount(const pa_pool* p, int32_t b) {
   return p->refcount[b];
 }
 
-int32_t pa_num_free(const pa_pool* p) { return p ? p->top : -1; }
+int32_t pa_num_free(const pa_pool* p) { return p ? available(p) : -1; }
 
 pa_status pa_pool_stats(const pa_pool* p, pa_pool_stats_t* out) {
   if (!p || !out) return PA_ERR_INVALID_ARG;
@@ -180,10 +296,82 @@ pa_status pa_pool_stats(const pa_pool* p, pa_pool_stats_t* out) {
     shared += p->refcount[b] > 1;
   }
   out->num_blocks = p->num_blocks;
-  out->num_free = p->top;
+  out->num_free = available(p);
   out->num_used = used;
   out->num_shared = shared;
   out->copies = p->copies;
+  out->num_cached = p->cached;
+  out->num_evictable = p->lru_len;
+  out->prefix_hits = p->prefix_hits;
+  return PA_OK;
+}
+
+pa_status pa_prefix_match(pa_pool* p, const int32_t* tokens, int32_t num_tokens,
+                          int32_t* table_out, int32_t max_blocks, int32_t* num_matched) {
+  if (!p || !num_matched || num_tokens < 0 || max_blocks < 0 || (num_tokens > 0 && !tokens))
+    return PA_ERR_INVALID_ARG;
+  *num_matched = 0;
+  const int32_t chunks = num_tokens / PA_BLOCK_SIZE;
+  if (chunks > 0 && max_blocks > 0 && !table_out) return PA_ERR_INVALID_ARG;
+  uint64_t parent = 0;
+  int32_t n = 0;
+  while (n < chunks && n < max_blocks) {
+    auto it = p->index->find(make_key(parent, tokens + (size_t)n * PA_BLOCK_SIZE));
+    if (it == p->index->end()) break;
+    const int32_t b = it->second;
+    table_out[n++] = b;
+    parent = p->serial[b];
+  }
+  for (int32_t i = 0; i < n; ++i) take_ref(p, table_out[i]);
+  p->prefix_hits += n;
+  *num_matched = n;
+  return PA_OK;
+}
+
+pa_status pa_prefix_register(pa_pool* p, const int32_t* table_row, int32_t nblocks,
+                             const int32_t* tokens, int32_t num_tokens, int32_t* num_added) {
+  if (!p || nblocks < 0 || num_tokens < 0 || (num_tokens > 0 && !tokens)) return PA_ERR_INVALID_ARG;
+  const int32_t chunks = num_tokens / PA_BLOCK_SIZE;
+  if (chunks > nblocks || (chunks > 0 && !table_row)) return PA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < chunks; ++i) {
+    const int32_t b = table_row[i];
+    if (!held(p, b)) return PA_ERR_BAD_BLOCK;
+    if (p->serial[b] != 0 &&
+        std::memcmp(p->key[b].tokens.data(), tokens + (size_t)i * PA_BLOCK_SIZE,
+                    sizeof(int32_t) * PA_BLOCK_SIZE) != 0)
+      return PA_ERR_INVALID_ARG;
+  }
+  int32_t added = 0;
+  uint64_t parent = 0;
+  const uint64_t first_serial = p->next_serial;
+  for (int32_t i = 0; i < chunks; ++i) {
+    const int32_t b = table_row[i];
+    if (p->serial[b] == 0) {
+      const Key k = make_key(parent, tokens + (size_t)i * PA_BLOCK_SIZE);
+      auto it = p->index->find(k);
+      if (it != p->index->end()) {  // same prefix cached in another block
+        parent = p->serial[it->second];
+        continue;
+      }
+      try {
+        p->index->emplace(k, b);
+      } catch (...) {  // out of host memory: undo this call's entries
+        for (int32_t j = 0; j < i; ++j) {
+          const int32_t c = table_row[j];
+          if (p->serial[c] >= first_serial) uncache(p, c);
+        }
+        p->next_serial = first_serial;
+        if (num_added) *num_added = 0;
+        return PA_ERR_HOST_MEMORY;
+      }
+      p->key[b] = k;
+      p->serial[b] = p->next_serial++;
+      ++p->cached;
+      ++added;
+    }
+    parent = p->serial[b];
+  }
+  if (num_added) *num_added = added;
   return PA_OK;
 }
 

@@ -50,8 +50,10 @@ class HostPhase:
     value: np.ndarray
 
 
-def plan(w):
-    """Host side of the batch: (BlockManager, [A1, A2, B] phases)."""
+def plan(w, prefix_cache: bool = False):
+    """Host side of the batch: (BlockManager, [A1, A2, B] phases).  With
+    ``prefix_cache`` the sequences of a shared prompt take its whole blocks
+    from the pool's prefix cache instead of forking the first one."""
     s_count = w.num_seqs
     lens = np.asarray(w.context_lens, dtype=np.int64)
     max_blocks = max(1, int(-(-lens.max() // BLOCK_SIZE)))
@@ -77,6 +79,16 @@ def plan(w):
     for s in range(s_count):
         p = int(w.prompt_of[s])
         if p < 0:
+            continue
+        if prefix_cache:
+            toks = w.prompt_tokens(p)
+            i0 = bm.match(s, toks)
+            sl, cow = bm.append(s, len(toks) - i0)
+            assert cow is None
+            slots.append(sl)
+            ks.append(w.k_prompt[poff[p] + i0:poff[p + 1]])
+            vs.append(w.v_prompt[poff[p] + i0:poff[p + 1]])
+            bm.register(s, toks)
             continue
         if p in owner:
             bm.fork(s, owner[p])
@@ -118,13 +130,14 @@ class DeviceBatch:
     (same tables) for benchmarks that must not hit in the last-level cache.
     """
 
-    def __init__(self, w, device="cuda", copies: int = 1, fill: float | None = NAN_FILL):
+    def __init__(self, w, device="cuda", copies: int = 1, fill: float | None = NAN_FILL,
+                 prefix_cache: bool = False):
         import torch
 
         self.w = w
         self.device = device
         self.torch_dtype = torch_dtype(w.dtype)
-        self.bm, self.phases = plan(w)
+        self.bm, self.phases = plan(w, prefix_cache)
         self.num_blocks = w.num_blocks + 1  # + poison block
         self.tables = torch.from_numpy(self.bm.rows.copy()).to(device)
         self.context_lens = torch.from_numpy(np.asarray(w.context_lens, np.int32)).to(device)

@@ -90,11 +90,13 @@ def test_single_block_calls_and_errors_match():
     assert lib.refcount(99) == -1
 
 
-@pytest.mark.parametrize("config", [1, 2, 3, 4, "4b", 5])
-def test_workload_tables_slots_and_copies_match_the_oracle(config):
+@pytest.mark.parametrize("config,prefix_cache", [(1, False), (2, False), (3, False), (4, False),
+                                                 ("4b", False), (5, False), (4, True),
+                                                 ("4b", True)])
+def test_workload_tables_slots_and_copies_match_the_oracle(config, prefix_cache):
     w = workloads.make(config, values=False)
-    ref = step.plan(w)
-    bm, phases = runner.plan(w)
+    ref = step.plan(w, prefix_cache)
+    bm, phases = runner.plan(w, prefix_cache)
     for s in range(w.num_seqs):
         assert bm.table(s) == ref.tables[s]
     # table padding points at the extra poison block
@@ -105,8 +107,12 @@ def test_workload_tables_slots_and_copies_match_the_oracle(config):
         assert np.array_equal(ph_lib.slots, ph_ref.slots)
     assert [bm.pool.refcount(b) for b in range(w.num_blocks)] == ref.pool.refcount
     assert bm.pool.num_free() == ref.pool.num_free()
-    if config == 4:
+    if config == 4 and not prefix_cache:
         assert len(phases[2].pairs) == 192
+    if prefix_cache:  # no shared partial block, so nothing to copy
+        assert all(len(ph.pairs) == 0 for ph in phases)
+        st = bm.pool.stats()
+        assert st["cached"] == ref.pool.stats()["cached"] and st["prefix_hits"] == ref.pool.prefix_hits
 
 
 def test_workload_token_values_follow_the_same_slots():
@@ -116,3 +122,88 @@ def test_workload_token_values_follow_the_same_slots():
     _, phases = runner.plan(w)
     for a, b in zip(phases, ref.phases):
         assert np.array_equal(a.key, b.key) and np.array_equal(a.value, b.value)
+
+
+def _err(fn):
+    try:
+        return fn(), None
+    except opool.PoolError as e:
+        return None, type(e).__name__
+    except pa.PAError as e:
+        return None, {-1: "InvalidArg", -2: "OutOfBlocks", -3: "BadBlock"}[e.status]
+
+
+def test_prefix_cache_operation_sequences_match_the_oracle():
+    """match / append / register / free / fork through the prefix cache, with
+    token lists built from a few shared 16-token phrases so that prefixes
+    repeat; tables, counts, free and cached totals, hits and errors must agree
+    after every operation."""
+    for seed in range(4):
+        rnd = random.Random(100 + seed)
+        nb = rnd.choice([12, 40, 96])
+        order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+        ref = opool.BlockPool(nb, order)
+        lib = pa.Pool(nb, order)
+        cap = 12
+        phrases = [[rnd.randrange(3) for _ in range(16)] for _ in range(3)]
+        seqs = []  # [ref table, lib row, lib nblocks, tokens]
+        for _ in range(1500):
+            op = rnd.random()
+            if op < 0.3:
+                toks = sum((rnd.choice(phrases) for _ in range(rnd.randint(0, 4))), [])
+                toks += [rnd.randrange(3) for _ in range(rnd.randint(0, 24))]
+                if not toks:
+                    continue
+                t_ref = ref.match_prefix(toks)
+                m_lib = lib.prefix_match(toks, cap)
+                assert m_lib.tolist() == t_ref
+                row = np.zeros(cap, np.int32)
+                row[:len(m_lib)] = m_lib
+                pos = 16 * len(t_ref)
+                out_ref, e_ref = _err(lambda: ref.append(t_ref, pos, len(toks) - pos, max_blocks=cap))
+                out_lib, e_lib = _err(lambda: lib.append_slots(row, len(m_lib), pos, len(toks) - pos))
+                assert e_ref == e_lib
+                if e_ref is not None:  # give the matched blocks back
+                    ref.free_table(t_ref)
+                    lib.free_table(m_lib)
+                    continue
+                assert list(out_lib[0]) == out_ref[0] and out_lib[2] is None and out_ref[1] is None
+                seqs.append([t_ref, row, out_lib[1], toks])
+                assert ref.register(t_ref, toks) == lib.prefix_register(row[:out_lib[1]], toks)
+            elif op < 0.55 and seqs:
+                sq = rnd.choice(seqs)
+                t_ref, row, nbl, toks = sq
+                new = rnd.choice([[rnd.randrange(3) for _ in range(rnd.randint(1, 20))],
+                                  list(rnd.choice(phrases))])
+                out_ref, e_ref = _err(lambda: ref.append(t_ref, len(toks), len(new), max_blocks=cap))
+                out_lib, e_lib = _err(lambda: lib.append_slots(row, nbl, len(toks), len(new)))
+                assert e_ref == e_lib
+                if e_ref is None:
+                    assert list(out_lib[0]) == out_ref[0] and out_lib[2] == out_ref[1]
+                    sq[2] = out_lib[1]
+                    toks.extend(new)
+                    if out_ref[1] is None:  # a copied block would hold its source's tokens too
+                        assert ref.register(t_ref, toks) == lib.prefix_register(row[:sq[2]], toks)
+            elif op < 0.65 and seqs:
+                sq = rnd.choice(seqs)
+                seqs.append([ref.fork(sq[0]), sq[1].copy(), sq[2], list(sq[3])])
+                lib.fork(sq[1][:sq[2]])
+            elif op < 0.68 and seqs:
+                sq = rnd.choice(seqs)
+                bad = list(sq[3])
+                if len(bad) >= 16:
+                    bad[0] += 1  # claims other tokens for a (maybe cached) block
+                    _, e_ref = _err(lambda: ref.register(sq[0], bad))
+                    _, e_lib = _err(lambda: lib.prefix_register(sq[1][:sq[2]], bad))
+                    assert e_ref == e_lib
+            elif seqs:
+                t_ref, row, nbl, _ = seqs.pop(rnd.randrange(len(seqs)))
+                ref.free_table(t_ref)
+                lib.free_table(row[:nbl])
+            for t_ref, row, nbl, _ in seqs:
+                assert row[:nbl].tolist() == t_ref
+            assert [lib.refcount(b) for b in range(nb)] == ref.refcount
+            st, so = lib.stats(), ref.stats()
+            for k in ("free", "used", "shared", "copies", "cached", "evictable", "prefix_hits"):
+                assert st[k] == so[k], k
+        assert ref.prefix_hits > 0

@@ -20,9 +20,9 @@ from tests.helpers import NAN_BITS, assert_close, bits_of
 pytestmark = pytest.mark.gpu
 
 
-def _run_small(w, partition_size=pa.PARTITION_AUTO):
-    ref_plan, kc, vc, ref = step.run(w, NAN_BITS[w.dtype])
-    db = runner.DeviceBatch(w)
+def _run_small(w, partition_size=pa.PARTITION_AUTO, prefix_cache=False):
+    ref_plan, kc, vc, ref = step.run(w, NAN_BITS[w.dtype], prefix_cache=prefix_cache)
+    db = runner.DeviceBatch(w, prefix_cache=prefix_cache)
     db.prefill()
     db.step(partition_size=partition_size)
     return db, ref
@@ -102,6 +102,15 @@ def test_shared_prefix_small_against_oracle():
                               seed=8, prompt_lens=[21, 32, 45], prompt_of=[0, 0, 0, 1, 1, 1, 2, 2])
     db, ref = _run_small(w)
     assert_close(db.out_bits(), ref, "bf16", "shared prefix")
+
+
+def test_shared_prefix_small_through_prefix_cache_against_oracle():
+    print("[gpu] shared prefix small, prefix cache", flush=True)
+    w = workloads.make_custom([1, 5, 20, 2, 3, 40, 7, 9], hq=8, hkv=2, d=128, dtype="bf16",
+                              seed=8, prompt_lens=[21, 32, 45], prompt_of=[0, 0, 0, 1, 1, 1, 2, 2])
+    db, ref = _run_small(w, prefix_cache=True)
+    assert db.bm.pool.stats()["prefix_hits"] > 0
+    assert_close(db.out_bits(), ref, "bf16", "shared prefix, prefix cache")
 
 
 def test_zero_length_rows_give_zeros_and_others_unaffected():
@@ -239,4 +248,16 @@ def test_full_size_block_relabelling_is_bit_identical():
     db2.prefill()
     db2.step()
     assert not np.array_equal(db2.bm.rows, db.bm.rows)
+    assert np.array_equal(db2.out_bits(), base)
+
+
+def test_full_size_shared_prefix_through_cache_is_bit_identical_to_forks():
+    print("[gpu] full-size workload 4: prefix cache vs forks", flush=True)
+    w, db = _full(4)
+    base = db.out_bits()
+    db2 = runner.DeviceBatch(w, prefix_cache=True)
+    db2.prefill()
+    db2.step()
+    assert not np.array_equal(db2.bm.rows, db.bm.rows)
+    assert db2.bm.pool.stats()["prefix_hits"] == 64 * 3 * 128
     assert np.array_equal(db2.out_bits(), base)

@@ -9,8 +9,11 @@ and reference counts stay equal to table references.
 """
 import random
 
+import numpy as np
 import pytest
 
+import workloads
+from oracle import step
 from oracle.pool import BLOCK_SIZE, BadBlock, BlockPool, InvalidArg, OutOfBlocks, blocks_for
 
 
@@ -215,3 +218,34 @@ def test_random_operations_with_prefix_cache_conserve_references():
                 assert ledger[table[p // BLOCK_SIZE] * BLOCK_SIZE + p % BLOCK_SIZE] == tok
         _conservation(pool, [t for t, _ in seqs])
     assert pool.prefix_hits > 100
+
+
+@pytest.mark.parametrize("config", [4, "4b"])
+def test_shared_prefix_workload_through_the_cache_closed_forms(config):
+    """The shared-prefix workloads with their prompts taken from the cache
+    instead of forked: every prompt's whole blocks are cached once, every
+    later sequence of a prompt hits all of them, nothing is copied, and the
+    pool ends with exactly as many blocks in use as fork + copy-on-write."""
+    w = workloads.make(config, values=False)
+    forked = step.plan(w)
+    cached = step.plan(w, prefix_cache=True)
+    n_prompts = len(w.prompt_lens)
+    per = [int(np.sum(w.prompt_of == p)) for p in range(n_prompts)]
+    whole = [int(n) // BLOCK_SIZE for n in w.prompt_lens]
+    st = cached.pool.stats()
+    assert st["cached"] == sum(whole)
+    assert cached.pool.prefix_hits == sum((k - 1) * b for k, b in zip(per, whole))
+    assert all(len(ph.pairs) == 0 for ph in cached.phases)
+    assert st["used"] == forked.pool.stats()["used"]
+    for s in range(w.num_seqs):
+        assert len(cached.tables[s]) == blocks_for(int(w.context_lens[s]))
+
+
+def test_decode_through_the_cache_equals_decode_through_forks():
+    """Attention sees only each sequence's K/V, not where the blocks sit:
+    the prefix-cached layout decodes bit-identically to the forked one."""
+    w = workloads.make_custom([3, 17, 1, 30, 2, 16], hq=4, hkv=2, d=16, dtype="bf16", seed=12,
+                              prompt_lens=[37, 32], prompt_of=[0, 0, 0, 1, 1, 1])
+    _, _, _, a = step.run(w, np.uint16(0x7FC0))
+    _, _, _, b = step.run(w, np.uint16(0x7FC0), prefix_cache=True)
+    assert np.array_equal(a, b)

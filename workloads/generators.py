@@ -118,6 +118,12 @@ class Workload:
     def elem_bytes(self) -> int:
         return elem_bytes(self.dtype)
 
+    def prompt_tokens(self, p: int) -> np.ndarray:
+        """Token ids of shared prompt ``p`` (int32): id = p * 2**16 + position.
+        The K/V drawn for a prompt token belong to that id alone, so a prefix
+        cache keyed on ids may share them."""
+        return (int(p) * 65536 + np.arange(int(self.prompt_lens[p]))).astype(np.int32)
+
     def sequence_kv(self, s: int):
         """Contiguous (K, V) bits of sequence ``s``, positions 0..len-1."""
         parts_k, parts_v = [], []
