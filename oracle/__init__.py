@@ -25,6 +25,9 @@ What it computes, and where the pages define it
 * ``accounting``-- the KV-size closed form and the block/waste arithmetic
                    ("KV Cache for the intermediate", section "Precise scientific
                    definition", the KV_size equation and its worked example).
+* ``quant``     -- the INT8 cache: per-channel symmetric codes, and decode
+                   attention over the values they stand for ("KV Cache for the
+                   intermediate", section "KV Cache Quantization").
 * ``step``      -- the order in which a batch is prefilled and stepped, built
                    from the calls above.
 
@@ -32,4 +35,4 @@ Every function is pinned by ``tests/test_oracle_*.py`` against values the pages
 print, closed forms, brute force on tiny inputs, a library routine and
 invariants; see the header of each module for the pins that cover it.
 """
-from . import accounting, attention, cache_ops, numerics, pool, step  # noqa: F401
+from . import accounting, attention, cache_ops, numerics, pool, quant, step  # noqa: F401

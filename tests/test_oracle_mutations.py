@@ -128,3 +128,30 @@ def test_planted_match_without_reference_is_caught(monkeypatch):
     monkeypatch.setattr(pool.BlockPool, "match_prefix", match_no_ref)
     with pytest.raises((AssertionError, pool.PoolError)):  # a count check, or a later call on an unheld block
         tpre.test_cached_blocks_outlive_their_sequence()
+
+
+from oracle import quant  # noqa: E402
+from tests import test_oracle_quant as tq  # noqa: E402
+
+
+def _quantize_with(rounding, lo=-127):
+    def q(bits, dtype, scale):
+        from oracle.numerics import to_f64
+        x = to_f64(bits, dtype).astype(np.float32)
+        with np.errstate(over="ignore", invalid="ignore"):
+            y = rounding(x / np.asarray(scale, np.float32))
+        y = np.where(np.isnan(y), np.float32(0), y)
+        return np.clip(y, lo, 127).astype(np.int8)
+    return q
+
+
+@pytest.mark.parametrize("bad,pin", [
+    (_quantize_with(np.trunc), lambda: tq.test_codes_are_the_nearest_integer_of_the_exact_ratio("bf16")),
+    (_quantize_with(lambda y: np.sign(y) * np.floor(np.abs(y) + 0.5)),
+     tq.test_ties_go_to_even_and_sign_is_symmetric),
+    (_quantize_with(np.rint, lo=-128), tq.test_saturation_infinities_nan_and_no_minus_128),
+], ids=["truncate", "half-away", "minus-128"])
+def test_planted_quantization_mistake_is_caught(monkeypatch, bad, pin):
+    monkeypatch.setattr(quant, "quantize", bad)
+    with pytest.raises(AssertionError):
+        pin()
