@@ -33,6 +33,14 @@
  *      ((b * Hkv + h) * (D / X) + d / X) * 16 * X + r * X + d % X.
  *   V: [num_blocks][Hkv][D][16]: at ((b * Hkv + h) * D + d) * 16 + r.
  *   Slot s is row s % 16 of block s / 16.
+ *
+ * INT8 cache layout (PA_I8; int8 codes, D a multiple of 64): each (block,
+ * head) is D * 16 bytes at (b * Hkv + h) * D * 16, made of D / 64 slabs of
+ * 1 KiB; in slab d / 64:
+ *   K: token r, dimension d at ((d / 16) % 4 * 16 + r) * 16 + d % 16;
+ *   V: token r, dimension d at ((r / 4) * 16 + d % 16) * 16 + (d / 16) % 4 * 4 + r % 4.
+ * Either way one 16-byte load per lane of a 64-lane wave reads a contiguous
+ * KiB that feeds the matrix cores directly.
  */
 #ifndef PA_H
 #define PA_H
@@ -59,6 +67,7 @@ typedef int32_t pa_dtype;
 #define PA_F32 0
 #define PA_F16 1
 #define PA_BF16 2
+#define PA_I8 3 /* codes of an INT8 cache: pa_copy_blocks and the *_int8 calls */
 
 #define PA_BLOCK_SIZE 16
 
@@ -277,6 +286,45 @@ pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const vo
                                     int32_t max_blocks_per_seq, int32_t max_context_len,
                                     int32_t partition_size, void* workspace,
                                     size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * INT8 KV cache ("KV Cache for the intermediate", section "KV Cache
+ * Quantization": K and V kept as 8-bit integers instead of 16-bit floats
+ * halve the cache, with per-channel scales).  Symmetric codes with one fp32
+ * scale per (KV head, channel), k_scale and v_scale device [Hkv][D], all > 0,
+ * chosen by the caller; the cache stands for the values code * scale.  Block
+ * copies use pa_copy_blocks with dtype PA_I8.
+ * ------------------------------------------------------------------------- */
+
+/* Quantize and store the K and V of `num_tokens` new tokens:
+ * code = clamp(rint(x / scale), -127, 127), with x the value of key / value
+ * (dtype F32, F16 or BF16, [num_tokens][Hkv][D]) in fp32, one IEEE fp32
+ * division and round-half-to-even; NaN gives 0.  Codes go to the INT8 layout
+ * above.  Slots out of [0, num_blocks * 16) are skipped; tokens must map to
+ * distinct slots.  head_dim: a multiple of 64, at most 512. */
+pa_status pa_reshape_and_cache_int8(const void* key, const void* value, void* k_cache,
+                                    void* v_cache, const int64_t* slot_mapping,
+                                    const float* k_scale, const float* v_scale,
+                                    int32_t num_tokens, int32_t num_blocks,
+                                    int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                    void* stream);
+
+/* pa_paged_attention_decode over an INT8 cache: out[s, h] = attention of
+ * q[s, h] over the values code_K * k_scale, code_V * v_scale of the
+ * sequence's positions.  q and out have dtype F16 or BF16; head_dim 64 or
+ * 128; partition_size NONE, AUTO or a positive multiple of 16 (the balanced
+ * split serves 16-bit caches only); the workspace is sized by
+ * pa_decode_workspace_bytes as for a 16-bit cache.  Other arguments and
+ * errors as pa_paged_attention_decode. */
+pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, const void* v_cache,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_tables,
+                                         const int32_t* context_lens, float scale, void* out,
+                                         int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         int32_t partition_size, void* workspace,
+                                         size_t workspace_bytes, pa_dtype dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Kernel timing.  Between pa_timing_begin and pa_timing_end every kernel the

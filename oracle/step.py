@@ -26,7 +26,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import attention, cache_ops
+from . import attention, cache_ops, quant
 from .pool import BLOCK_SIZE as pool_block
 from .pool import BlockPool
 
@@ -145,6 +145,24 @@ def run(w, fill_bits, phases=None, prefix_cache: bool = False):
     out = attention.paged_decode(w.q, k_cache, v_cache, pl.padded_tables(width, 0),
                                  pl.context_lens, w.scale, w.dtype)
     return pl, k_cache, v_cache, out
+
+
+def run_int8(w, fill_code: int = 127, prefix_cache: bool = False):
+    """``run`` over an INT8 cache with the workload's per-channel scales: the
+    phases' tokens are quantized as they are written.  Returns (plan, k_codes,
+    v_codes, out)."""
+    pl = plan(w, prefix_cache)
+    sk, sv = w.int8_scales()
+    shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    k_codes = np.full(shape, fill_code, dtype=np.int8)
+    v_codes = k_codes.copy()
+    for ph in pl.phases:
+        cache_ops.copy_blocks(k_codes, v_codes, ph.pairs)
+        quant.reshape_and_cache(ph.key, ph.value, w.dtype, k_codes, v_codes, ph.slots, sk, sv)
+    width = max(1, max(len(t) for t in pl.tables))
+    out = quant.paged_decode(w.q, k_codes, v_codes, sk, sv, pl.padded_tables(width, 0),
+                             pl.context_lens, w.scale, w.dtype)
+    return pl, k_codes, v_codes, out
 
 
 def decode_sequences(w, k_cache, v_cache, tables, seqs) -> np.ndarray:

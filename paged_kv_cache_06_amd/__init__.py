@@ -6,7 +6,8 @@ memory and the stream; nothing here computes on tensors.  When ``libpa.so`` is
 missing every call raises -- there is no fallback.
 
 The names follow the C ABI of ``include/pa.h`` without its ``pa_`` prefix:
-``reshape_and_cache``, ``copy_blocks``, ``paged_attention_decode``, the pool
+``reshape_and_cache``, ``copy_blocks``, ``paged_attention_decode``, their INT8
+cache forms ``reshape_and_cache_int8`` and ``paged_attention_decode_int8``, the pool
 calls on :class:`Pool` (``alloc``, ``free``, ``incref``, ``fork``,
 ``free_table``, ``append_slots``, ``prefix_match``, ``prefix_register``,
 ``refcount``, ``num_free``, ``stats``) and ``blocks_for_bytes``.
@@ -22,8 +23,8 @@ __all__ = [
     "BLOCK_SIZE", "PARTITION_NONE", "PARTITION_AUTO", "PARTITION_BALANCED", "PAError", "load", "lib_path",
     "Pool", "BlockManager", "blocks_for_bytes", "reshape_and_cache", "copy_blocks",
     "paged_attention_decode", "decode_workspace_bytes", "decode_auto_partition",
-    "decode_set_max_groups",
-    "new_kv_cache", "logical_view", "timing_begin", "timing_end", "status_string",
+    "decode_set_max_groups", "reshape_and_cache_int8", "paged_attention_decode_int8",
+    "new_kv_cache", "new_kv_cache_int8", "logical_view", "timing_begin", "timing_end", "status_string",
 ]
 
 BLOCK_SIZE = 16
@@ -74,6 +75,11 @@ _SIGNATURES = {
     "pa_paged_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_p, _c_i32,
                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                            _c_p, _c_sz, _c_i32, _c_p]),
+    "pa_reshape_and_cache_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
+                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
+    "pa_paged_attention_decode_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f,
+                                                _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                _c_i32, _c_i32, _c_p, _c_sz, _c_i32, _c_p]),
     "pa_timing_begin": (_c_i32, [_c_i32]),
     "pa_timing_end": (_c_i32, [ctypes.POINTER(ctypes.c_double), _P_I32]),
 }
@@ -288,7 +294,7 @@ def _torch():
 
 def _dtype_code(t) -> int:
     torch = _torch()
-    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int8: 3}
     if t.dtype not in codes:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return codes[t.dtype]
@@ -323,8 +329,31 @@ def new_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, devic
             torch.full(vshape, fill, dtype=dtype, device=device))
 
 
+def new_kv_cache_int8(num_blocks: int, num_kv_heads: int, head_dim: int, device="cuda",
+                      fill: int | None = None):
+    """(k_cache, v_cache) int8 tensors of an INT8 cache: [NB, Hkv, D/64, 1024],
+    one KiB slab of 64 dimensions x 16 tokens per row (layout in include/pa.h)."""
+    torch = _torch()
+    _need(head_dim % 64 == 0, "head_dim must be a multiple of 64")
+    shape = (num_blocks, num_kv_heads, head_dim // 64, 1024)
+    if fill is None:
+        return (torch.empty(shape, dtype=torch.int8, device=device),
+                torch.empty(shape, dtype=torch.int8, device=device))
+    return (torch.full(shape, fill, dtype=torch.int8, device=device),
+            torch.full(shape, fill, dtype=torch.int8, device=device))
+
+
 def logical_view(k_cache, v_cache):
     """The caches as [num_blocks, Hkv, 16, head_dim] copies (for inspection)."""
+    torch = _torch()
+    if k_cache.dtype == torch.int8:
+        nb, hkv, slabs, _ = k_cache.shape
+        # K slab: [chunk of 16 dims][token][dim % 16]
+        k = k_cache.reshape(nb, hkv, slabs, 4, 16, 16).permute(0, 1, 4, 2, 3, 5)
+        # V slab: [token / 4][dim % 16][16-dim slice][token % 4]
+        v = v_cache.reshape(nb, hkv, slabs, 4, 16, 4, 4).permute(0, 1, 3, 6, 2, 5, 4)
+        return (k.reshape(nb, hkv, 16, slabs * 64).contiguous(),
+                v.reshape(nb, hkv, 16, slabs * 64).contiguous())
     nb, hkv, dx, bs, x = k_cache.shape
     k = k_cache.permute(0, 1, 3, 2, 4).reshape(nb, hkv, bs, dx * x)
     v = v_cache.permute(0, 1, 3, 2)
@@ -332,6 +361,14 @@ def logical_view(k_cache, v_cache):
 
 
 def _cache_dims(k_cache, v_cache):
+    torch = _torch()
+    if k_cache.dtype == torch.int8:
+        _need(k_cache.dim() == 4 and k_cache.shape[3] == 1024 and
+              tuple(v_cache.shape) == tuple(k_cache.shape) and v_cache.dtype == torch.int8,
+              "INT8 caches must both be int8 [NB, Hkv, D/64, 1024]")
+        _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+        nb, hkv, slabs, _ = k_cache.shape
+        return nb, hkv, slabs * 64
     _need(k_cache.dim() == 5 and v_cache.dim() == 4, "caches must be [NB,Hkv,D/X,16,X] and "
           "[NB,Hkv,D,16]")
     nb, hkv, dx, bs, x = k_cache.shape
@@ -369,6 +406,32 @@ def copy_blocks(k_cache, v_cache, block_pairs) -> None:
     _check(load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs.contiguous()), n,
                                  nb, hkv, d, _dtype_code(k_cache), _stream(k_cache)),
            "pa_copy_blocks")
+
+
+def _scales(scale, hkv, d, name):
+    torch = _torch()
+    _need(scale.dtype == torch.float32 and tuple(scale.shape) == (hkv, d) and
+          scale.is_contiguous(), f"{name} must be contiguous float32 [Hkv, D]")
+    return _ptr(scale)
+
+
+def reshape_and_cache_int8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale) -> None:
+    """Quantize key/value [T, Hkv, D] (fp32/fp16/bf16) with per-channel scales
+    k_scale / v_scale (float32 [Hkv, D]) and write the codes into their slots."""
+    torch = _torch()
+    _need(k_cache.dtype == torch.int8, "INT8 caches expected")
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    t = key.shape[0]
+    _need(tuple(key.shape) == (t, hkv, d) and tuple(value.shape) == (t, hkv, d),
+          "key/value must be [T, Hkv, D]")
+    _need(key.is_contiguous() and value.is_contiguous(), "key/value must be contiguous")
+    _need(key.dtype == value.dtype, "key/value dtypes differ")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == t,
+          "slot_mapping must be int64 [T]")
+    _check(load().pa_reshape_and_cache_int8(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping.contiguous()),
+        _scales(k_scale, hkv, d, "k_scale"), _scales(v_scale, hkv, d, "v_scale"), t, nb, hkv, d,
+        _dtype_code(key), _stream(key)), "pa_reshape_and_cache_int8")
 
 
 def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
@@ -415,6 +478,15 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
           "context_lens must be int32 [S]")
     mb = block_tables.shape[1]
     mcl = mb * BLOCK_SIZE if max_context_len is None else int(max_context_len)
+    ws_ptr, ws_bytes = _workspace(q, s, hq, d, mcl, partition_size, workspace)
+    _check(load().pa_paged_attention_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens.contiguous()),
+        float(scale), _ptr(out), s, hq, hkv, d, mb, mcl, int(partition_size), ws_ptr, ws_bytes,
+        _dtype_code(q), _stream(q)), "pa_paged_attention_decode")
+
+
+def _workspace(q, s, hq, d, mcl, partition_size, workspace):
+    torch = _torch()
     need = decode_workspace_bytes(s, hq, d, mcl, partition_size)
     if workspace is None and need > 0:
         key = (q.device, need)
@@ -425,10 +497,34 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
             _workspaces[key] = workspace
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(load().pa_paged_attention_decode(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens.contiguous()),
+    return ws_ptr, ws_bytes
+
+
+def paged_attention_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                context_lens, scale, out, *, max_context_len: int | None = None,
+                                partition_size: int = PARTITION_AUTO, workspace=None) -> None:
+    """paged_attention_decode over an INT8 cache whose values are code * scale
+    (k_scale / v_scale float32 [Hkv, D]); q and out fp16 or bf16."""
+    torch = _torch()
+    _need(k_cache.dtype == torch.int8, "INT8 caches expected")
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    s, hq, dq = q.shape
+    _need(dq == d and tuple(out.shape) == (s, hq, d), "q/out must be [S, Hq, D]")
+    _need(q.is_contiguous() and out.is_contiguous(), "q/out must be contiguous")
+    _need(q.dtype == out.dtype, "q/out dtypes differ")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == s and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == s,
+          "context_lens must be int32 [S]")
+    mb = block_tables.shape[1]
+    mcl = mb * BLOCK_SIZE if max_context_len is None else int(max_context_len)
+    ws_ptr, ws_bytes = _workspace(q, s, hq, d, mcl, partition_size, workspace)
+    _check(load().pa_paged_attention_decode_int8(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _scales(k_scale, hkv, d, "k_scale"),
+        _scales(v_scale, hkv, d, "v_scale"), _ptr(block_tables), _ptr(context_lens.contiguous()),
         float(scale), _ptr(out), s, hq, hkv, d, mb, mcl, int(partition_size), ws_ptr, ws_bytes,
-        _dtype_code(q), _stream(q)), "pa_paged_attention_decode")
+        _dtype_code(q), _stream(q)), "pa_paged_attention_decode_int8")
 
 
 # ------------------------------------------------------------------ timing

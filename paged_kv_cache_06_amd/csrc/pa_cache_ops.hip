@@ -52,6 +52,50 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   for (int i = 0; i < X; ++i) vdst[i * kBlock] = vv.e[i];
 }
 
+// INT8 cache ("KV Cache for the intermediate", section "KV Cache
+// Quantization"): one thread per (token, head, 16-dimension chunk c).  Codes
+// are clamp(rint(x / s), -127, 127) in fp32 (NaN -> 0); the 16 K codes of a
+// chunk are one 16-byte store, the 16 V codes land 16 bytes apart (the V
+// layout groups 4 tokens of 4 dimension slices per lane of the decode).
+template <typename Tag>
+__global__ __launch_bounds__(256) void reshape_and_cache_i8_kernel(
+    const typename Tag::Bits* __restrict__ key, const typename Tag::Bits* __restrict__ value,
+    int8_t* __restrict__ k_cache, int8_t* __restrict__ v_cache, const int64_t* __restrict__ slots,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int32_t num_tokens,
+    int64_t num_slots, int32_t hkv, int32_t head_dim) {
+  const int chunks = head_dim / 16;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(num_tokens) * hkv * chunks;
+  if (gid >= total) return;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t th = gid / chunks;  // token * hkv + head
+  const int h = static_cast<int>(th % hkv);
+  const int64_t t = th / hkv;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t b = slot / kBlock;
+  const int r = static_cast<int>(slot % kBlock);
+  const int64_t src = th * head_dim + static_cast<int64_t>(c) * 16;
+  const float* ks = k_scale + static_cast<int64_t>(h) * head_dim + c * 16;
+  const float* vs = v_scale + static_cast<int64_t>(h) * head_dim + c * 16;
+  const int64_t slab = (b * hkv + h) * static_cast<int64_t>(head_dim) * kBlock + (c / 4) * 1024;
+
+  auto code = [](float x, float s) {
+    float y = rintf(__fdiv_rn(x, s));
+    y = (y != y) ? 0.f : fminf(fmaxf(y, -127.f), 127.f);
+    return static_cast<uint32_t>(static_cast<int32_t>(y)) & 0xFFu;
+  };
+  uint32_t kw[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) kw[e / 4] |= code(Tag::to_f32(key[src + e]), ks[e]) << (8 * (e % 4));
+  *reinterpret_cast<uint4*>(k_cache + slab + ((c % 4) * 16 + r) * 16) =
+      make_uint4(kw[0], kw[1], kw[2], kw[3]);
+  int8_t* vdst = v_cache + slab + ((r / 4) * 16) * 16 + (c % 4) * 4 + r % 4;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    vdst[e * 16] = static_cast<int8_t>(code(Tag::to_f32(value[src + e]), vs[e]));
+}
+
 // grid.x = pair * 2 + (0: K, 1: V); grid.y splits the block's bytes.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
                                                           uint4* __restrict__ v_cache,
@@ -80,6 +124,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
 }
 
 bool cache_shape_ok(int32_t num_blocks, int32_t hkv, int32_t head_dim, pa_dtype dt) {
+  if (dt == PA_I8) return num_blocks > 0 && hkv > 0 && head_dim > 0 && head_dim % 64 == 0 &&
+                          head_dim <= 512;
   if (!valid_dtype(dt) || num_blocks <= 0 || hkv <= 0 || head_dim <= 0) return false;
   const int x = 16 / elem_bytes(dt);
   return head_dim % x == 0 && head_dim <= 512;
@@ -122,12 +168,51 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   return s;
 }
 
+pa_status pa_reshape_and_cache_int8(const void* key, const void* value, void* k_cache,
+                                    void* v_cache, const int64_t* slot_mapping,
+                                    const float* k_scale, const float* v_scale,
+                                    int32_t num_tokens, int32_t num_blocks,
+                                    int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                    void* stream) {
+  using namespace pa;
+  if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || !cache_shape_ok(num_blocks, num_kv_heads, head_dim, PA_I8))
+    return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping || !k_scale || !v_scale)
+    return PA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / 16);
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * kBlock;
+  int8_t* kc = static_cast<int8_t*>(k_cache);
+  int8_t* vc = static_cast<int8_t*>(v_cache);
+  const int slot = timing_start(PA_KERNEL_RESHAPE_AND_CACHE, st);
+  const dim3 g(static_cast<uint32_t>(grid)), b(256);
+  if (dtype == PA_F32)
+    reshape_and_cache_i8_kernel<F32T><<<g, b, 0, st>>>(
+        static_cast<const float*>(key), static_cast<const float*>(value), kc, vc, slot_mapping,
+        k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim);
+  else if (dtype == PA_BF16)
+    reshape_and_cache_i8_kernel<BF16T><<<g, b, 0, st>>>(
+        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), kc, vc,
+        slot_mapping, k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim);
+  else
+    reshape_and_cache_i8_kernel<F16T><<<g, b, 0, st>>>(
+        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), kc, vc,
+        slot_mapping, k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim);
+  const pa_status s = launch_status();
+  timing_stop(slot, st);
+  return s;
+}
+
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
                          int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
                          int32_t head_dim, pa_dtype dtype, void* stream) {
   using namespace pa;
   if (num_pairs < 0 || !cache_shape_ok(num_blocks, num_kv_heads, head_dim, dtype))
-    return valid_dtype(dtype) ? PA_ERR_INVALID_ARG : PA_ERR_UNSUPPORTED;
+    return valid_dtype(dtype) || dtype == PA_I8 ? PA_ERR_INVALID_ARG : PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
   if (num_pairs > (0x7fffffff >> 1)) return PA_ERR_INVALID_ARG;

@@ -13,7 +13,7 @@ namespace pa {
 constexpr int kBlock = PA_BLOCK_SIZE;  // token slots per KV block
 constexpr int kWave = 64;
 
-inline int elem_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : 2; }
+inline int elem_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : dt == PA_I8 ? 1 : 2; }
 inline bool valid_dtype(pa_dtype dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
 
 // ---- scalar conversions (storage bits <-> fp32) ----

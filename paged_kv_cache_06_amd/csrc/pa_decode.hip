@@ -47,6 +47,7 @@
 // work-group per query head, VALU dot products, 256-position chunks with the
 // same online softmax and the same partial-result format.
 #include "pa_decode_balanced.h"
+#include "pa_decode_int8.h"
 #include "pa_decode_common.h"
 namespace pa {
 namespace {
@@ -180,6 +181,58 @@ __global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_ke
     const int h = e / D, d = e % D;
     float M, L, A;
     combine_waves<W>(comb, a.nh_max, D, h, d, M, L, A);
+    const size_t row = row0 + h;
+    if (nparts <= 1) {
+      a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
+    } else {
+      const size_t part = row * a.np_max + p;
+      a.ws_acc[part * D + d] = A;
+      if (d == 0) {
+        a.ws_ml[2 * part] = M;
+        a.ws_ml[2 * part + 1] = L;
+      }
+    }
+  }
+}
+
+// decode_items_kernel over an INT8 cache (same items, partitions and
+// partials); the V scale multiplies each merged result before it is stored.
+template <typename Tag, int D>
+__global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_i8_kernel(
+    DecodeArgs a, const int4* __restrict__ items) {
+  constexpr int W = kItemWaves;
+  extern __shared__ float comb[];
+  const int heads = a.hkv * a.head_blocks;
+  const int4 it = items[blockIdx.x / heads];
+  if (it.x < 0) return;
+  const int gh = blockIdx.x % heads;
+  const int s = it.x, p = it.y, len = it.z;
+  const int g = gh / a.head_blocks, h0 = (gh % a.head_blocks) * 16;
+  const int nh = min(16, a.group - h0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int start = p * a.part_size;
+  const int end = min(len, start + a.part_size);
+  const int nblk = max(end - start + kBlock - 1, 0) / kBlock;
+  const int b_first = start / kBlock + wave;
+  const int count = nblk > wave ? (nblk - wave + W - 1) / W : 0;
+  const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
+  const int ids = load_ids<W>(trow, b_first, count);
+  uint4 qh[D / 32], ql[D / 32];
+  const float back = load_q_i8<Tag, D>(a, s, g, h0, nh, qh, ql);
+  WaveState<D> st;
+  st.reset();
+  attend_blocks_i8<D, W>(a, trow, ids, b_first, count, end, g, qh, ql, a.scale_log2 * back, st);
+  stage_partials<D, W>(comb, a.nh_max, nh, st);
+  __syncthreads();
+
+  const int nparts = min((len + a.part_size - 1) / a.part_size, a.np_max);
+  const size_t row0 = static_cast<size_t>(s) * a.hq_total + g * a.group + h0;
+  const float* vs = a.v_scale + static_cast<size_t>(g) * D;
+  for (int e = threadIdx.x; e < nh * D; e += W * kWave) {
+    const int h = e / D, d = e % D;
+    float M, L, A;
+    combine_waves<W>(comb, a.nh_max, D, h, d, M, L, A);
+    A *= vs[d];
     const size_t row = row0 + h;
     if (nparts <= 1) {
       a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
@@ -429,7 +482,7 @@ template <typename Tag>
 pa_status launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
                  const int32_t* lens, float scale_log2, void* out, int num_seqs, int hq, int hkv,
                  int head_dim, int max_blocks, const Split& sp, char* ws, bool use_mfma,
-                 hipStream_t st) {
+                 hipStream_t st, const float* k_scale = nullptr, const float* v_scale = nullptr) {
   using E = typename Tag::Bits;
   const int group = hq / hkv;
   const int head_blocks = use_mfma ? (group + 15) / 16 : 1;
@@ -455,14 +508,22 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   pa_status status = PA_OK;
   if (use_mfma) {
     if constexpr (sizeof(E) == 2) {
-      const DecodeArgs a = mfma_args<Tag>(q, k_cache, v_cache, tables, lens, scale_log2, out,
-                                          num_seqs, hq, hkv, max_blocks, sp, ws_ml, ws_acc);
+      DecodeArgs a = mfma_args<Tag>(q, k_cache, v_cache, tables, lens, scale_log2, out,
+                                    num_seqs, hq, hkv, max_blocks, sp, ws_ml, ws_acc);
+      a.k_scale = k_scale;
+      a.v_scale = v_scale;
       const size_t lds = comb_floats(kItemWaves, a.nh_max, head_dim) * sizeof(float);
       const dim3 g3(static_cast<uint32_t>(grid)), b3(kItemThreads);
-      if (head_dim == 128)
+      if (k_scale) {  // INT8 cache
+        if (head_dim == 128)
+          decode_items_i8_kernel<Tag, 128><<<g3, b3, lds, st>>>(a, items);
+        else
+          decode_items_i8_kernel<Tag, 64><<<g3, b3, lds, st>>>(a, items);
+      } else if (head_dim == 128) {
         decode_items_kernel<Tag, 128><<<g3, b3, lds, st>>>(a, items);
-      else
+      } else {
         decode_items_kernel<Tag, 64><<<g3, b3, lds, st>>>(a, items);
+      }
       status = launch_status();
     }
   } else {
@@ -487,6 +548,47 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
 }  // namespace pa
 
 extern "C" {
+
+pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, const void* v_cache,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_tables,
+                                         const int32_t* context_lens, float scale, void* out,
+                                         int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         int32_t partition_size, void* workspace,
+                                         size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  using namespace pa;
+  if (dtype != PA_BF16 && dtype != PA_F16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (partition_size == PA_PARTITION_BALANCED) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
+    return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !context_lens || !out)
+    return PA_ERR_INVALID_ARG;
+  Split sp;
+  if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp))
+    return PA_ERR_INVALID_ARG;
+  const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return PA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const float scale_log2 = scale * kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == PA_BF16)
+    return launch<BF16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
+                         ws, true, st, k_scale, v_scale);
+  return launch<F16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out, num_seqs,
+                      num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp, ws, true, st,
+                      k_scale, v_scale);
+}
 
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype) {

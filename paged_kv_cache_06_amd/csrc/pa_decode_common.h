@@ -102,6 +102,8 @@ struct DecodeArgs {
   uint16_t* out;
   float* ws_ml;
   float* ws_acc;
+  const float* k_scale;  // INT8 cache only: [Hkv][D] per-channel scales
+  const float* v_scale;
   float scale_log2;
   int num_seqs, hq_total, hkv, group, head_blocks, max_blocks, part_size, np_max;
   int nh_max;  // query heads of the largest head group (<= 16): LDS rows per wave
@@ -189,24 +191,20 @@ __device__ __forceinline__ void load_block(const DecodeArgs& a, int g, int phys,
   for (int sl = 0; sl < D / 16; ++sl) r.vf[sl] = buffer_load8(rv, vo + sl * 512);
 }
 
-// One block (logical index blk) into the running state: positions at or past
-// `len` are masked.
-// `qf(t)` gives the B operand of QK k-step t (registers or LDS).
-template <typename Tag, int D, typename QOperand>
-__device__ __forceinline__ void attend_block(const DecodeArgs& a, BlockRegs<D>& r, int blk,
-                                             int len, const QOperand& qf, WaveState<D>& st) {
-  constexpr int kSteps = D / 32;   // QK k-steps of 32 dims
+// Softmax update and PV product of one block (logical index blk) whose raw
+// scores sc (lane l: head l%16, tokens 4*(l/16) .. +3) are known: scores are
+// multiplied by sl2 (the softmax scale in log2 units), positions at or past
+// `len` are masked, vf holds the block's V as PV A operands.
+template <typename Tag, int D>
+__device__ __forceinline__ void block_update(uint2* vf, f32x4_t sc, float sl2, int blk, int len,
+                                             WaveState<D>& st) {
   constexpr int kSlices = D / 16;  // PV output slices of 16 dims
   const int lane = threadIdx.x & (kWave - 1);
   const int kg = lane >> 4;  // k-group of the MFMA operands
-  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < kSteps; ++t) sc = Mfma<Tag>::qk(r.kf[t], qf(t), sc);
-
   const int pos0 = blk * kBlock + kg * 4;  // position of this lane's first score
   float s4[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s4[i] = (pos0 + i < len) ? sc[i] * a.scale_log2 : -INFINITY;
+  for (int i = 0; i < 4; ++i) s4[i] = (pos0 + i < len) ? sc[i] * sl2 : -INFINITY;
   float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -225,8 +223,8 @@ __device__ __forceinline__ void attend_block(const DecodeArgs& a, BlockRegs<D>& 
     const uint32_t hi = (pos0 + 2 < len ? 0x0000FFFFu : 0u) | (pos0 + 3 < len ? 0xFFFF0000u : 0u);
 #pragma unroll
     for (int sl = 0; sl < kSlices; ++sl) {
-      r.vf[sl].x &= lo;
-      r.vf[sl].y &= hi;
+      vf[sl].x &= lo;
+      vf[sl].y &= hi;
     }
   }
   // P as hi + lo in the storage dtype: two products, near-fp32 weights
@@ -235,9 +233,22 @@ __device__ __forceinline__ void attend_block(const DecodeArgs& a, BlockRegs<D>& 
                                    p4[2] - Mfma<Tag>::lo(ph.y), p4[3] - Mfma<Tag>::hi(ph.y));
 #pragma unroll
   for (int sl = 0; sl < kSlices; ++sl) {
-    st.acc[sl] = Mfma<Tag>::pv(r.vf[sl], ph, st.acc[sl]);
-    st.acc[sl] = Mfma<Tag>::pv(r.vf[sl], pl, st.acc[sl]);
+    st.acc[sl] = Mfma<Tag>::pv(vf[sl], ph, st.acc[sl]);
+    st.acc[sl] = Mfma<Tag>::pv(vf[sl], pl, st.acc[sl]);
   }
+}
+
+// One block (logical index blk) into the running state: positions at or past
+// `len` are masked.
+// `qf(t)` gives the B operand of QK k-step t (registers or LDS).
+template <typename Tag, int D, typename QOperand>
+__device__ __forceinline__ void attend_block(const DecodeArgs& a, BlockRegs<D>& r, int blk,
+                                             int len, const QOperand& qf, WaveState<D>& st) {
+  constexpr int kSteps = D / 32;   // QK k-steps of 32 dims
+  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < kSteps; ++t) sc = Mfma<Tag>::qk(r.kf[t], qf(t), sc);
+  block_update<Tag, D>(r.vf, sc, a.scale_log2, blk, len, st);
 }
 
 // Attends one wave's blocks b_first + W*i (i < count) of the sequence whose
@@ -377,6 +388,8 @@ DecodeArgs mfma_args(const void* q, const void* k_cache, const void* v_cache,
   a.out = static_cast<uint16_t*>(out);
   a.ws_ml = ws_ml;
   a.ws_acc = ws_acc;
+  a.k_scale = nullptr;
+  a.v_scale = nullptr;
   a.scale_log2 = scale_log2;
   a.num_seqs = num_seqs;
   a.hq_total = hq;

@@ -20,7 +20,8 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import (BLOCK_SIZE, PARTITION_AUTO, BlockManager, Pool, copy_blocks, new_kv_cache,
-               paged_attention_decode, reshape_and_cache)
+               new_kv_cache_int8, paged_attention_decode, paged_attention_decode_int8,
+               reshape_and_cache, reshape_and_cache_int8)
 
 _TORCH_DTYPE = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
 NAN_FILL = float("nan")
@@ -128,10 +129,12 @@ class DeviceBatch:
     it, as do all never-written slots, so any read past a sequence's end
     shows up in the output.  ``copies`` > 1 keeps that many independent caches
     (same tables) for benchmarks that must not hit in the last-level cache.
+    ``int8`` keeps an INT8 cache with the workload's per-channel scales (its
+    poison block and unwritten slots hold code 127).
     """
 
     def __init__(self, w, device="cuda", copies: int = 1, fill: float | None = NAN_FILL,
-                 prefix_cache: bool = False):
+                 prefix_cache: bool = False, int8: bool = False):
         import torch
 
         self.w = w
@@ -142,8 +145,17 @@ class DeviceBatch:
         self.tables = torch.from_numpy(self.bm.rows.copy()).to(device)
         self.context_lens = torch.from_numpy(np.asarray(w.context_lens, np.int32)).to(device)
         self.max_context_len = int(np.max(w.context_lens))
-        self.caches = [new_kv_cache(self.num_blocks, w.num_kv_heads, w.head_dim,
-                                    self.torch_dtype, device, fill) for _ in range(copies)]
+        self.int8 = int8
+        if int8:  # INT8 cache: the poison and unwritten slots hold code 127
+            sk, sv = w.int8_scales()
+            self.k_scale = torch.from_numpy(sk).to(device)
+            self.v_scale = torch.from_numpy(sv).to(device)
+            self.caches = [new_kv_cache_int8(self.num_blocks, w.num_kv_heads, w.head_dim, device,
+                                             None if fill is None else 127)
+                           for _ in range(copies)]
+        else:
+            self.caches = [new_kv_cache(self.num_blocks, w.num_kv_heads, w.head_dim,
+                                        self.torch_dtype, device, fill) for _ in range(copies)]
         self.q = self._dev(w.q)
         self.out = torch.empty(w.q.shape, dtype=self.torch_dtype, device=device)
         self.dev_phases = [self._dev_phase(ph) for ph in self.phases]
@@ -163,7 +175,11 @@ class DeviceBatch:
         if ph["pairs"].shape[0]:
             copy_blocks(kc, vc, ph["pairs"])
         if ph["slots"].shape[0]:
-            reshape_and_cache(ph["key"], ph["value"], kc, vc, ph["slots"])
+            if self.int8:
+                reshape_and_cache_int8(ph["key"], ph["value"], kc, vc, ph["slots"], self.k_scale,
+                                       self.v_scale)
+            else:
+                reshape_and_cache(ph["key"], ph["value"], kc, vc, ph["slots"])
 
     def prefill(self):
         for cache in self.caches:
@@ -177,6 +193,13 @@ class DeviceBatch:
 
     def decode(self, copy: int = 0, partition_size: int = PARTITION_AUTO, out=None):
         kc, vc = self.caches[copy]
+        if self.int8:
+            paged_attention_decode_int8(self.q, kc, vc, self.k_scale, self.v_scale, self.tables,
+                                        self.context_lens, self.w.scale,
+                                        self.out if out is None else out,
+                                        max_context_len=self.max_context_len,
+                                        partition_size=partition_size)
+            return
         paged_attention_decode(self.q, kc, vc, self.tables, self.context_lens, self.w.scale,
                                self.out if out is None else out,
                                max_context_len=self.max_context_len,

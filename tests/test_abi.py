@@ -76,6 +76,28 @@ def test_host_only_calls_and_argument_errors_without_a_gpu():
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 4, 2, 64, 0, None) == 0
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 1, 4, 2, 64, 0, None) == -1
     assert lib.pa_copy_blocks(None, None, None, 0, 4, 2, 60, 2, None) == -1
+    # INT8 cache calls: argument checks on the host
+    p16 = ctypes.c_void_p(16)
+    assert lib.pa_copy_blocks(None, None, None, 0, 4, 2, 128, 3, None) == 0  # PA_I8
+    assert lib.pa_copy_blocks(None, None, None, 0, 4, 2, 96, 3, None) == -1  # D % 64 != 0
+    assert lib.pa_reshape_and_cache_int8(None, None, None, None, None, None, None, 0, 4, 2, 64,
+                                         2, None) == 0
+    assert lib.pa_reshape_and_cache_int8(None, None, None, None, None, None, None, 0, 4, 2, 96,
+                                         2, None) == -1
+    assert lib.pa_reshape_and_cache_int8(None, None, None, None, None, None, None, 0, 4, 2, 64,
+                                         3, None) == -4  # input values cannot be int8
+    assert lib.pa_reshape_and_cache_int8(p16, p16, p16, p16, p16, None, p16, 1, 4, 2, 64, 2,
+                                         None) == -1  # no K scales
+
+    def dec8(dtype=2, d=128, part=0, scales=p16):
+        return lib.pa_paged_attention_decode_int8(p16, p16, p16, scales, scales, p16, p16, 1.0,
+                                                  p16, 4, 8, 4, d, 64, 1024, part, None, 0,
+                                                  dtype, None)
+    assert dec8(dtype=0) == -4  # fp32 queries
+    assert dec8(d=256) == -4
+    assert dec8(part=pa.PARTITION_BALANCED) == -4
+    assert dec8(scales=None) == -1
+    assert dec8(part=256) == -6  # no workspace
 
 
 def test_workspace_size_closed_form():

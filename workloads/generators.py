@@ -118,6 +118,17 @@ class Workload:
     def elem_bytes(self) -> int:
         return elem_bytes(self.dtype)
 
+    def int8_scales(self):
+        """Per-channel scales (k_scale, v_scale), float32 [Hkv, D], of an INT8
+        cache of this workload: (3.5 + U[0, 1)) / 127, so that codes saturate
+        only beyond 3.5-4.5 standard deviations of the N(0, 1) values.  Drawn
+        from their own stream (seed, 8), leaving every other draw unchanged."""
+        rng = np.random.default_rng([int(self.seed), 8])
+        shape = (self.num_kv_heads, self.head_dim)
+        k = ((3.5 + rng.random(shape)) / 127).astype(np.float32)
+        v = ((3.5 + rng.random(shape)) / 127).astype(np.float32)
+        return k, v
+
     def prompt_tokens(self, p: int) -> np.ndarray:
         """Token ids of shared prompt ``p`` (int32): id = p * 2**16 + position.
         The K/V drawn for a prompt token belong to that id alone, so a prefix
