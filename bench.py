@@ -36,30 +36,42 @@ DECODE_KERNELS = {
     "decode_stream_kernel": ("pa_decode_balanced.hip", "pa_decode_common.h"),
     "decode_items_kernel": ("pa_decode.hip", "pa_decode_common.h"),
     "decode_generic_kernel": ("pa_decode.hip", "pa_decode_common.h"),
+    "decode_items_i8_kernel": ("pa_decode.hip", "pa_decode_int8.h", "pa_decode_common.h"),
 }
 
 
-def decode_bytes(w):
+def traffic_file(kernel):
+    if kernel == "decode_items_kernel":
+        return TRAFFIC_FILE
+    return os.path.join(ROOT, "profiles", f"decode_traffic_{kernel}.json")
+
+
+def decode_bytes(w, int8=False):
     """Algorithmic bytes of one decode call: every cached K and V element of every
-    (sequence, KV head) once, q and out once, table entries in use and lengths."""
+    (sequence, KV head) once, q and out once, table entries in use and lengths
+    (INT8 cache: 1-byte elements plus the two [Hkv, D] fp32 scale arrays)."""
     import numpy as np
     lens = np.asarray(w.context_lens, dtype=np.int64)
     e = w.elem_bytes
-    kv = int(lens.sum()) * 2 * w.num_kv_heads * w.head_dim * e
+    kv = int(lens.sum()) * 2 * w.num_kv_heads * w.head_dim * (1 if int8 else e)
     qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * e
     tables = 4 * int((-(-lens // 16)).sum())
-    return kv + qo + tables + 4 * w.num_seqs
+    scales = 2 * w.num_kv_heads * w.head_dim * 4 if int8 else 0
+    return kv + qo + tables + 4 * w.num_seqs + scales
 
 
-def step_bytes(w, db):
+def step_bytes(w, db, int8=False):
     """decode bytes + the step's token writes (read + write + slots) + block copies."""
     B = db.phases[2]
     e = w.elem_bytes
+    ec = 1 if int8 else e
     t = B.slots.shape[0]
-    writes = 2 * (2 * t * w.num_kv_heads * w.head_dim * e) + 8 * t
-    block = w.num_kv_heads * 16 * w.head_dim * e
+    writes = 2 * t * w.num_kv_heads * w.head_dim * (e + ec) + 8 * t
+    if int8:
+        writes += 2 * w.num_kv_heads * w.head_dim * 4
+    block = w.num_kv_heads * 16 * w.head_dim * ec
     copies = B.pairs.shape[0] * 2 * (2 * block) + 16 * B.pairs.shape[0]
-    return decode_bytes(w) + writes + copies
+    return decode_bytes(w, int8) + writes + copies
 
 
 def source_hash(kernel):
@@ -73,7 +85,7 @@ def source_hash(kernel):
 def load_traffic(workload, kernel):
     """Counter-measured HBM bytes per launch of `kernel`, if taken on its current source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -83,7 +95,7 @@ def load_traffic(workload, kernel):
     return t.get("bytes_per_launch")
 
 
-def pmc_summary(fetch_dir, write_dir, workload, kernel, out_path=TRAFFIC_FILE):
+def pmc_summary(fetch_dir, write_dir, workload, kernel, out_path=None):
     """HBM bytes per decode launch from two rocprofv3 --pmc runs of this bench
     (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch), each scaled by
     what the same counter reads for the run's plain 1 GiB device copy."""
@@ -115,16 +127,19 @@ def pmc_summary(fetch_dir, write_dir, workload, kernel, out_path=TRAFFIC_FILE):
                            "dispatches": len(dec)}
     result["bytes_per_launch"] = (result["FETCH_SIZE"]["bytes_per_launch"]
                                   + result["WRITE_SIZE"]["bytes_per_launch"])
+    out_path = out_path or traffic_file(kernel)
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         json.dump(result, f, indent=1)
     print(json.dumps(result))
 
 
-def cpu_baseline(w, budget_s):
-    """The oracle (fp64 NumPy) on the first sequences of the batch, ~budget_s of work."""
+def cpu_baseline(w, budget_s, int8=False):
+    """The oracle (fp64 NumPy) on the first sequences of the batch, ~budget_s of work
+    (INT8 cache: the oracle's quantization of each sequence's K/V, then attention
+    over code * scale)."""
     import numpy as np
-    from oracle import attention
+    from oracle import attention, quant
     from oracle.numerics import to_f64
     from threadpoolctl import threadpool_limits
     limiter = threadpool_limits(1)  # the oracle is a single-threaded loop; keep BLAS at 1
@@ -132,18 +147,24 @@ def cpu_baseline(w, budget_s):
     q = to_f64(w.q, w.dtype)
     group = w.num_q_heads // w.num_kv_heads
     e = w.elem_bytes
+    ec = 1 if int8 else e
+    sk, sv = w.int8_scales() if int8 else (None, None)
     done_tokens, done_bytes, seqs, passes = 0, 0, 0, 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:  # whole passes over the batch, or a prefix
         for s in range(w.num_seqs):
             kb, vb = w.sequence_kv(s)
-            K, V = to_f64(kb, w.dtype), to_f64(vb, w.dtype)
+            if int8:
+                K = quant.dequantize(quant.quantize(kb, w.dtype, sk), sk)
+                V = quant.dequantize(quant.quantize(vb, w.dtype, sv), sv)
+            else:
+                K, V = to_f64(kb, w.dtype), to_f64(vb, w.dtype)
             for g in range(w.num_kv_heads):
                 for h in range(g * group, (g + 1) * group):
                     attention.attend(q[s, h], K[:, g], V[:, g], w.scale)
             n = int(w.context_lens[s])
             done_tokens += n
-            done_bytes += (n * 2 * w.num_kv_heads * w.head_dim * e
+            done_bytes += (n * 2 * w.num_kv_heads * w.head_dim * ec
                            + 2 * w.num_q_heads * w.head_dim * e)
             seqs += 1
             if time.perf_counter() - t0 > budget_s:
@@ -156,7 +177,8 @@ def cpu_baseline(w, budget_s):
             "tokens_per_s": round(done_tokens / dt, 1),
             "sample": f"{seqs} sequence decodes in {passes} pass(es) over the {w.num_seqs}-sequence "
                       f"batch ({done_tokens} attended tokens), oracle decode (fp64 NumPy "
-                      f"gather + softmax attention), {dt:.1f} s"}
+                      f"gather{' + INT8 quantize/dequantize' if int8 else ''} + softmax "
+                      f"attention), {dt:.1f} s"}
 
 
 def main():
@@ -168,6 +190,9 @@ def main():
     ap.add_argument("--copies", type=int, default=0,
                     help="KV pool copies used round-robin (default: enough for >= 1.5 GB)")
     ap.add_argument("--partition", type=int, default=-1, help="-1 auto, -2 balanced split, 0 none, else tokens")
+    ap.add_argument("--kv", choices=("native", "int8"), default="native",
+                    help="KV cache storage: the workload's dtype, or INT8 codes with "
+                         "per-channel scales")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -177,14 +202,15 @@ def main():
                     help="main decode kernel the --pmc-summary counters belong to")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
-                         "bench, taken with --calibrate-copy 1024, into " + TRAFFIC_FILE)
+                         "bench, taken with --calibrate-copy 1024, into profiles/ "
+                         "(decode_traffic.json for the items kernel, "
+                         "decode_traffic_<kernel>.json otherwise)")
     args = ap.parse_args()
 
     if args.pmc_summary:
         import workloads
-        pmc_summary(*args.pmc_summary, workloads.CONFIG_NAMES[int(args.config)
-                                                               if args.config.isdigit()
-                                                               else args.config],
+        name = workloads.CONFIG_NAMES[int(args.config) if args.config.isdigit() else args.config]
+        pmc_summary(*args.pmc_summary, name + ("-int8kv" if args.kv == "int8" else ""),
                     args.kernel)
         return
 
@@ -208,9 +234,14 @@ def main():
 
     t_setup = time.perf_counter()
     w = workloads.make(args.config)
-    pool_bytes = 2 * (w.num_blocks + 1) * w.num_kv_heads * 16 * w.head_dim * w.elem_bytes
+    int8 = args.kv == "int8"
+    if int8 and (w.dtype == "f32" or w.head_dim not in (64, 128)):
+        print("the INT8 cache serves fp16/bf16 queries at head_dim 64 or 128", file=sys.stderr)
+        sys.exit(2)
+    ec = 1 if int8 else w.elem_bytes
+    pool_bytes = 2 * (w.num_blocks + 1) * w.num_kv_heads * 16 * w.head_dim * ec
     copies = args.copies or max(1, int(np.ceil(1.5e9 / pool_bytes)))
-    db = runner.DeviceBatch(w, copies=copies)
+    db = runner.DeviceBatch(w, copies=copies, int8=int8)
     db.prefill()
     torch.cuda.synchronize()
     print(f"# setup {time.perf_counter() - t_setup:.1f} s: workload {w.name}, "
@@ -238,8 +269,8 @@ def main():
     kt = pa.timing_end()
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    sbytes = step_bytes(w, db)
-    dbytes = decode_bytes(w)
+    sbytes = step_bytes(w, db, int8)
+    dbytes = decode_bytes(w, int8)
     tokens = int(np.sum(w.context_lens))
     dec = kt["decode"]
     dec_ms = dec["ms"] / max(1, dec["launches"])
@@ -247,13 +278,16 @@ def main():
     ps = args.partition if args.partition != -1 else pa.decode_auto_partition(
         w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, db.max_context_len,
         {"f32": 0, "f16": 1, "bf16": 2}[w.dtype])
-    if ps == pa.PARTITION_BALANCED:
+    if int8:
+        main_kernel = "decode_items_i8_kernel"
+    elif ps == pa.PARTITION_BALANCED:
         main_kernel = "decode_stream_kernel"
     elif w.dtype != "f32" and w.head_dim in (64, 128):
         main_kernel = "decode_items_kernel"
     else:
         main_kernel = "decode_generic_kernel"
-    traffic = load_traffic(w.name, main_kernel)
+    workload_name = w.name + ("-int8kv" if int8 else "")
+    traffic = load_traffic(workload_name, main_kernel)
     result = {
         "metric": METRIC,
         "value": round(sbytes / (ms_step * 1e-3) / 1e9, 2),
@@ -265,9 +299,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": f"i8kv+{w.dtype}" if int8 else w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+        "config": {"workload": workload_name, "kv_cache": "int8 per-channel" if int8 else w.dtype,
+                   "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
                    "attended_tokens": tokens, "max_context_len": db.max_context_len,
                    "partition_size": ps, "kv_pool_copies": copies, "parallelism": "none"},
@@ -291,7 +326,7 @@ def main():
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = n
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, int8)
     print(json.dumps(result), flush=True)
 
 

@@ -217,11 +217,11 @@ __global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_i8
   const int count = nblk > wave ? (nblk - wave + W - 1) / W : 0;
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
   const int ids = load_ids<W>(trow, b_first, count);
-  uint4 qh[D / 32], ql[D / 32];
-  const float back = load_q_i8<Tag, D>(a, s, g, h0, nh, qh, ql);
+  uint4 qf[D / 32];
+  const float back = load_q_i8<Tag, D>(a, s, g, h0, nh, qf);
   WaveState<D> st;
   st.reset();
-  attend_blocks_i8<D, W>(a, trow, ids, b_first, count, end, g, qh, ql, a.scale_log2 * back, st);
+  attend_blocks_i8<D, W>(a, trow, ids, b_first, count, end, g, qf, a.scale_log2 * back, st);
   stage_partials<D, W>(comb, a.nh_max, nh, st);
   __syncthreads();
 

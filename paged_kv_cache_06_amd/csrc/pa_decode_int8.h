@@ -27,8 +27,9 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 // then 1152 is subtracted from both halves at once.
 __device__ __forceinline__ uint2 codes_to_f16(uint32_t w) {
   const uint32_t u = w ^ 0x80808080u;
-  const uint32_t lo = (u & 0xFFu) | ((u & 0xFF00u) << 8) | 0x64006400u;
-  const uint32_t hi = ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u) | 0x64006400u;
+  // byte permutes of {0x64646464 : u}: selector bytes 0-3 pick u, 4 picks 0x64
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // u0, 64, u1, 64
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // u2, 64, u3, 64
   const f16x2_t bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
   const f16x2_t a = __builtin_bit_cast(f16x2_t, lo) - bias;
   const f16x2_t b = __builtin_bit_cast(f16x2_t, hi) - bias;
@@ -44,14 +45,17 @@ struct I8Regs {
   uint4 v[D / 64];
 };
 
+// `valid` false: the loads are issued with an empty range, read nothing and
+// give zeros (so that a wave's load sequence does not depend on its count).
 template <int D>
 __device__ __forceinline__ void load_block_i8(const DecodeArgs& a, int g, int phys,
-                                              I8Regs<D>& r) {
+                                              I8Regs<D>& r, bool valid = true) {
   const uint32_t lane = threadIdx.x & (kWave - 1);
   constexpr uint32_t kBytes = D * kBlock;  // one KV head of one block
   const size_t off = (static_cast<size_t>(phys) * a.hkv + g) * kBytes;
-  const auto rk = buffer_of(reinterpret_cast<const char*>(a.k_cache) + off, kBytes);
-  const auto rv = buffer_of(reinterpret_cast<const char*>(a.v_cache) + off, kBytes);
+  const uint32_t range = valid ? kBytes : 0u;
+  const auto rk = buffer_of(reinterpret_cast<const char*>(a.k_cache) + off, range);
+  const auto rv = buffer_of(reinterpret_cast<const char*>(a.v_cache) + off, range);
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) r.k[i] = buffer_load16(rk, lane * 16 + i * 1024);
 #pragma unroll
@@ -83,7 +87,7 @@ __device__ __forceinline__ void convert_block_i8(const I8Regs<D>& r, uint4* kf, 
 // pre-scaling back out of this lane's scores.  Rows past nh read 0.
 template <typename Tag, int D>
 __device__ __forceinline__ float load_q_i8(const DecodeArgs& a, int s, int g, int h0, int nh,
-                                           uint4* qh, uint4* ql) {
+                                           uint4* qh) {
   const uint32_t lane = threadIdx.x & (kWave - 1);
   const uint32_t n = lane & 15, kg = lane >> 4;
   const auto rq = buffer_of(a.q + (static_cast<size_t>(s) * a.hq_total + g * a.group + h0) * D,
@@ -113,18 +117,14 @@ __device__ __forceinline__ float load_q_i8(const DecodeArgs& a, int s, int g, in
   const float up = ldexpf(1.f, 15 - ex);
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) {
-    uint32_t hw[4], lw[4];
+    uint32_t hw[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float v0 = x[m][e] * up, v1 = x[m][e + 1] * up;
-      const _Float16 h0v = static_cast<_Float16>(v0), h1v = static_cast<_Float16>(v1);
-      const _Float16 l0v = static_cast<_Float16>(v0 - static_cast<float>(h0v));
-      const _Float16 l1v = static_cast<_Float16>(v1 - static_cast<float>(h1v));
-      hw[e / 2] = __builtin_bit_cast(uint32_t, f16x2_t{h0v, h1v});
-      lw[e / 2] = __builtin_bit_cast(uint32_t, f16x2_t{l0v, l1v});
+      const f16x2_t v = {static_cast<_Float16>(x[m][e] * up),
+                         static_cast<_Float16>(x[m][e + 1] * up)};
+      hw[e / 2] = __builtin_bit_cast(uint32_t, v);
     }
     qh[m] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    ql[m] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
   return ldexpf(1.f, ex - 15);
 }
@@ -134,21 +134,36 @@ __device__ __forceinline__ float load_q_i8(const DecodeArgs& a, int s, int g, in
 template <int D, int W>
 __device__ __forceinline__ void attend_blocks_i8(const DecodeArgs& a, const int32_t* trow,
                                                  int ids, int b_first, int count, int len, int g,
-                                                 const uint4* qh, const uint4* ql, float sl2,
+                                                 const uint4* qh, float sl2,
                                                  WaveState<D>& st) {
-  for (int j = 0; j < count; ++j) {
-    if (j > 0 && (j & 63) == 0) ids = load_ids<W>(trow, b_first + W * j, count - j);
-    I8Regs<D> r;
-    load_block_i8<D>(a, g, __builtin_amdgcn_readlane(ids, j & 63), r);
+  auto attend = [&](const I8Regs<D>& r, int blk) {
     uint4 kf[D / 32];
     uint2 vf[D / 16];
     convert_block_i8<D>(r, kf, vf);
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) sc = Mfma<F16T>::qk(kf[m], qh[m], sc);
-#pragma unroll
-    for (int m = 0; m < D / 32; ++m) sc = Mfma<F16T>::qk(kf[m], ql[m], sc);
-    block_update<F16T, D>(vf, sc, sl2, b_first + W * j, len, st);
+    block_update<F16T, D>(vf, sc, sl2, blk, len, st);
+  };
+  // Software pipeline over two register sets: the next block's loads are in
+  // flight while the current one is converted and multiplied (an INT8 block is
+  // half the bytes of a 16-bit one for the same compute).  Every iteration
+  // issues the same loads, empty-ranged past the end, so the waits stay exact.
+  for (int c0 = 0; c0 < count; c0 += 64) {
+    if (c0 > 0) ids = load_ids<W>(trow, b_first + W * c0, count - c0);
+    const int n = min(64, count - c0);
+    const int blk0 = b_first + W * c0;
+    I8Regs<D> ra, rb;
+    load_block_i8<D>(a, g, __builtin_amdgcn_readlane(ids, 0), ra);
+    for (int j = 0; j < n; j += 2) {
+      load_block_i8<D>(a, g, __builtin_amdgcn_readlane(ids, (j + 1) & 63), rb, j + 1 < n);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
+      attend(ra, blk0 + W * j);
+      if (j + 1 >= n) break;
+      load_block_i8<D>(a, g, __builtin_amdgcn_readlane(ids, (j + 2) & 63), ra, j + 2 < n);
+      __builtin_amdgcn_sched_barrier(0);
+      attend(rb, blk0 + W * (j + 1));
+    }
   }
 }
 
