@@ -277,7 +277,7 @@ def main():
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
     ps = args.partition if args.partition != -1 else pa.decode_auto_partition(
         w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, db.max_context_len,
-        {"f32": 0, "f16": 1, "bf16": 2}[w.dtype])
+        3 if int8 else {"f32": 0, "f16": 1, "bf16": 2}[w.dtype])
     if int8:
         main_kernel = "decode_items_i8_kernel"
     elif ps == pa.PARTITION_BALANCED:

@@ -234,7 +234,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t max_context_len, int32_t partition_size);
 
 /* The partition size PA_PARTITION_AUTO resolves to for these sizes
- * (PA_PARTITION_NONE or a positive multiple of 16). */
+ * (PA_PARTITION_NONE or a positive multiple of 16); dtype PA_I8 gives the
+ * choice of pa_paged_attention_decode_int8. */
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
 

@@ -436,20 +436,28 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(
 // when that still gives ~1024 items (one per resident work-group): their items
 // are then mostly full partitions of one size, and fewer of them means less to
 // merge (on MI355X: 32K-position batch of 8, 190 us against 194 us at 1024).
-int auto_partition(int num_seqs, int hkv, int max_len) {
-  if (max_len <= 1024) return PA_PARTITION_NONE;
-  if (max_len >= 16384 && static_cast<int64_t>(num_seqs) * ((max_len + 2047) / 2048) * hkv >= 1024)
-    return 2048;
-  int ps = 1024;
+// An INT8 cache moves half the bytes per position, so every size above doubles
+// and every item count halves (measured on MI355X: the mixed 70B-layer batch
+// decodes in 62.7 us at 2048 against 63.6 us at 1024, the 32K batch in 99 us
+// at 4096 against 103 us at 2048).
+int auto_partition(int num_seqs, int hkv, int max_len, int kv_bytes = 2) {
+  const int k = kv_bytes == 1 ? 2 : 1;
+  if (max_len <= 1024 * k) return PA_PARTITION_NONE;
+  const int long_part = 2048 * k;
+  if (max_len >= 16384 &&
+      static_cast<int64_t>(num_seqs) * ((max_len + long_part - 1) / long_part) * hkv >= 1024 / k)
+    return long_part;
+  int ps = 1024 * k;
   while (ps > 256 &&
-         static_cast<int64_t>(num_seqs) * ((max_len + ps - 1) / ps) * hkv < 2048)
+         static_cast<int64_t>(num_seqs) * ((max_len + ps - 1) / ps) * hkv < 2048 / k)
     ps /= 2;
   return ps;
 }
 
-bool resolve_split(int partition_size, int num_seqs, int hkv, int max_len, Split* out) {
+bool resolve_split(int partition_size, int num_seqs, int hkv, int max_len, Split* out,
+                   int kv_bytes = 2) {
   int ps = partition_size;
-  if (ps == PA_PARTITION_AUTO) ps = auto_partition(num_seqs, hkv, max_len);
+  if (ps == PA_PARTITION_AUTO) ps = auto_partition(num_seqs, hkv, max_len, kv_bytes);
   if (ps < 0 || ps % kBlock != 0) return false;
   if (ps == PA_PARTITION_NONE) ps = max(kBlock, (max_len + kBlock - 1) / kBlock * kBlock);
   out->part = ps;
@@ -573,7 +581,7 @@ pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, con
   if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !context_lens || !out)
     return PA_ERR_INVALID_ARG;
   Split sp;
-  if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp))
+  if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp, 1))
     return PA_ERR_INVALID_ARG;
   const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
@@ -594,8 +602,8 @@ int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype) {
   (void)num_q_heads;
   (void)head_dim;
-  (void)dtype;
-  return pa::auto_partition(num_seqs, num_kv_heads, max_context_len);
+  return pa::auto_partition(num_seqs, num_kv_heads, max_context_len,
+                            dtype == PA_I8 ? 1 : pa::elem_bytes(dtype));
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
