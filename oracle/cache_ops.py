@@ -32,3 +32,11 @@ def copy_blocks(k_cache, v_cache, pairs) -> None:
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():
         k_cache[dst] = k_cache[src]
         v_cache[dst] = v_cache[src]
+
+
+def transfer_blocks(src_k, src_v, dst_k, dst_v, pairs) -> None:
+    """For each (s, d): block d of the destination caches becomes block s of
+    the source caches (the data side of moving blocks between tiers)."""
+    for s, d in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():
+        dst_k[d] = src_k[s]
+        dst_v[d] = src_v[s]

@@ -44,6 +44,18 @@ consume room in the pool (same page, trade-offs section).  Readings:
   eviction list; allocation takes an uncached free block first (LIFO as
   above) and only then evicts the least recently released cached block.
 
+Host tier (swapping): when the device pool runs short, individual blocks can
+move to a pool in host memory instead of whole sequences ("KV Cache and
+PagedAttention: why your LLM server slows down", the contrast between
+all-or-nothing eviction of a whole sequence to the CPU and fine-grained
+eviction of small pages).  Readings: the host tier is a second BlockPool of
+the same block shape; ``swap_blocks`` moves a list of blocks from one pool to
+the other -- each gets a fresh block in the destination (taken in list order,
+before anything is released), the (source, destination) pairs are what the
+device must copy, and the source block loses the one reference that moved
+(a block still shared by others stays where it is for them).  All or
+nothing.
+
 Pins (tests/test_oracle_pool.py): the pages' worked examples (token 17 -> second
 block; 300 of a 4096 reservation idle), block count = ceil(len/16) with waste
 below 16 slots per sequence, reference-count conservation against the tables
@@ -52,7 +64,11 @@ shared-prefix workload's closed-form copy count and block count.  Prefix
 caching (tests/test_oracle_prefix.py): matched blocks = floor(common prefix /
 16) by brute force over random token lists, cached blocks outliving their
 sequences, eviction order, no false hit through a reused block id, and the
-shared-prompt block count in closed form.
+shared-prompt block count in closed form.  Swapping (tests/test_oracle_swap.py):
+references conserved across both tiers, a swap out and back in restores every
+sequence's K/V bits and decode output exactly, shared blocks stay for the other
+sharers, all-or-nothing failure, and the page's fine-grained versus
+whole-sequence eviction counts.
 """
 from __future__ import annotations
 
@@ -255,3 +271,16 @@ class BlockPool:
         return {"num_blocks": self.num_blocks, "free": self.num_free(), "used": used,
                 "shared": shared, "copies": self.copies_made, "cached": len(self.key_of),
                 "evictable": len(self.lru), "prefix_hits": self.prefix_hits}
+
+
+def swap_blocks(src: BlockPool, dst: BlockPool, blocks) -> list:
+    """Move ``blocks`` (ids held in ``src``) to ``dst``: returns the
+    (src_block, dst_block) pairs to copy, in list order; the caller's table
+    entries become the dst blocks.  All or nothing."""
+    blocks = [src._check(b) for b in blocks]
+    if dst.num_free() < len(blocks):
+        raise OutOfBlocks("destination pool cannot take these blocks")
+    pairs = [(b, dst.alloc()) for b in blocks]
+    for b in blocks:
+        src.free(b)
+    return pairs

@@ -155,3 +155,29 @@ def test_planted_quantization_mistake_is_caught(monkeypatch, bad, pin):
     monkeypatch.setattr(quant, "quantize", bad)
     with pytest.raises(AssertionError):
         pin()
+
+
+from oracle import cache_ops  # noqa: E402
+from tests import test_oracle_swap as tsw  # noqa: E402
+
+
+def test_planted_swap_without_release_is_caught(monkeypatch):
+    def leaky(src, dst, blocks):
+        blocks = [src._check(b) for b in blocks]
+        if dst.num_free() < len(blocks):
+            raise pool.OutOfBlocks("short")
+        return [(b, dst.alloc()) for b in blocks]  # forgets to release the source
+    monkeypatch.setattr(pool, "swap_blocks", leaky)
+    monkeypatch.setattr(tsw, "swap_blocks", leaky)
+    with pytest.raises(AssertionError):
+        tsw.test_random_swaps_conserve_references_in_both_tiers()
+
+
+def test_planted_backwards_transfer_is_caught(monkeypatch):
+    def backwards(src_k, src_v, dst_k, dst_v, pairs):
+        for s, d in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():
+            dst_k[s] = src_k[d]
+            dst_v[s] = src_v[d]
+    monkeypatch.setattr(cache_ops, "transfer_blocks", backwards)
+    with pytest.raises((AssertionError, IndexError)):
+        tsw.test_swap_out_and_back_in_restores_every_sequence_exactly()
