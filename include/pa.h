@@ -174,6 +174,22 @@ pa_status pa_prefix_match(pa_pool* pool, const int32_t* tokens, int32_t num_toke
 pa_status pa_prefix_register(pa_pool* pool, const int32_t* table_row, int32_t nblocks,
                              const int32_t* tokens, int32_t num_tokens, int32_t* num_added);
 
+/* Host tier ("KV Cache and PagedAttention: why your LLM server slows down":
+ * when memory fills, small pages move to the CPU instead of whole
+ * sequences).  A second pool whose ids index a cache in pinned host memory
+ * of the same shape is the host tier.  pa_swap_blocks moves blocks[0..n)
+ * (ids held in `src`) to `dst`: each gets a fresh dst block, taken in list
+ * order before anything is released, pairs_out (host, [n][2]) receives
+ * (src block, dst block) -- the copies pa_transfer_blocks must make, and the
+ * caller's new table entries -- and each listed src block loses one
+ * reference (a block still shared stays for its other holders).  A block may
+ * be listed as often as it has references.  All-or-nothing:
+ * PA_ERR_BAD_BLOCK if a block is not held (often enough),
+ * PA_ERR_OUT_OF_BLOCKS if dst has fewer than n free blocks,
+ * PA_ERR_INVALID_ARG on NULL pointers, n < 0 or src == dst. */
+pa_status pa_swap_blocks(pa_pool* src, pa_pool* dst, const int32_t* blocks, int32_t n,
+                         int64_t* pairs_out);
+
 /* Reference count of a block (-1 if the id is out of range). */
 int32_t pa_refcount(const pa_pool* pool, int32_t block);
 /* Blocks an allocation can take: uncached free ones plus evictable cached ones. */
@@ -217,6 +233,18 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
                          int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
                          int32_t head_dim, pa_dtype dtype, void* stream);
+
+/* Copy whole blocks between two caches of the same shape and dtype (PA_I8
+ * for INT8 caches): for each pair, block dst of dst_k/dst_v becomes block src
+ * of src_k/src_v.  Each cache pointer, and block_pairs (int64 [num_pairs][2]),
+ * may be device memory or pinned host memory (hipHostMalloc; torch
+ * pin_memory), reached through its device mapping; PA_ERR_INVALID_ARG for
+ * memory the device cannot reach.  Pairs with an id out of range are
+ * skipped.  The dsts must be distinct. */
+pa_status pa_transfer_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks,
+                             void* dst_k, void* dst_v, int32_t dst_num_blocks,
+                             const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                             int32_t head_dim, pa_dtype dtype, void* stream);
 
 /* Workspace bytes pa_paged_attention_decode needs for these sizes.
  * Fixed partitions (NONE or a positive size): the work list of the call (16
@@ -339,7 +367,8 @@ pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, con
 #define PA_KERNEL_RESHAPE_AND_CACHE 2
 #define PA_KERNEL_COPY_BLOCKS 3
 #define PA_KERNEL_DECODE_PLAN 4     /* work list of pa_paged_attention_decode */
-#define PA_NUM_KERNEL_KINDS 5
+#define PA_KERNEL_TRANSFER_BLOCKS 5 /* pa_transfer_blocks */
+#define PA_NUM_KERNEL_KINDS 6
 
 pa_status pa_timing_begin(int32_t capacity);
 pa_status pa_timing_end(double* ms_out /* [PA_NUM_KERNEL_KINDS] */,

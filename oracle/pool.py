@@ -277,7 +277,10 @@ def swap_blocks(src: BlockPool, dst: BlockPool, blocks) -> list:
     """Move ``blocks`` (ids held in ``src``) to ``dst``: returns the
     (src_block, dst_block) pairs to copy, in list order; the caller's table
     entries become the dst blocks.  All or nothing."""
-    blocks = [src._check(b) for b in blocks]
+    blocks = [int(b) for b in blocks]
+    for b in set(blocks):  # one held reference per listing
+        if not 0 <= b < src.num_blocks or src.refcount[b] < blocks.count(b):
+            raise BadBlock(f"block {b} is not held often enough")
     if dst.num_free() < len(blocks):
         raise OutOfBlocks("destination pool cannot take these blocks")
     pairs = [(b, dst.alloc()) for b in blocks]

@@ -10,7 +10,8 @@ The names follow the C ABI of ``include/pa.h`` without its ``pa_`` prefix:
 cache forms ``reshape_and_cache_int8`` and ``paged_attention_decode_int8``, the pool
 calls on :class:`Pool` (``alloc``, ``free``, ``incref``, ``fork``,
 ``free_table``, ``append_slots``, ``prefix_match``, ``prefix_register``,
-``refcount``, ``num_free``, ``stats``) and ``blocks_for_bytes``.
+``refcount``, ``num_free``, ``stats``), ``swap_blocks`` and
+``transfer_blocks`` (the host tier) and ``blocks_for_bytes``.
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ __all__ = [
     "Pool", "BlockManager", "blocks_for_bytes", "reshape_and_cache", "copy_blocks",
     "paged_attention_decode", "decode_workspace_bytes", "decode_auto_partition",
     "decode_set_max_groups", "reshape_and_cache_int8", "paged_attention_decode_int8",
+    "swap_blocks", "transfer_blocks", "new_host_kv_cache",
     "new_kv_cache", "new_kv_cache_int8", "logical_view", "timing_begin", "timing_end", "status_string",
 ]
 
@@ -31,7 +33,8 @@ BLOCK_SIZE = 16
 PARTITION_NONE = 0
 PARTITION_AUTO = -1
 PARTITION_BALANCED = -2
-KERNEL_KINDS = ("decode", "decode_reduce", "reshape_and_cache", "copy_blocks", "decode_plan")
+KERNEL_KINDS = ("decode", "decode_reduce", "reshape_and_cache", "copy_blocks", "decode_plan",
+                "transfer_blocks")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -64,6 +67,9 @@ _SIGNATURES = {
     "pa_num_free": (_c_i32, [_c_p]),
     "pa_pool_stats": (_c_i32, [_c_p, ctypes.POINTER(_Stats)]),
     "pa_prefix_match": (_c_i32, [_c_p, _P_I32, _c_i32, _P_I32, _c_i32, _P_I32]),
+    "pa_swap_blocks": (_c_i32, [_c_p, _c_p, _P_I32, _c_i32, _P_I64]),
+    "pa_transfer_blocks": (_c_i32, [_c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32,
+                                    _c_i32, _c_i32, _c_p]),
     "pa_prefix_register": (_c_i32, [_c_p, _P_I32, _c_i32, _P_I32, _c_i32, _P_I32]),
     "pa_blocks_for_bytes": (_c_i64, [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_reshape_and_cache": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
@@ -223,6 +229,17 @@ class Pool:
         _check(load().pa_prefix_register(self._h, _i32p(t), t.size, _i32p(k), k.size,
                                          ctypes.byref(n)), "pa_prefix_register")
         return n.value
+
+
+def swap_blocks(src: Pool, dst: Pool, blocks) -> np.ndarray:
+    """Move ``blocks`` (held in ``src``) to ``dst`` (e.g. the device pool and a
+    host pool): returns int64 [n, 2] (src block, dst block) pairs, the copies
+    for :func:`transfer_blocks` and the new table entries."""
+    b = np.ascontiguousarray(blocks, dtype=np.int32)
+    pairs = np.empty((max(b.size, 1), 2), dtype=np.int64)
+    _check(load().pa_swap_blocks(src._h, dst._h, _i32p(b), b.size,
+                                 pairs.ctypes.data_as(_P_I64)), "pa_swap_blocks")
+    return pairs[:b.size]
 
 
 class BlockManager:
@@ -432,6 +449,42 @@ def reshape_and_cache_int8(key, value, k_cache, v_cache, slot_mapping, k_scale, 
         _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping.contiguous()),
         _scales(k_scale, hkv, d, "k_scale"), _scales(v_scale, hkv, d, "v_scale"), t, nb, hkv, d,
         _dtype_code(key), _stream(key)), "pa_reshape_and_cache_int8")
+
+
+def new_host_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype):
+    """(k_cache, v_cache) in pinned host memory, laid out like the device caches
+    (int8 dtype: the INT8 layout), for blocks moved out of the device pool."""
+    torch = _torch()
+    if dtype == torch.int8:
+        shape = (num_blocks, num_kv_heads, head_dim // 64, 1024)
+        return (torch.empty(shape, dtype=dtype, pin_memory=True),
+                torch.empty(shape, dtype=dtype, pin_memory=True))
+    x = 16 // torch.tensor([], dtype=dtype).element_size()
+    kshape = (num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x)
+    vshape = (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE)
+    return (torch.empty(kshape, dtype=dtype, pin_memory=True),
+            torch.empty(vshape, dtype=dtype, pin_memory=True))
+
+
+def transfer_blocks(src_k, src_v, dst_k, dst_v, block_pairs) -> None:
+    """Copy blocks between two caches of one shape (device or pinned host):
+    block_pairs int64 [n, 2] of (src, dst), on the device or pinned."""
+    torch = _torch()
+    nbs, hkv, d = _cache_dims(src_k, src_v)
+    nbd, hkv2, d2 = _cache_dims(dst_k, dst_v)
+    _need((hkv, d) == (hkv2, d2) and src_k.dtype == dst_k.dtype, "caches differ in shape")
+    for t in (src_k, src_v, dst_k, dst_v):
+        _need(t.is_cuda or t.is_pinned(), "host caches must be pinned")
+    _need(block_pairs.dtype == torch.int64 and block_pairs.dim() == 2 and
+          block_pairs.shape[1] == 2 and block_pairs.is_contiguous() and
+          (block_pairs.is_cuda or block_pairs.is_pinned()),
+          "block_pairs must be contiguous int64 [n, 2], on the device or pinned")
+    dev = next(t for t in (src_k, dst_k, block_pairs) if t.is_cuda) \
+        if any(t.is_cuda for t in (src_k, dst_k, block_pairs)) else None
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    _check(load().pa_transfer_blocks(_ptr(src_k), _ptr(src_v), nbs, _ptr(dst_k), _ptr(dst_v), nbd,
+                                     _ptr(block_pairs), block_pairs.shape[0], hkv, d,
+                                     _dtype_code(src_k), stream), "pa_transfer_blocks")
 
 
 def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,

@@ -123,6 +123,52 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
   }
 }
 
+// Blocks between two caches of the same shape, e.g. device memory and pinned
+// host memory (moving blocks between tiers, "KV Cache and PagedAttention: why
+// your LLM server slows down": fine-grained eviction of small pages to the CPU).
+// grid.x = pair * 2 + (0: K, 1: V); grid.y splits the block's bytes.  Every
+// thread keeps 4 loads of 16 bytes in flight, which the host link's latency
+// needs.
+__global__ __launch_bounds__(256) void transfer_blocks_kernel(
+    const uint4* __restrict__ src_k, const uint4* __restrict__ src_v, uint4* __restrict__ dst_k,
+    uint4* __restrict__ dst_v, const int64_t* __restrict__ pairs, int32_t src_blocks,
+    int32_t dst_blocks, int64_t vec_per_block) {
+  const int pair = blockIdx.x >> 1;
+  const uint4* sc = (blockIdx.x & 1) ? src_v : src_k;
+  uint4* dc = (blockIdx.x & 1) ? dst_v : dst_k;
+  const int64_t src = pairs[2 * pair];
+  const int64_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4* s = sc + src * vec_per_block;
+  uint4* d = dc + dst * vec_per_block;
+  constexpr int kPerThread = 4;
+  const int64_t base = static_cast<int64_t>(blockIdx.y) * 256 * kPerThread + threadIdx.x;
+  uint4 tmp[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int64_t j = base + i * 256;
+    if (j < vec_per_block) tmp[i] = s[j];
+  }
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int64_t j = base + i * 256;
+    if (j < vec_per_block) d[j] = tmp[i];
+  }
+}
+
+// The address the device uses for `p`: device memory as it is, pinned host
+// memory through its device mapping; nullptr for memory the device cannot
+// reach (pageable host memory).
+void* device_address(const void* p) {
+  hipPointerAttribute_t attr;
+  if (!p || hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error the query leaves on pageable memory
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeHost) return nullptr;
+  return attr.devicePointer;
+}
+
 bool cache_shape_ok(int32_t num_blocks, int32_t hkv, int32_t head_dim, pa_dtype dt) {
   if (dt == PA_I8) return num_blocks > 0 && hkv > 0 && head_dim > 0 && head_dim % 64 == 0 &&
                           head_dim <= 512;
@@ -223,6 +269,36 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
   const int slot = timing_start(PA_KERNEL_COPY_BLOCKS, st);
   copy_blocks_kernel<<<dim3(2 * num_pairs, static_cast<uint32_t>(gy)), dim3(256), 0, st>>>(
       static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), block_pairs, num_blocks, vec);
+  const pa_status s = launch_status();
+  timing_stop(slot, st);
+  return s;
+}
+
+pa_status pa_transfer_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks,
+                             void* dst_k, void* dst_v, int32_t dst_num_blocks,
+                             const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                             int32_t head_dim, pa_dtype dtype, void* stream) {
+  using namespace pa;
+  if (num_pairs < 0 || !cache_shape_ok(src_num_blocks, num_kv_heads, head_dim, dtype) ||
+      dst_num_blocks <= 0)
+    return valid_dtype(dtype) || dtype == PA_I8 ? PA_ERR_INVALID_ARG : PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > (0x7fffffff >> 1)) return PA_ERR_INVALID_ARG;
+  const void* sk = device_address(src_k);
+  const void* sv = device_address(src_v);
+  void* dk = device_address(dst_k);
+  void* dv = device_address(dst_v);
+  const void* pr = device_address(block_pairs);
+  if (!sk || !sv || !dk || !dv || !pr) return PA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t bytes = static_cast<int64_t>(num_kv_heads) * kBlock * head_dim * elem_bytes(dtype);
+  const int64_t vec = bytes / 16;
+  const int64_t gy = (vec + 1023) / 1024;
+  const int slot = timing_start(PA_KERNEL_TRANSFER_BLOCKS, st);
+  transfer_blocks_kernel<<<dim3(2 * num_pairs, static_cast<uint32_t>(gy)), dim3(256), 0, st>>>(
+      static_cast<const uint4*>(sk), static_cast<const uint4*>(sv), static_cast<uint4*>(dk),
+      static_cast<uint4*>(dv), static_cast<const int64_t*>(pr), src_num_blocks, dst_num_blocks,
+      vec);
   const pa_status s = launch_status();
   timing_stop(slot, st);
   return s;

@@ -281,6 +281,25 @@ pa_status pa_append_slots(pa_pool* p, int32_t* row, int32_t* nblocks, int32_t ma
   return PA_OK;
 }
 
+pa_status pa_swap_blocks(pa_pool* src, pa_pool* dst, const int32_t* blocks, int32_t n,
+                         int64_t* pairs_out) {
+  if (!src || !dst || src == dst || n < 0 || (n > 0 && (!blocks || !pairs_out)))
+    return PA_ERR_INVALID_ARG;
+  // every listed block must be held, one reference per listing: take the
+  // references off tentatively, then put them back
+  int32_t ok = 0;
+  while (ok < n && held(src, blocks[ok])) --src->refcount[blocks[ok++]];
+  for (int32_t i = 0; i < ok; ++i) ++src->refcount[blocks[i]];
+  if (ok < n) return PA_ERR_BAD_BLOCK;
+  if (available(dst) < n) return PA_ERR_OUT_OF_BLOCKS;
+  for (int32_t i = 0; i < n; ++i) {
+    pairs_out[2 * i] = blocks[i];
+    pairs_out[2 * i + 1] = pop(dst);
+  }
+  for (int32_t i = 0; i < n; ++i) drop(src, blocks[i]);
+  return PA_OK;
+}
+
 int32_t pa_refcount(const pa_pool* p, int32_t b) {
   if (!p || b < 0 || b >= p->num_blocks) return -1;
   return p->refcount[b];

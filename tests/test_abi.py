@@ -76,6 +76,13 @@ def test_host_only_calls_and_argument_errors_without_a_gpu():
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 4, 2, 64, 0, None) == 0
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 1, 4, 2, 64, 0, None) == -1
     assert lib.pa_copy_blocks(None, None, None, 0, 4, 2, 60, 2, None) == -1
+    # host tier: argument checks (no device call)
+    pool = pa.Pool(4)
+    assert lib.pa_swap_blocks(None, None, None, 0, None) == -1
+    assert lib.pa_swap_blocks(pool._h, pool._h, None, 0, None) == -1  # same pool twice
+    assert lib.pa_transfer_blocks(None, None, 4, None, None, 4, None, 0, 2, 64, 2, None) == 0
+    assert lib.pa_transfer_blocks(None, None, 4, None, None, 4, None, 1, 2, 64, 7, None) == -4
+    assert lib.pa_transfer_blocks(None, None, 4, None, None, 0, None, 1, 2, 64, 2, None) == -1
     # INT8 cache calls: argument checks on the host
     p16 = ctypes.c_void_p(16)
     assert lib.pa_copy_blocks(None, None, None, 0, 4, 2, 128, 3, None) == 0  # PA_I8

@@ -207,3 +207,59 @@ def test_prefix_cache_operation_sequences_match_the_oracle():
             for k in ("free", "used", "shared", "copies", "cached", "evictable", "prefix_hits"):
                 assert st[k] == so[k], k
         assert ref.prefix_hits > 0
+
+
+def test_swap_blocks_between_two_pools_matches_the_oracle():
+    """Random appends, forks, frees and whole-table swaps between a device pool
+    and a host pool, plus requests that must fail (repeated, unheld ids):
+    pairs, counts, free lists and errors agree after every operation."""
+    for seed in range(3):
+        rnd = random.Random(300 + seed)
+        ng, nc = rnd.choice([(24, 16), (64, 64)])
+        og = np.random.default_rng(seed).permutation(ng).astype(np.int32)
+        oc = np.random.default_rng(seed + 50).permutation(nc).astype(np.int32)
+        rg, rc = opool.BlockPool(ng, og), opool.BlockPool(nc, oc)
+        lg, lc = pa.Pool(ng, og), pa.Pool(nc, oc)
+        seqs = []  # [tier, table]
+        for _ in range(1200):
+            op = rnd.random()
+            if op < 0.3:
+                t = []
+                n = rnd.randint(1, 60)
+                row = np.zeros(8, np.int32)
+                out_ref, e_ref = _err(lambda: rg.append(t, 0, n, max_blocks=8))
+                out_lib, e_lib = _err(lambda: lg.append_slots(row, 0, 0, n))
+                assert e_ref == e_lib
+                if e_ref is None:
+                    assert row[:out_lib[1]].tolist() == t
+                    seqs.append(["g", t])
+            elif op < 0.4 and seqs:
+                tier, t = rnd.choice(seqs)
+                ref, lib = (rg, lg) if tier == "g" else (rc, lc)
+                seqs.append([tier, ref.fork(t)])
+                lib.fork(t)
+            elif op < 0.8 and seqs:
+                sq = rnd.choice(seqs)
+                tier, t = sq
+                (rs, rd, ls, ld) = (rg, rc, lg, lc) if tier == "g" else (rc, rg, lc, lg)
+                blocks = list(t)
+                bad = rnd.random() < 0.15
+                if bad:  # a block listed more often than it is held, or not held at all
+                    once = [b for b in t if rs.refcount[b] == 1]
+                    free = [b for b in range(rs.num_blocks) if rs.refcount[b] == 0]
+                    blocks.append(rnd.choice(once + free + [rs.num_blocks + 1]))
+                out_ref, e_ref = _err(lambda: opool.swap_blocks(rs, rd, blocks))
+                out_lib, e_lib = _err(lambda: pa.swap_blocks(ls, ld, blocks))
+                assert e_ref == e_lib, (e_ref, e_lib)
+                assert (e_ref == "BadBlock") == bad
+                if e_ref is None:
+                    assert out_lib.tolist() == [list(p) for p in out_ref]
+                    sq[0] = "c" if tier == "g" else "g"
+                    sq[1] = [d for _, d in out_ref]
+            elif seqs:
+                tier, t = seqs.pop(rnd.randrange(len(seqs)))
+                (lg if tier == "g" else lc).free_table(t)
+                (rg if tier == "g" else rc).free_table(t)  # empties t: the library goes first
+            assert [lg.refcount(b) for b in range(ng)] == rg.refcount
+            assert [lc.refcount(b) for b in range(nc)] == rc.refcount
+            assert lg.num_free() == rg.num_free() and lc.num_free() == rc.num_free()
