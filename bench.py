@@ -181,6 +181,76 @@ def cpu_baseline(w, budget_s, int8=False):
                       f"attention), {dt:.1f} s"}
 
 
+HOST_LINK_PEAK_GBS = 63.0  # PCIe 5.0 x16 per direction: 32 GT/s x 16 lanes x 128/130
+
+
+def swap_bench(args):
+    """Move every block of the batch to a pinned host pool and back, K times:
+    pool bookkeeping (pa_swap_blocks) on the host, one pa_transfer_blocks per
+    direction on the device.  Prints one JSON line."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_06_amd as pa
+    import workloads
+    from paged_kv_cache_06_amd import runner
+    w = workloads.make(args.config)
+    int8 = args.kv == "int8"
+    db = runner.DeviceBatch(w, int8=int8)
+    db.prefill()
+    torch.cuda.synchronize()
+    kd, vd = db.caches[0]
+    host = pa.Pool(w.num_blocks)
+    kh, vh = pa.new_host_kv_cache(w.num_blocks, w.num_kv_heads, w.head_dim, kd.dtype)
+    nb = [int(n) for n in db.bm.nblocks]
+    ec = 1 if int8 else w.elem_bytes
+    block_bytes = 2 * w.num_kv_heads * 16 * w.head_dim * ec
+    t_out = t_in = t_host = 0.0
+    moved = 0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for it in range(args.warmup + args.steps):
+        h0 = time.perf_counter()
+        out_pairs = [pa.swap_blocks(db.bm.pool, host, db.bm.rows[s, :nb[s]])
+                     for s in range(w.num_seqs)]
+        h1 = time.perf_counter()
+        po = torch.from_numpy(np.concatenate(out_pairs)).cuda()
+        ev[0].record()
+        pa.transfer_blocks(kd, vd, kh, vh, po)
+        ev[1].record()
+        h2 = time.perf_counter()
+        in_pairs = [pa.swap_blocks(host, db.bm.pool, p[:, 1]) for p in out_pairs]
+        h3 = time.perf_counter()
+        for s, p in enumerate(in_pairs):
+            db.bm.rows[s, :nb[s]] = p[:, 1]
+        pi = torch.from_numpy(np.concatenate(in_pairs)).cuda()
+        ev[2].record()
+        pa.transfer_blocks(kh, vh, kd, vd, pi)
+        ev[3].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            t_out += ev[0].elapsed_time(ev[1])
+            t_in += ev[2].elapsed_time(ev[3])
+            t_host += (h1 - h0) + (h3 - h2)
+            moved += po.shape[0]
+    n = max(1, args.steps)
+    per_dir = moved / n * block_bytes
+    out_gbs = per_dir / (t_out / n * 1e-3) / 1e9
+    in_gbs = per_dir / (t_in / n * 1e-3) / 1e9
+    value = 2 * per_dir / ((t_out + t_in) / n * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "block swap device <-> pinned host GB/s", "value": round(value, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t_out + t_in) / n, 4), "higher_is_better": True,
+        "dtype": "i8" if int8 else w.dtype, "data": "synthetic",
+        "config": {"workload": w.name + ("-int8kv" if int8 else ""), "blocks_per_direction":
+                   int(moved / n), "block_bytes": block_bytes},
+        "swap_out_gbs": round(out_gbs, 2), "swap_in_gbs": round(in_gbs, 2),
+        "host_bookkeeping_ms_per_step": round(t_host / n * 1e3, 3),
+        "roofline": {"bound": "host-link", "kernel": "transfer_blocks_kernel",
+                     "achieved": round(value, 2), "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HOST_LINK_PEAK_GBS, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +263,9 @@ def main():
     ap.add_argument("--kv", choices=("native", "int8"), default="native",
                     help="KV cache storage: the workload's dtype, or INT8 codes with "
                          "per-channel scales")
+    ap.add_argument("--swap", action="store_true",
+                    help="instead of decode steps: move every block of the batch to a pinned "
+                         "host pool and back (host-tier swap bandwidth)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -225,6 +298,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.swap:
+        swap_bench(args)
+        return
     import paged_kv_cache_06_amd as pa
     if not os.path.exists(pa.lib_path()):
         from paged_kv_cache_06_amd import _build
