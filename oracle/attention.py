@@ -22,6 +22,12 @@ Readings (the pages print no attention formula; listed in the design doc):
   calculation for softmax", 2018) gives the same result; ``partials`` and
   ``merge`` write that rule out for the tests of split-K.
 
+``paged_prefill`` extends decode to a chunk of several new tokens per
+sequence, each attending causally (pins in tests/test_oracle_prefill.py: one
+token equals ``paged_decode`` bit for bit, a whole prompt equals torch's
+causal scaled_dot_product_attention in float64, later positions cannot
+change earlier outputs, brute force on tiny inputs).
+
 Pins (tests/test_oracle_attention.py): brute force with Python scalars on tiny
 inputs, torch's scaled_dot_product_attention in float64, invariance under any
 relabelling of physical blocks, weights that sum to 1, len=1 -> v_0 exactly,
@@ -79,6 +85,42 @@ def paged_decode(q_bits, k_cache_bits, v_cache_bits, block_tables, context_lens,
             V = gather(v_cache_bits, block_tables[s], length, g, dtype)
             for h in range(g * group, (g + 1) * group):
                 out[s, h] = attend(q[s, h], K, V, scale)
+    return out
+
+
+def paged_prefill(q_bits, k_cache_bits, v_cache_bits, block_tables, query_start, context_lens,
+                  scale: float, dtype: str) -> np.ndarray:
+    """Attention of a chunk of new tokens per sequence (chunked prefill).
+
+    Every token needs the K and V of all tokens before it ("KV Cache and
+    PagedAttention: why your LLM server slows down", second article, section
+    "What is the KV cache?"); a chunk of n_s new tokens of sequence s whose
+    K/V are already in the cache (like the decoded token, reading R2) are the
+    last n_s of its len_s positions, and query i of the chunk, at position
+    p = len_s - n_s + i, attends to positions 0..p (causal).  n_s = 1 is
+    decode.  q_bits [T, Hq, D] holds the chunks back to back: sequence s owns
+    rows query_start[s] .. query_start[s+1]-1.  Returns float64 [T, Hq, D].
+    """
+    T, Hq, D = q_bits.shape
+    Hkv = k_cache_bits.shape[1]
+    group = Hq // Hkv
+    q = to_f64(q_bits, dtype)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for s in range(len(context_lens)):
+        a, b = int(query_start[s]), int(query_start[s + 1])
+        length = int(context_lens[s])
+        n = b - a
+        if n == 0:
+            continue
+        if n > length:
+            raise ValueError("a chunk cannot be longer than its sequence")
+        for g in range(Hkv):
+            K = gather(k_cache_bits, block_tables[s], length, g, dtype)
+            V = gather(v_cache_bits, block_tables[s], length, g, dtype)
+            for i in range(n):
+                p = length - n + i
+                for h in range(g * group, (g + 1) * group):
+                    out[a + i, h] = attend(q[a + i, h], K[:p + 1], V[:p + 1], scale)
     return out
 
 

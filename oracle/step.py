@@ -147,6 +147,20 @@ def run(w, fill_bits, phases=None, prefix_cache: bool = False):
     return pl, k_cache, v_cache, out
 
 
+def run_prefill(w, fill_bits):
+    """``run`` for a chunked-prefill batch: after the step wrote every chunk's
+    K/V, each chunk's queries (``w.chunk_q``) attend causally.  Returns (plan,
+    k_cache, v_cache, out [T, Hq, D])."""
+    pl = plan(w)
+    k_cache, v_cache = empty_cache(w, fill_bits)
+    for ph in pl.phases:
+        apply_phase(ph, k_cache, v_cache)
+    width = max(1, max(len(t) for t in pl.tables))
+    out = attention.paged_prefill(w.chunk_q, k_cache, v_cache, pl.padded_tables(width, 0),
+                                  w.query_start, pl.context_lens, w.scale, w.dtype)
+    return pl, k_cache, v_cache, out
+
+
 def run_int8(w, fill_code: int = 127, prefix_cache: bool = False):
     """``run`` over an INT8 cache with the workload's per-channel scales: the
     phases' tokens are quantized as they are written.  Returns (plan, k_codes,

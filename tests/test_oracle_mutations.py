@@ -181,3 +181,38 @@ def test_planted_backwards_transfer_is_caught(monkeypatch):
     monkeypatch.setattr(cache_ops, "transfer_blocks", backwards)
     with pytest.raises((AssertionError, IndexError)):
         tsw.test_swap_out_and_back_in_restores_every_sequence_exactly()
+
+
+from tests import test_oracle_prefill as tpf  # noqa: E402
+
+
+def _prefill_window(extra):
+    def bad(q_bits, k_cache_bits, v_cache_bits, block_tables, query_start, context_lens, scale,
+            dtype):
+        T, Hq, D = q_bits.shape
+        group = Hq // k_cache_bits.shape[1]
+        q = attention.to_f64(q_bits, dtype)
+        out = np.zeros((T, Hq, D))
+        for s in range(len(context_lens)):
+            a, b = int(query_start[s]), int(query_start[s + 1])
+            length, n = int(context_lens[s]), b - a
+            for g in range(k_cache_bits.shape[1]):
+                K = attention.gather(k_cache_bits, block_tables[s], length, g, dtype)
+                V = attention.gather(v_cache_bits, block_tables[s], length, g, dtype)
+                for i in range(n):
+                    p = length if extra is None else length - n + i + extra
+                    for h in range(g * group, (g + 1) * group):
+                        out[a + i, h] = attention.attend(q[a + i, h], K[:p], V[:p], scale)
+        return out
+    return bad
+
+
+@pytest.mark.parametrize("bad,pin", [
+    (_prefill_window(0), tpf.test_one_token_chunks_are_decode_bit_for_bit),  # drops position p
+    (_prefill_window(None), tpf.test_later_positions_cannot_change_earlier_queries),  # not causal
+    (_prefill_window(None), tpf.test_whole_prompts_match_torch_causal_sdpa_float64),
+], ids=["off-by-one", "non-causal", "non-causal-sdpa"])
+def test_planted_prefill_mistake_is_caught(monkeypatch, bad, pin):
+    monkeypatch.setattr(attention, "paged_prefill", bad)
+    with pytest.raises(AssertionError):
+        pin()

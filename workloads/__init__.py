@@ -12,6 +12,7 @@ from .generators import (  # noqa: F401
     Workload,
     make,
     make_custom,
+    make_prefill,
     round_to_dtype_bits,
     bits_dtype,
 )

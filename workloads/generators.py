@@ -36,6 +36,9 @@ CONFIG_NAMES = {
     5: "long-context-32k-f16",
     # variant of 4: one prefix shared by all 256 sequences
     "4b": "shared-prefix-all-bf16",
+    # chunked prefill: 16 sequences, a 512-token chunk each after U{0..3584}
+    # cached tokens, Llama-3-8B layer shape
+    "prefill": "chunked-prefill-8b-bf16",
 }
 
 
@@ -92,6 +95,13 @@ class Workload:
     v_private: np.ndarray
     block_size: int = BLOCK_SIZE
     notes: dict = field(default_factory=dict)
+    # chunked prefill: one query per token the step writes, [sum(step_lens), Hq, D]
+    chunk_q: np.ndarray | None = None
+
+    @property
+    def query_start(self) -> np.ndarray:
+        """Row offsets of each sequence's chunk in ``chunk_q`` (int32 [S + 1])."""
+        return np.concatenate([[0], np.cumsum(self.step_lens, dtype=np.int64)]).astype(np.int32)
 
     # ---- bookkeeping helpers (index arithmetic over the arrays above) ----
     @property
@@ -216,6 +226,23 @@ def _pool_size_unshared(lens, factor=1.1):
     return int(math.ceil(factor * int(_ceil_div(lens, BLOCK_SIZE).sum())))
 
 
+def make_prefill(chunk_lens, cached_lens, *, hq, hkv, d, dtype, seed=0, name="prefill-custom",
+                 num_blocks=None) -> Workload:
+    """Chunked-prefill batch: sequence s holds cached_lens[s] tokens and
+    appends a chunk of chunk_lens[s] >= 1 tokens in the step; ``chunk_q``
+    holds one query per chunk token, drawn after everything else."""
+    chunk_lens = np.asarray(chunk_lens, dtype=np.int32)
+    lens = np.asarray(cached_lens, dtype=np.int32) + chunk_lens
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if num_blocks is None:
+        num_blocks = max(1, int(math.ceil(1.25 * _pool_size_unshared(lens, 1.0))) + 2)
+    w = _build(name, seed, rng, hq=hq, hkv=hkv, d=d, dtype=dtype,
+               prompt_of=-np.ones(lens.shape[0], np.int32), prompt_lens=[], private_lens=lens,
+               num_blocks=num_blocks, step_lens=chunk_lens)
+    w.chunk_q = _normal_bits(rng, int(chunk_lens.sum()) * hq * d, dtype).reshape(-1, hq, d)
+    return w
+
+
 def make(config, seed=None, values=True) -> Workload:
     """Workload ``config`` (1..5 or "4b") with its own seed unless one is given.
 
@@ -227,6 +254,14 @@ def make(config, seed=None, values=True) -> Workload:
         key = int(config)
     if key not in CONFIG_NAMES:
         raise ValueError(f"unknown workload {config!r}")
+    if key == "prefill":
+        seed = 6 if seed is None else int(seed)
+        rng = np.random.Generator(np.random.PCG64(seed))
+        cached = rng.integers(0, 3584, size=16, endpoint=True).astype(np.int32)
+        w = make_prefill(np.full(16, 512, np.int32), cached, hq=32, hkv=8, d=128, dtype="bf16",
+                         seed=seed + 1000, name=CONFIG_NAMES[key])
+        w.seed = seed
+        return w
     seed = (4 if key == "4b" else int(key)) if seed is None else int(seed)
     rng = np.random.Generator(np.random.PCG64(seed))
     name = CONFIG_NAMES[key]
