@@ -316,6 +316,28 @@ pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const vo
                                     int32_t partition_size, void* workspace,
                                     size_t workspace_bytes, pa_dtype dtype, void* stream);
 
+/* Chunked prefill: sequence s appends a chunk of n_s new tokens whose K/V are
+ * already in the cache (pa_reshape_and_cache first, as for decode); query i
+ * of the chunk sits at position p = len_s - n_s + i and attends to positions
+ * 0..p (causal), as every token needs the K and V of all tokens before it
+ * ("KV Cache and PagedAttention: why your LLM server slows down", second
+ * article, section "What is the KV cache?").  One token per sequence is
+ * decode.
+ *   q, out        device [T][num_q_heads][head_dim], the chunks back to back:
+ *                 sequence s owns rows query_start[s] .. query_start[s+1]-1
+ *   query_start   device int32 [num_seqs + 1], non-decreasing, from 0
+ *   context_lens  device int32 [num_seqs]: len_s including the chunk
+ *                 (len_s >= n_s; larger n_s is read as len_s = n_s)
+ *   max_chunk_len host bound of every n_s (a larger chunk is cut to it)
+ * Other arguments as pa_paged_attention_decode.  dtype F16 or BF16, head_dim
+ * 64 or 128, else PA_ERR_UNSUPPORTED. */
+pa_status pa_paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* query_start,
+                                     const int32_t* context_lens, float scale, void* out,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t max_blocks_per_seq,
+                                     int32_t max_chunk_len, pa_dtype dtype, void* stream);
+
 /* ---------------------------------------------------------------------------
  * INT8 KV cache ("KV Cache for the intermediate", section "KV Cache
  * Quantization": K and V kept as 8-bit integers instead of 16-bit floats
@@ -368,7 +390,8 @@ pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, con
 #define PA_KERNEL_COPY_BLOCKS 3
 #define PA_KERNEL_DECODE_PLAN 4     /* work list of pa_paged_attention_decode */
 #define PA_KERNEL_TRANSFER_BLOCKS 5 /* pa_transfer_blocks */
-#define PA_NUM_KERNEL_KINDS 6
+#define PA_KERNEL_PREFILL 6         /* pa_paged_attention_prefill */
+#define PA_NUM_KERNEL_KINDS 7
 
 pa_status pa_timing_begin(int32_t capacity);
 pa_status pa_timing_end(double* ms_out /* [PA_NUM_KERNEL_KINDS] */,

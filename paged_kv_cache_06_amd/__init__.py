@@ -6,7 +6,8 @@ memory and the stream; nothing here computes on tensors.  When ``libpa.so`` is
 missing every call raises -- there is no fallback.
 
 The names follow the C ABI of ``include/pa.h`` without its ``pa_`` prefix:
-``reshape_and_cache``, ``copy_blocks``, ``paged_attention_decode``, their INT8
+``reshape_and_cache``, ``copy_blocks``, ``paged_attention_decode``,
+``paged_attention_prefill`` (chunked prefill), their INT8
 cache forms ``reshape_and_cache_int8`` and ``paged_attention_decode_int8``, the pool
 calls on :class:`Pool` (``alloc``, ``free``, ``incref``, ``fork``,
 ``free_table``, ``append_slots``, ``prefix_match``, ``prefix_register``,
@@ -25,7 +26,7 @@ __all__ = [
     "Pool", "BlockManager", "blocks_for_bytes", "reshape_and_cache", "copy_blocks",
     "paged_attention_decode", "decode_workspace_bytes", "decode_auto_partition",
     "decode_set_max_groups", "reshape_and_cache_int8", "paged_attention_decode_int8",
-    "swap_blocks", "transfer_blocks", "new_host_kv_cache",
+    "swap_blocks", "transfer_blocks", "new_host_kv_cache", "paged_attention_prefill",
     "new_kv_cache", "new_kv_cache_int8", "logical_view", "timing_begin", "timing_end", "status_string",
 ]
 
@@ -34,7 +35,7 @@ PARTITION_NONE = 0
 PARTITION_AUTO = -1
 PARTITION_BALANCED = -2
 KERNEL_KINDS = ("decode", "decode_reduce", "reshape_and_cache", "copy_blocks", "decode_plan",
-                "transfer_blocks")
+                "transfer_blocks", "prefill")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -86,6 +87,9 @@ _SIGNATURES = {
     "pa_paged_attention_decode_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f,
                                                 _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                                 _c_i32, _c_i32, _c_p, _c_sz, _c_i32, _c_p]),
+    "pa_paged_attention_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_p,
+                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                            _c_i32, _c_p]),
     "pa_timing_begin": (_c_i32, [_c_i32]),
     "pa_timing_end": (_c_i32, [ctypes.POINTER(ctypes.c_double), _P_I32]),
 }
@@ -578,6 +582,31 @@ def paged_attention_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_tab
         _scales(v_scale, hkv, d, "v_scale"), _ptr(block_tables), _ptr(context_lens.contiguous()),
         float(scale), _ptr(out), s, hq, hkv, d, mb, mcl, int(partition_size), ws_ptr, ws_bytes,
         _dtype_code(q), _stream(q)), "pa_paged_attention_decode_int8")
+
+
+def paged_attention_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale,
+                            out, *, max_chunk_len: int) -> None:
+    """Chunked prefill: the chunk queries q [T, Hq, D] (sequence s owns rows
+    query_start[s] .. query_start[s+1]-1, the last positions of its
+    context_lens[s]) attend causally over the paged cache; out [T, Hq, D]."""
+    torch = _torch()
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    t, hq, dq = q.shape
+    _need(dq == d and tuple(out.shape) == (t, hq, d), "q/out must be [T, Hq, D]")
+    _need(q.is_contiguous() and out.is_contiguous(), "q/out must be contiguous")
+    _need(q.dtype == out.dtype == k_cache.dtype, "dtypes differ")
+    s = context_lens.numel()
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == s and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(query_start.dtype == torch.int32 and query_start.numel() == s + 1 and
+          query_start.is_contiguous(), "query_start must be contiguous int32 [S + 1]")
+    _need(context_lens.dtype == torch.int32, "context_lens must be int32 [S]")
+    _check(load().pa_paged_attention_prefill(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(query_start),
+        _ptr(context_lens.contiguous()), float(scale), _ptr(out), s, hq, hkv, d,
+        block_tables.shape[1], int(max_chunk_len), _dtype_code(q), _stream(q)),
+        "pa_paged_attention_prefill")
 
 
 # ------------------------------------------------------------------ timing

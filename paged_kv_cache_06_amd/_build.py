@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_pool.cpp", "pa_timing.hip", "pa_cache_ops.hip", "pa_decode.hip", "pa_decode_balanced.hip"]
+SOURCES = ["pa_pool.cpp", "pa_timing.hip", "pa_cache_ops.hip", "pa_decode.hip", "pa_decode_balanced.hip", "pa_prefill.hip"]
 ARCH = "gfx950"
 
 

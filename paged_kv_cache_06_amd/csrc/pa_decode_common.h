@@ -195,16 +195,18 @@ __device__ __forceinline__ void load_block(const DecodeArgs& a, int g, int phys,
 // scores sc (lane l: head l%16, tokens 4*(l/16) .. +3) are known: scores are
 // multiplied by sl2 (the softmax scale in log2 units), positions at or past
 // `len` are masked, vf holds the block's V as PV A operands.
+// `lim` (per lane, at most len): scores of positions at or past it are masked
+// (a causal limit per column); `len` bounds the V rows that hold data.
 template <typename Tag, int D>
-__device__ __forceinline__ void block_update(uint2* vf, f32x4_t sc, float sl2, int blk, int len,
-                                             WaveState<D>& st) {
+__device__ __forceinline__ void block_update_lim(uint2* vf, f32x4_t sc, float sl2, int blk,
+                                                 int len, int lim, WaveState<D>& st) {
   constexpr int kSlices = D / 16;  // PV output slices of 16 dims
   const int lane = threadIdx.x & (kWave - 1);
   const int kg = lane >> 4;  // k-group of the MFMA operands
   const int pos0 = blk * kBlock + kg * 4;  // position of this lane's first score
   float s4[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s4[i] = (pos0 + i < len) ? sc[i] * sl2 : -INFINITY;
+  for (int i = 0; i < 4; ++i) s4[i] = (pos0 + i < lim) ? sc[i] * sl2 : -INFINITY;
   float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -236,6 +238,12 @@ __device__ __forceinline__ void block_update(uint2* vf, f32x4_t sc, float sl2, i
     st.acc[sl] = Mfma<Tag>::pv(vf[sl], ph, st.acc[sl]);
     st.acc[sl] = Mfma<Tag>::pv(vf[sl], pl, st.acc[sl]);
   }
+}
+
+template <typename Tag, int D>
+__device__ __forceinline__ void block_update(uint2* vf, f32x4_t sc, float sl2, int blk, int len,
+                                             WaveState<D>& st) {
+  block_update_lim<Tag, D>(vf, sc, sl2, blk, len, len, st);
 }
 
 // One block (logical index blk) into the running state: positions at or past

@@ -21,7 +21,7 @@ import numpy as np
 
 from . import (BLOCK_SIZE, PARTITION_AUTO, BlockManager, Pool, copy_blocks, new_kv_cache,
                new_kv_cache_int8, paged_attention_decode, paged_attention_decode_int8,
-               reshape_and_cache, reshape_and_cache_int8)
+               paged_attention_prefill, reshape_and_cache, reshape_and_cache_int8)
 
 _TORCH_DTYPE = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
 NAN_FILL = float("nan")
@@ -204,6 +204,21 @@ class DeviceBatch:
                                self.out if out is None else out,
                                max_context_len=self.max_context_len,
                                partition_size=partition_size)
+
+    def attend_chunks(self, copy: int = 0, out=None):
+        """Chunked prefill of a batch with ``chunk_q``: the step's tokens
+        (phase B, already written) attend causally; returns the output tensor."""
+        import torch
+        if not hasattr(self, "chunk_q"):
+            self.chunk_q = self._dev(self.w.chunk_q)
+            self.query_start = torch.from_numpy(self.w.query_start).to(self.device)
+            self.chunk_out = torch.empty_like(self.chunk_q)
+            self.max_chunk = int(np.max(self.w.step_lens))
+        kc, vc = self.caches[copy]
+        o = self.chunk_out if out is None else out
+        paged_attention_prefill(self.chunk_q, kc, vc, self.tables, self.query_start,
+                                self.context_lens, self.w.scale, o, max_chunk_len=self.max_chunk)
+        return o
 
     def out_bits(self, out=None) -> np.ndarray:
         import torch
