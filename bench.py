@@ -251,6 +251,72 @@ def swap_bench(args):
     }), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
+
+
+def prefill_flops(w):
+    """QK and PV of every chunk query against every position up to its own,
+    2 flops per multiply-add: sum over queries of (p + 1) * 4 * Hq * D."""
+    import numpy as np
+    lens = np.asarray(w.context_lens, dtype=np.int64)
+    n = np.asarray(w.step_lens, dtype=np.int64)
+    # positions p = len - n + i, i < n: sum of (p + 1) = n * (len - n) + n (n + 1) / 2
+    pairs = int((n * (lens - n) + n * (n + 1) // 2).sum())
+    return pairs * 4 * w.num_q_heads * w.head_dim, pairs
+
+
+def prefill_bench(args):
+    """Chunked prefill: the step writes every chunk's K/V and attends its
+    queries causally; K steps.  Prints one JSON line."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_06_amd as pa
+    import workloads
+    from paged_kv_cache_06_amd import runner
+    w = workloads.make("prefill")
+    db = runner.DeviceBatch(w)
+    db.prefill()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        db._apply(db.dev_phases[2], db.caches[0])
+        db.attend_chunks()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        db._apply(db.dev_phases[2], db.caches[0])
+        db.attend_chunks()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pa.timing_begin(4 * args.steps + 16)
+    for _ in range(args.steps):
+        db._apply(db.dev_phases[2], db.caches[0])
+        db.attend_chunks()
+    torch.cuda.synchronize()
+    kt = pa.timing_end()
+    flops, pairs = prefill_flops(w)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    k = kt["prefill"]
+    k_ms = k["ms"] / max(1, k["launches"])
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    tokens = int(np.sum(w.step_lens))
+    print(json.dumps({
+        "metric": "chunked-prefill paged attention TFLOP/s; prefill tokens/s",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "chunk_tokens": tokens,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "attended_pairs": pairs},
+        "prefill_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "kernels_ms_per_step": {kk: round(v["ms"] / max(1, v["launches"]), 5)
+                                for kk, v in kt.items() if v["launches"]},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops,
+                     "avg_launch_ms": round(k_ms, 5), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +332,9 @@ def main():
     ap.add_argument("--swap", action="store_true",
                     help="instead of decode steps: move every block of the batch to a pinned "
                          "host pool and back (host-tier swap bandwidth)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="instead of decode steps: the chunked-prefill workload (16 sequences, "
+                         "512-token chunks after U{0..3584} cached tokens, 32/8 heads, D 128)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -300,6 +369,9 @@ def main():
         sys.exit(1)
     if args.swap:
         swap_bench(args)
+        return
+    if args.prefill:
+        prefill_bench(args)
         return
     import paged_kv_cache_06_amd as pa
     if not os.path.exists(pa.lib_path()):

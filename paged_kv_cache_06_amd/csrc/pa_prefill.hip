@@ -5,9 +5,9 @@
 // cache?").  The chunk's K/V are in the cache before the call, as for decode,
 // so one token per sequence is exactly decode.
 //
-// One wave per unit of work = (sequence, KV head, group of up to 16 query
-// heads, a run of consecutive chunk queries); the 16 columns of its matrix-
-// core products are (query, head) pairs, query-major: with G query heads per
+// One wave per run of consecutive chunk queries of one (sequence, KV head,
+// group of up to 16 query heads); the 16 columns of its matrix-core products
+// are (query, head) pairs, query-major: with G query heads per
 // KV head (G <= 16) a wave serves 16 / G queries of that KV head at once, so
 // every K/V block it loads is multiplied against 16 query rows.  Per 16-token
 // block, as in decode:
@@ -36,37 +36,108 @@ struct PrefillArgs {
   int groups_max;           // query runs of the longest chunk: ceil(max_chunk / qpw)
 };
 
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14];
+// expcnt and lgkmcnt left unwaited)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillDepth = 4;  // K/V blocks in flight per work-group
+
+// One block's MFMA operands from an LDS stage (K: 16 bytes per lane per
+// k-step, 1 KiB apart; V: 8 bytes per lane per slice, 512 bytes apart), in one
+// block of LDS reads that ends with their wait.
+template <int D>
+__device__ __forceinline__ void read_block(uint32_t ka, uint32_t va, BlockRegs<D>& r);
+
+template <>
+__device__ __forceinline__ void read_block<128>(uint32_t ka, uint32_t va, BlockRegs<128>& r) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n"
+      "ds_read_b128 %1, %12 offset:1024\n"
+      "ds_read_b128 %2, %12 offset:2048\n"
+      "ds_read_b128 %3, %12 offset:3072\n"
+      "ds_read_b64 %4, %13\n"
+      "ds_read_b64 %5, %13 offset:512\n"
+      "ds_read_b64 %6, %13 offset:1024\n"
+      "ds_read_b64 %7, %13 offset:1536\n"
+      "ds_read_b64 %8, %13 offset:2048\n"
+      "ds_read_b64 %9, %13 offset:2560\n"
+      "ds_read_b64 %10, %13 offset:3072\n"
+      "ds_read_b64 %11, %13 offset:3584\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.kf[0]), "=&v"(r.kf[1]), "=&v"(r.kf[2]), "=&v"(r.kf[3]), "=&v"(r.vf[0]),
+        "=&v"(r.vf[1]), "=&v"(r.vf[2]), "=&v"(r.vf[3]), "=&v"(r.vf[4]), "=&v"(r.vf[5]),
+        "=&v"(r.vf[6]), "=&v"(r.vf[7])
+      : "v"(ka), "v"(va)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_block<64>(uint32_t ka, uint32_t va, BlockRegs<64>& r) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n"
+      "ds_read_b128 %1, %6 offset:1024\n"
+      "ds_read_b64 %2, %7\n"
+      "ds_read_b64 %3, %7 offset:512\n"
+      "ds_read_b64 %4, %7 offset:1024\n"
+      "ds_read_b64 %5, %7 offset:1536\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.kf[0]), "=&v"(r.kf[1]), "=&v"(r.vf[0]), "=&v"(r.vf[1]), "=&v"(r.vf[2]),
+        "=&v"(r.vf[3])
+      : "v"(ka), "v"(va)
+      : "memory");
+}
+
+// Work-group = 4 waves = 4 consecutive runs of chunk queries of one
+// (sequence, KV head, head block).  They walk the same K/V blocks, so each
+// block is brought into LDS once for all four by direct buffer-to-LDS loads
+// (each wave moves 1/4 of it) through a ring of kPrefillDepth stages, and
+// every wave reads its operands from there.
 template <typename Tag, int D>
-__global__ __launch_bounds__(kWave, 4) void prefill_kernel(PrefillArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int kStage = 2 * D * kBlock * 2;         // K then V of one block-head
+  constexpr int kChunksPerWave = D / 64;              // 1 KiB loads per wave per stage
+  extern __shared__ char ring[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
   const int n = lane & 15, kg = lane >> 4;
-  // unit = (run, sequence, KV head, head block), run-major from the last run
+  // unit = (run group, sequence, KV head, head block), from the last runs
   const int per_run = a.num_seqs * a.hkv * a.head_blocks;
   const int u = blockIdx.x;
-  const int run = a.groups_max - 1 - u / per_run;
+  const int run_groups = (a.groups_max + kPrefillWaves - 1) / kPrefillWaves;
+  const int rg = run_groups - 1 - u / per_run;
   const int r = u % per_run;
   const int s = r / (a.hkv * a.head_blocks);
   const int g = (r / a.head_blocks) % a.hkv;
   const int hb = r % a.head_blocks;
   const int q0 = uniform_load(a.qstart, s), q1 = uniform_load(a.qstart, s + 1);
-  // a length below the chunk reads as the chunk; both stop at the table's width
   const int len = min(max(uniform_load(a.lens, s), q1 - q0), a.max_blocks * kBlock);
   const int nchunk = min(q1 - q0, len);
-  const int i0 = run * a.qpw;
-  if (i0 >= nchunk) return;
-  const int nq = min(a.qpw, nchunk - i0);
+  const int i_wg = rg * kPrefillWaves * a.qpw;  // first query of the work-group
+  if (i_wg >= nchunk) return;                    // uniform over the work-group
+  const int i0 = i_wg + wave * a.qpw;            // first query of this wave
+  const int nq = max(0, min(a.qpw, nchunk - i0));
   const int h_base = hb * 16;
   const int nh = min(a.cols_heads, a.group - h_base);
-  // this lane's column: query i, head h
   const int ci = n / a.cols_heads, ch = n % a.cols_heads;
   const bool col_ok = ci < nq && ch < nh;
-  const int first_pos = len - nchunk + i0;  // position of the run's first query
-  const int col_pos = first_pos + (col_ok ? ci : nq - 1);
-  const int last_pos = first_pos + nq - 1;
-  const int nblk = last_pos / kBlock + 1;
+  const int first_pos = len - nchunk + i0;
+  const int col_pos = nq > 0 ? first_pos + (col_ok ? ci : nq - 1) : 0;
+  const int wave_last = nq > 0 ? first_pos + nq - 1 : 0;
+  const int wg_last = len - nchunk + min(nchunk, i_wg + kPrefillWaves * a.qpw) - 1;
+  const int nblk = wg_last / kBlock + 1;     // blocks the work-group walks
+  const int my_blk = wave_last / kBlock + 1;  // blocks this wave needs
 
-  // query operand: column n's row, dims (j*4 + kg)*8 .. +7 of k-step j; idle
-  // columns are 0
   uint4 qf[D / 32];
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) qf[j] = make_uint4(0, 0, 0, 0);
@@ -76,28 +147,58 @@ __global__ __launch_bounds__(kWave, 4) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) qf[j] = qrow[j * 4 + kg];
   }
-  DecodeArgs da;  // the fields the block loads use
-  da.k_cache = a.k_cache;
-  da.v_cache = a.v_cache;
-  da.hkv = a.hkv;
 
   WaveState<D> st;
   st.reset();
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
+  const uint32_t va_lane = ((lane & 15) * kBlock + (lane >> 4) * 4) * 2;
   for (int c0 = 0; c0 < nblk; c0 += 64) {
-    const int ids = load_ids<1>(trow, c0, nblk - c0);
     const int cn = min(64, nblk - c0);
-    for (int j = 0; j < cn; ++j) {
-      const int blk = c0 + j;
-      BlockRegs<D> rb;
-      load_block<D>(da, g, __builtin_amdgcn_readlane(ids, j), rb);
-      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    const int ids = load_ids<1>(trow, c0, cn);
+    (void)__builtin_amdgcn_readfirstlane(ids);  // the ids are in before any stage is issued
+    // this wave's share of block j of the chunk into its stage; blocks past
+    // the chunk are issued with an empty range (they write zeros), so that
+    // every wave always has the same number of loads in flight
+    auto issue = [&](int j) {
+      const bool real = j < cn;
+      const int phys = __builtin_amdgcn_readlane(ids, real ? j : 0);
+      const size_t off = (static_cast<size_t>(phys) * a.hkv + g) * (D * kBlock);
+      const uint32_t range = real ? D * kBlock * 2 : 0u;
+      const auto rk = buffer_of(a.k_cache + off, range);
+      const auto rv = buffer_of(a.v_cache + off, range);
+      char* dst = ring + (j % kPrefillDepth) * kStage;
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) sc = Mfma<Tag>::qk(rb.kf[t], qf[t], sc);
-      // causal limit of this lane's column: positions after the query's own
-      // are masked; V rows past the sequence's end are zeroed on its last block
-      block_update_lim<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos + 1, st);
+      for (int c = 0; c < kChunksPerWave; ++c) {
+        const int chunk = wave * kChunksPerWave + c;  // of the stage's 2 * D / 32 KiBs
+        const bool is_v = chunk >= D / 32;
+        const int byte = (is_v ? chunk - D / 32 : chunk) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? rv : rk,
+                                                 (lds_void_t)(dst + (is_v ? D * kBlock * 2 : 0) + byte),
+                                                 16, lane * 16 + byte, 0, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < kPrefillDepth - 1; ++j) issue(j);
+    for (int j = 0; j < cn; ++j) {
+      wait_vm<(kPrefillDepth - 2) * kChunksPerWave>();  // this wave's part of block j is in
+      // ... and every other wave's: a bare barrier (a fenced one would wait for
+      // every load in flight); the loads are counted in by the waits, and LDS
+      // reads of earlier rounds end with their own wait
+      __builtin_amdgcn_s_barrier();
+      issue(j + kPrefillDepth - 1);                      // into the stage read last round
+      const int blk = c0 + j;
+      if (blk < my_blk) {
+        const char* stg = ring + (j % kPrefillDepth) * kStage;
+        BlockRegs<D> rb;
+        read_block<D>(lds_addr(stg) + lane * 16, lds_addr(stg + D * kBlock * 2) + va_lane, rb);
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) sc = Mfma<Tag>::qk(rb.kf[t], qf[t], sc);
+        block_update_lim<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos + 1, st);
+      }
     }
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // the next chunk's first stages may be overwritten
   }
   float l_tot = st.l + __shfl_xor(st.l, 16);
   l_tot += __shfl_xor(l_tot, 32);
@@ -114,11 +215,12 @@ __global__ __launch_bounds__(kWave, 4) void prefill_kernel(PrefillArgs a) {
 
 template <typename Tag>
 pa_status launch_prefill(const PrefillArgs& a, int head_dim, int64_t units, hipStream_t st) {
-  const dim3 g3(static_cast<uint32_t>(units)), b3(kWave);
+  const dim3 g3(static_cast<uint32_t>(units)), b3(kPrefillWaves * kWave);
+  const size_t lds = static_cast<size_t>(kPrefillDepth) * 2 * head_dim * kBlock * 2;
   if (head_dim == 128)
-    prefill_kernel<Tag, 128><<<g3, b3, 0, st>>>(a);
+    prefill_kernel<Tag, 128><<<g3, b3, lds, st>>>(a);
   else
-    prefill_kernel<Tag, 64><<<g3, b3, 0, st>>>(a);
+    prefill_kernel<Tag, 64><<<g3, b3, lds, st>>>(a);
   return launch_status();
 }
 
@@ -162,8 +264,8 @@ pa_status pa_paged_attention_prefill(const void* q, const void* k_cache, const v
   a.cols_heads = std::min(a.group, 16);
   a.qpw = 16 / a.cols_heads;
   a.groups_max = (max_chunk_len + a.qpw - 1) / a.qpw;
-  const int64_t units =
-      static_cast<int64_t>(a.groups_max) * num_seqs * num_kv_heads * a.head_blocks;
+  const int64_t units = static_cast<int64_t>((a.groups_max + kPrefillWaves - 1) / kPrefillWaves) *
+                        num_seqs * num_kv_heads * a.head_blocks;
   if (units > 0x7fffffff) return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int slot = timing_start(PA_KERNEL_PREFILL, st);
