@@ -14,7 +14,7 @@
 //   scores[16 tok x 16 cols] = K . Q^T          (MFMA 16x16x32, K as A)
 //   online softmax per column, masked causally: token t counts for the column
 //   of the query at position p iff t <= p
-//   acc^T[D x 16 cols] += V^T . P^T             (MFMA 16x16x16, P as hi + lo)
+//   acc^T[D x 16 cols] += V^T . P^T             (MFMA 16x16x16)
 // Units are ordered so that the queries with the most positions start first.
 #include "pa_decode_common.h"
 
@@ -96,6 +96,53 @@ __device__ __forceinline__ void read_block<64>(uint32_t ka, uint32_t va, BlockRe
         "=&v"(r.vf[3])
       : "v"(ka), "v"(va)
       : "memory");
+}
+
+// Online-softmax step of one block for the prefill kernel.  Two departures
+// from decode's block_update, both for the matrix cores' sake (prefill is
+// bound by arithmetic, not by HBM): P enters PV as one value in the storage
+// dtype (decode's hi + lo pair doubles the PV products), and the running
+// maximum is raised only when a score exceeds it by more than 2^8 (the
+// weights then stay below 2^8, which fp32 sums and bf16/fp16 weights hold),
+// so that the accumulator is rescaled on few blocks instead of on every one.
+template <typename Tag, int D>
+__device__ __forceinline__ void prefill_update(uint2* vf, f32x4_t sc, float sl2, int blk, int len,
+                                               int lim, WaveState<D>& st) {
+  constexpr int kSlices = D / 16;
+  constexpr float kSlack = 8.f;  // log2 units
+  const int lane = threadIdx.x & (kWave - 1);
+  const int kg = lane >> 4;
+  const int pos0 = blk * kBlock + kg * 4;
+  float s4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s4[i] = (pos0 + i < lim) ? sc[i] * sl2 : -INFINITY;
+  float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kSlack) != 0) {  // some column outgrew its max
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = fast_exp2(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int sl = 0; sl < kSlices; ++sl) st.acc[sl] *= alpha;
+    st.m = m_new;
+  }
+  float p4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p4[i] = fast_exp2(s4[i] - st.m);
+  st.l += (p4[0] + p4[1]) + (p4[2] + p4[3]);
+  if ((blk + 1) * kBlock > len) {  // last block: zero V of positions past the end
+    const uint32_t lo = (pos0 + 0 < len ? 0x0000FFFFu : 0u) | (pos0 + 1 < len ? 0xFFFF0000u : 0u);
+    const uint32_t hi = (pos0 + 2 < len ? 0x0000FFFFu : 0u) | (pos0 + 3 < len ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int sl = 0; sl < kSlices; ++sl) {
+      vf[sl].x &= lo;
+      vf[sl].y &= hi;
+    }
+  }
+  const uint2 ph = Mfma<Tag>::pack(p4[0], p4[1], p4[2], p4[3]);
+#pragma unroll
+  for (int sl = 0; sl < kSlices; ++sl) st.acc[sl] = Mfma<Tag>::pv(vf[sl], ph, st.acc[sl]);
 }
 
 // Work-group = 4 waves = 4 consecutive runs of chunk queries of one
@@ -194,7 +241,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
         f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) sc = Mfma<Tag>::qk(rb.kf[t], qf[t], sc);
-        block_update_lim<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos + 1, st);
+        prefill_update<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos + 1, st);
       }
     }
     wait_vm<0>();
