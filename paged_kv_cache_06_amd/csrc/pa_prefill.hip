@@ -52,6 +52,10 @@ __device__ __forceinline__ void wait_vm() {
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillDepth = 4;  // K/V blocks in flight per work-group
+#ifndef PA_PREFILL_TILES
+#define PA_PREFILL_TILES 2
+#endif
+constexpr int kPrefillTiles = PA_PREFILL_TILES;  // 16-column tiles per wave
 
 // One block's MFMA operands from an LDS stage (K: 16 bytes per lane per
 // k-step, 1 KiB apart; V: 8 bytes per lane per slice, 512 bytes apart), in one
@@ -145,15 +149,17 @@ __device__ __forceinline__ void prefill_update(uint2* vf, f32x4_t sc, float sl2,
   for (int sl = 0; sl < kSlices; ++sl) st.acc[sl] = Mfma<Tag>::pv(vf[sl], ph, st.acc[sl]);
 }
 
-// Work-group = 4 waves = 4 consecutive runs of chunk queries of one
-// (sequence, KV head, head block).  They walk the same K/V blocks, so each
-// block is brought into LDS once for all four by direct buffer-to-LDS loads
-// (each wave moves 1/4 of it) through a ring of kPrefillDepth stages, and
-// every wave reads its operands from there.
+// Work-group = 4 waves x kPrefillTiles consecutive runs of chunk queries of
+// one (sequence, KV head, head block).  They walk the same K/V blocks, so
+// each block is brought into LDS once for all of them by direct
+// buffer-to-LDS loads (each wave moves 1/4 of it) through a ring of
+// kPrefillDepth stages; every wave reads the block's operands from there once
+// and multiplies them against its kPrefillTiles column tiles.
 template <typename Tag, int D>
 __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int kStage = 2 * D * kBlock * 2;         // K then V of one block-head
   constexpr int kChunksPerWave = D / 64;              // 1 KiB loads per wave per stage
+  constexpr int T = kPrefillTiles;
   extern __shared__ char ring[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
@@ -161,7 +167,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
   // unit = (run group, sequence, KV head, head block), from the last runs
   const int per_run = a.num_seqs * a.hkv * a.head_blocks;
   const int u = blockIdx.x;
-  const int run_groups = (a.groups_max + kPrefillWaves - 1) / kPrefillWaves;
+  const int runs_per_wg = kPrefillWaves * T;
+  const int run_groups = (a.groups_max + runs_per_wg - 1) / runs_per_wg;
   const int rg = run_groups - 1 - u / per_run;
   const int r = u % per_run;
   const int s = r / (a.hkv * a.head_blocks);
@@ -170,39 +177,49 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
   const int q0 = uniform_load(a.qstart, s), q1 = uniform_load(a.qstart, s + 1);
   const int len = min(max(uniform_load(a.lens, s), q1 - q0), a.max_blocks * kBlock);
   const int nchunk = min(q1 - q0, len);
-  const int i_wg = rg * kPrefillWaves * a.qpw;  // first query of the work-group
-  if (i_wg >= nchunk) return;                    // uniform over the work-group
-  const int i0 = i_wg + wave * a.qpw;            // first query of this wave
-  const int nq = max(0, min(a.qpw, nchunk - i0));
+  const int i_wg = rg * runs_per_wg * a.qpw;  // first query of the work-group
+  if (i_wg >= nchunk) return;                  // uniform over the work-group
   const int h_base = hb * 16;
   const int nh = min(a.cols_heads, a.group - h_base);
   const int ci = n / a.cols_heads, ch = n % a.cols_heads;
-  const bool col_ok = ci < nq && ch < nh;
-  const int first_pos = len - nchunk + i0;
-  const int col_pos = nq > 0 ? first_pos + (col_ok ? ci : nq - 1) : 0;
-  const int wave_last = nq > 0 ? first_pos + nq - 1 : 0;
-  const int wg_last = len - nchunk + min(nchunk, i_wg + kPrefillWaves * a.qpw) - 1;
+  // tile t of this wave: queries i0[t] .. i0[t] + nq[t] - 1
+  int i0[T], col_pos[T];
+  bool col_ok[T];
+  int wave_last = 0;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    i0[t] = i_wg + (wave * T + t) * a.qpw;
+    const int nq = max(0, min(a.qpw, nchunk - i0[t]));
+    col_ok[t] = ci < nq && ch < nh;
+    const int first_pos = len - nchunk + i0[t];
+    col_pos[t] = nq > 0 ? first_pos + (col_ok[t] ? ci : nq - 1) : 0;
+    if (nq > 0) wave_last = first_pos + nq - 1;
+  }
+  const int wg_last = len - nchunk + min(nchunk, i_wg + runs_per_wg * a.qpw) - 1;
   const int nblk = wg_last / kBlock + 1;     // blocks the work-group walks
   const int my_blk = wave_last / kBlock + 1;  // blocks this wave needs
 
-  uint4 qf[D / 32];
+  uint4 qf[T][D / 32];
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) qf[j] = make_uint4(0, 0, 0, 0);
-  if (col_ok) {
-    const size_t row = static_cast<size_t>(q0 + i0 + ci) * a.hq + g * a.group + h_base + ch;
-    const uint4* qrow = reinterpret_cast<const uint4*>(a.q + row * D);
+  for (int t = 0; t < T; ++t) {
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) qf[j] = qrow[j * 4 + kg];
+    for (int j = 0; j < D / 32; ++j) qf[t][j] = make_uint4(0, 0, 0, 0);
+    if (col_ok[t]) {
+      const size_t row = static_cast<size_t>(q0 + i0[t] + ci) * a.hq + g * a.group + h_base + ch;
+      const uint4* qrow = reinterpret_cast<const uint4*>(a.q + row * D);
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) qf[t][j] = qrow[j * 4 + kg];
+    }
   }
 
-  WaveState<D> st;
-  st.reset();
+  WaveState<D> st[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) st[t].reset();
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
   const uint32_t va_lane = ((lane & 15) * kBlock + (lane >> 4) * 4) * 2;
   for (int c0 = 0; c0 < nblk; c0 += 64) {
     const int cn = min(64, nblk - c0);
     const int ids = load_ids<1>(trow, c0, cn);
-    (void)__builtin_amdgcn_readfirstlane(ids);  // the ids are in before any stage is issued
     // this wave's share of block j of the chunk into its stage; blocks past
     // the chunk are issued with an empty range (they write zeros), so that
     // every wave always has the same number of loads in flight
@@ -238,25 +255,32 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
         const char* stg = ring + (j % kPrefillDepth) * kStage;
         BlockRegs<D> rb;
         read_block<D>(lds_addr(stg) + lane * 16, lds_addr(stg + D * kBlock * 2) + va_lane, rb);
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) sc = Mfma<Tag>::qk(rb.kf[t], qf[t], sc);
-        prefill_update<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos + 1, st);
+        for (int t = 0; t < T; ++t) {
+          f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < D / 32; ++k) sc = Mfma<Tag>::qk(rb.kf[k], qf[t][k], sc);
+          prefill_update<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos[t] + 1, st[t]);
+        }
       }
     }
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();  // the next chunk's first stages may be overwritten
   }
-  float l_tot = st.l + __shfl_xor(st.l, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (!col_ok) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* orow = a.out + (static_cast<size_t>(q0 + i0 + ci) * a.hq + g * a.group + h_base + ch) * D;
 #pragma unroll
-  for (int sl = 0; sl < D / 16; ++sl) {
-    const f32x4_t v = st.acc[sl];
-    const uint2 packed = Mfma<Tag>::pack(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-    *reinterpret_cast<uint2*>(orow + sl * 16 + kg * 4) = packed;
+  for (int t = 0; t < T; ++t) {
+    float l_tot = st[t].l + __shfl_xor(st[t].l, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (!col_ok[t]) continue;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow =
+        a.out + (static_cast<size_t>(q0 + i0[t] + ci) * a.hq + g * a.group + h_base + ch) * D;
+#pragma unroll
+    for (int sl = 0; sl < D / 16; ++sl) {
+      const f32x4_t v = st[t].acc[sl];
+      const uint2 packed = Mfma<Tag>::pack(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      *reinterpret_cast<uint2*>(orow + sl * 16 + kg * 4) = packed;
+    }
   }
 }
 
@@ -311,7 +335,8 @@ pa_status pa_paged_attention_prefill(const void* q, const void* k_cache, const v
   a.cols_heads = std::min(a.group, 16);
   a.qpw = 16 / a.cols_heads;
   a.groups_max = (max_chunk_len + a.qpw - 1) / a.qpw;
-  const int64_t units = static_cast<int64_t>((a.groups_max + kPrefillWaves - 1) / kPrefillWaves) *
+  const int runs_per_wg = kPrefillWaves * kPrefillTiles;
+  const int64_t units = static_cast<int64_t>((a.groups_max + runs_per_wg - 1) / runs_per_wg) *
                         num_seqs * num_kv_heads * a.head_blocks;
   if (units > 0x7fffffff) return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
