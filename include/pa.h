@@ -377,6 +377,23 @@ pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, con
                                          int32_t partition_size, void* workspace,
                                          size_t workspace_bytes, pa_dtype dtype, void* stream);
 
+/* One decode step: pa_reshape_and_cache of the step's new tokens
+ * (key/value/slot_mapping/num_new_tokens/num_blocks as there) followed by
+ * pa_paged_attention_decode (the other arguments as there), with the same
+ * results.  On the matrix-core path with fixed partitions the token writes
+ * run in the same launch as the decode's work list, saving one kernel
+ * launch per step; otherwise the two calls run one after the other.  The
+ * write and decode arguments are all checked before anything is launched
+ * (num_seqs = 0: only the write). */
+pa_status pa_decode_step(const void* key, const void* value, const int64_t* slot_mapping,
+                         int32_t num_new_tokens, int32_t num_blocks, const void* q, void* k_cache,
+                         void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes,
+                         pa_dtype dtype, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Kernel timing.  Between pa_timing_begin and pa_timing_end every kernel the
  * library launches is bracketed by HIP events on its own stream.
@@ -388,7 +405,8 @@ pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, con
 #define PA_KERNEL_DECODE_REDUCE 1   /* merge pass of split sequences */
 #define PA_KERNEL_RESHAPE_AND_CACHE 2
 #define PA_KERNEL_COPY_BLOCKS 3
-#define PA_KERNEL_DECODE_PLAN 4     /* work list of pa_paged_attention_decode */
+#define PA_KERNEL_DECODE_PLAN 4     /* work list of pa_paged_attention_decode (in
+                                       pa_decode_step: with the token writes) */
 #define PA_KERNEL_TRANSFER_BLOCKS 5 /* pa_transfer_blocks */
 #define PA_KERNEL_PREFILL 6         /* pa_paged_attention_prefill */
 #define PA_NUM_KERNEL_KINDS 7

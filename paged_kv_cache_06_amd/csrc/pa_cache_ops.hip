@@ -12,44 +12,15 @@
 // [blocks][Hkv][D/X][16][X]); V is stored transposed per block
 // ([blocks][Hkv][D][16]) so that the decode kernel can feed the 16 token
 // values of one dimension straight into the matrix cores.
-#include "pa_common.h"
+#include "pa_cache_write.h"
 
 namespace pa {
 namespace {
 
 // One thread per (token, head, 16-byte chunk of D).
 template <typename E>
-__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
-    const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ k_cache,
-    E* __restrict__ v_cache, const int64_t* __restrict__ slots, int32_t num_tokens,
-    int64_t num_slots, int32_t hkv, int32_t head_dim) {
-  constexpr int X = 16 / sizeof(E);
-  const int chunks = head_dim / X;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(num_tokens) * hkv * chunks;
-  if (gid >= total) return;
-  const int c = static_cast<int>(gid % chunks);
-  const int64_t th = gid / chunks;  // token * hkv + head
-  const int h = static_cast<int>(th % hkv);
-  const int64_t t = th / hkv;
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t b = slot / kBlock;
-  const int r = static_cast<int>(slot % kBlock);
-  const int64_t src = th * head_dim + static_cast<int64_t>(c) * X;
-  const int64_t head_base = (b * hkv + h) * static_cast<int64_t>(head_dim) * kBlock;
-
-  const uint4 kv = *reinterpret_cast<const uint4*>(key + src);
-  *reinterpret_cast<uint4*>(k_cache + head_base + (static_cast<int64_t>(c) * kBlock + r) * X) = kv;
-
-  union {
-    uint4 v;
-    E e[X];
-  } vv;
-  vv.v = *reinterpret_cast<const uint4*>(value + src);
-  E* vdst = v_cache + head_base + static_cast<int64_t>(c) * X * kBlock + r;
-#pragma unroll
-  for (int i = 0; i < X; ++i) vdst[i * kBlock] = vv.e[i];
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs<E> w) {
+  write_token_chunk<E>(w, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
 }
 
 // INT8 cache ("KV Cache for the intermediate", section "KV Cache
@@ -199,15 +170,13 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * kBlock;
   const int slot = timing_start(PA_KERNEL_RESHAPE_AND_CACHE, st);
   if (dtype == PA_F32) {
-    reshape_and_cache_kernel<float><<<dim3(grid), dim3(256), 0, st>>>(
-        static_cast<const float*>(key), static_cast<const float*>(value),
-        static_cast<float*>(k_cache), static_cast<float*>(v_cache), slot_mapping, num_tokens,
-        num_slots, num_kv_heads, head_dim);
+    reshape_and_cache_kernel<float><<<dim3(grid), dim3(256), 0, st>>>(cache_write_args<float>(
+        key, value, k_cache, v_cache, slot_mapping, num_tokens, num_slots, num_kv_heads,
+        head_dim));
   } else {
     reshape_and_cache_kernel<uint16_t><<<dim3(grid), dim3(256), 0, st>>>(
-        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
-        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), slot_mapping,
-        num_tokens, num_slots, num_kv_heads, head_dim);
+        cache_write_args<uint16_t>(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                   num_slots, num_kv_heads, head_dim));
   }
   const pa_status s = launch_status();
   timing_stop(slot, st);

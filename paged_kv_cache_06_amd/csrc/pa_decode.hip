@@ -48,6 +48,7 @@
 // same online softmax and the same partial-result format.
 #include "pa_decode_balanced.h"
 #include "pa_decode_int8.h"
+#include "pa_cache_write.h"
 #include "pa_decode_common.h"
 namespace pa {
 namespace {
@@ -88,9 +89,10 @@ __device__ __forceinline__ int plan_parts(const PlanArgs& a, int len) {
 // The item list, largest first (see the file header).  One work-group; each
 // thread takes a run of consecutive sequences, so one exclusive scan of its
 // per-class counts places every item, in sequence order within a class.
-__global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
-  constexpr int kVals = kClasses + 2;  // classes, full partitions, split sequences
-  __shared__ int wave_tot[kWaves * kVals];
+constexpr int kPlanVals = kClasses + 2;  // classes, full partitions, split sequences
+
+__device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
+  constexpr int kVals = kPlanVals;
   const int S = a.num_seqs;
   const int per = (S + kThreads - 1) / kThreads;
   const int i0 = threadIdx.x * per;
@@ -140,6 +142,25 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
     a.meta[0] = total;
     a.meta[1] = all[kClasses + 1];
   }
+}
+
+__global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
+  __shared__ int wave_tot[kWaves * kPlanVals];
+  plan_body(a, wave_tot);
+}
+
+// One decode step in fewer launches: work-group 0 builds the plan while the
+// others write the step's new tokens into the cache (both only read their
+// inputs, so they can run side by side); the decode kernels follow on the
+// stream.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void decode_prep_kernel(PlanArgs a, CacheWriteArgs<E> w) {
+  __shared__ int wave_tot[kWaves * kPlanVals];
+  if (blockIdx.x == 0) {
+    plan_body(a, wave_tot);
+    return;
+  }
+  write_token_chunk<E>(w, static_cast<int64_t>(blockIdx.x - 1) * kThreads + threadIdx.x);
 }
 
 // Work-group i serves item i / heads of the plan (heads = KV heads x query
@@ -490,7 +511,8 @@ template <typename Tag>
 pa_status launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
                  const int32_t* lens, float scale_log2, void* out, int num_seqs, int hq, int hkv,
                  int head_dim, int max_blocks, const Split& sp, char* ws, bool use_mfma,
-                 hipStream_t st, const float* k_scale = nullptr, const float* v_scale = nullptr) {
+                 hipStream_t st, const float* k_scale = nullptr, const float* v_scale = nullptr,
+                 const CacheWriteArgs<typename Tag::Bits>* write = nullptr) {
   using E = typename Tag::Bits;
   const int group = hq / hkv;
   const int head_blocks = use_mfma ? (group + 15) / 16 : 1;
@@ -506,11 +528,22 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   float* ws_acc = reinterpret_cast<float*>(ws + lay.acc);
   if (use_mfma || sp.np > 1) {
     PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np};
-    const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);
-    decode_plan_kernel<<<dim3(1), dim3(kThreads), 0, st>>>(pa);
-    const pa_status ps = launch_status();
-    timing_stop(pslot, st);
-    if (ps != PA_OK) return ps;
+    if (write) {  // the step's cache writes ride along with the plan
+      const int64_t chunks =
+          static_cast<int64_t>(write->num_tokens) * write->hkv * (write->head_dim * sizeof(E) / 16);
+      const int64_t wgs = 1 + (chunks + kThreads - 1) / kThreads;
+      const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);
+      decode_prep_kernel<E><<<dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), 0, st>>>(pa, *write);
+      const pa_status ps = launch_status();
+      timing_stop(pslot, st);
+      if (ps != PA_OK) return ps;
+    } else {
+      const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);
+      decode_plan_kernel<<<dim3(1), dim3(kThreads), 0, st>>>(pa);
+      const pa_status ps = launch_status();
+      timing_stop(pslot, st);
+      if (ps != PA_OK) return ps;
+    }
   }
   int slot = timing_start(PA_KERNEL_DECODE, st);
   pa_status status = PA_OK;
@@ -620,14 +653,26 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return fixed;
 }
 
-pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
-                                    const int32_t* block_tables, const int32_t* context_lens,
-                                    float scale, void* out, int32_t num_seqs,
-                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                    int32_t max_blocks_per_seq, int32_t max_context_len,
-                                    int32_t partition_size, void* workspace,
-                                    size_t workspace_bytes, pa_dtype dtype, void* stream) {
-  using namespace pa;
+}  // extern "C"
+
+namespace pa {
+namespace {
+
+// The new tokens of a fused decode step (pa_decode_step); key == nullptr: none.
+struct StepWrite {
+  const void* key;
+  const void* value;
+  const int64_t* slots;
+  int32_t num_tokens;
+  int32_t num_blocks;
+};
+
+pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      pa_dtype dtype, void* stream, const StepWrite& wr) {
   if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0)
@@ -663,24 +708,85 @@ pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const vo
   char* ws = static_cast<char*>(workspace);
   const float scale_log2 = scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool fused = wr.key != nullptr && wr.num_tokens > 0 && use_mfma && !balanced;
+  if (wr.key != nullptr && wr.num_tokens > 0 && !fused) {  // write first, then decode
+    const pa_status ws_st =
+        pa_reshape_and_cache(wr.key, wr.value, const_cast<void*>(k_cache),
+                             const_cast<void*>(v_cache), wr.slots, wr.num_tokens, wr.num_blocks,
+                             num_kv_heads, head_dim, dtype, stream);
+    if (ws_st != PA_OK) return ws_st;
+  }
   if (balanced)
     return launch_balanced_split(dtype, q, k_cache, v_cache, block_tables, context_lens,
                                  scale_log2, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                  max_blocks_per_seq, ranges, ws, st);
+  const int64_t num_slots = static_cast<int64_t>(wr.num_blocks) * kBlock;
   switch (dtype) {
-    case PA_BF16:
+    case PA_BF16: {
+      const auto w = cache_write_args<uint16_t>(wr.key, wr.value, const_cast<void*>(k_cache),
+                                                const_cast<void*>(v_cache), wr.slots,
+                                                wr.num_tokens, num_slots, num_kv_heads, head_dim);
       return launch<BF16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                            num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
-                           ws, use_mfma, st);
-    case PA_F16:
+                           ws, use_mfma, st, nullptr, nullptr, fused ? &w : nullptr);
+    }
+    case PA_F16: {
+      const auto w = cache_write_args<uint16_t>(wr.key, wr.value, const_cast<void*>(k_cache),
+                                                const_cast<void*>(v_cache), wr.slots,
+                                                wr.num_tokens, num_slots, num_kv_heads, head_dim);
       return launch<F16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
-                          ws, use_mfma, st);
+                          ws, use_mfma, st, nullptr, nullptr, fused ? &w : nullptr);
+    }
     default:
       return launch<F32T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
                           ws, false, st);
   }
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    float scale, void* out, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  return pa::decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                         num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                         max_context_len, partition_size, workspace, workspace_bytes, dtype,
+                         stream, pa::StepWrite{nullptr, nullptr, nullptr, 0, 0});
+}
+
+pa_status pa_decode_step(const void* key, const void* value, const int64_t* slot_mapping,
+                         int32_t num_new_tokens, int32_t num_blocks, const void* q, void* k_cache,
+                         void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes,
+                         pa_dtype dtype, void* stream) {
+  using namespace pa;
+  // the write's own checks, as pa_reshape_and_cache makes them
+  if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_new_tokens < 0 || num_blocks <= 0 || head_dim % (16 / elem_bytes(dtype)) != 0 ||
+      head_dim > 512)
+    return PA_ERR_INVALID_ARG;
+  if (num_new_tokens > 0 && (!key || !value || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  if ((static_cast<int64_t>(num_new_tokens) * num_kv_heads * head_dim + 255) / 256 > 0x7fffffff)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0)  // nothing to attend: only the write
+    return pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_new_tokens,
+                                num_blocks, num_kv_heads, head_dim, dtype, stream);
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, max_context_len,
+                     partition_size, workspace, workspace_bytes, dtype, stream,
+                     StepWrite{key, value, slot_mapping, num_new_tokens, num_blocks});
 }
 
 }  // extern "C"

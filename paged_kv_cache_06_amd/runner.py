@@ -19,7 +19,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import (BLOCK_SIZE, PARTITION_AUTO, BlockManager, Pool, copy_blocks, new_kv_cache,
+from . import (BLOCK_SIZE, PARTITION_AUTO, BlockManager, Pool, copy_blocks, decode_step,
+               new_kv_cache,
                new_kv_cache_int8, paged_attention_decode, paged_attention_decode_int8,
                paged_attention_prefill, reshape_and_cache, reshape_and_cache_int8)
 
@@ -186,10 +187,23 @@ class DeviceBatch:
             for ph in self.dev_phases[:2]:
                 self._apply(ph, cache)
 
-    def step(self, copy: int = 0, partition_size: int = PARTITION_AUTO, out=None):
+    def step(self, copy: int = 0, partition_size: int = PARTITION_AUTO, out=None,
+             fused: bool = True):
+        """The step: block copies (if any), then the new tokens' cache writes and
+        the decode -- through decode_step (one launch fewer) unless ``fused``
+        is False or the cache is INT8."""
         cache = self.caches[copy]
-        self._apply(self.dev_phases[2], cache)
-        self.decode(copy, partition_size, out)
+        ph = self.dev_phases[2]
+        if not fused or self.int8 or ph["slots"].shape[0] == 0:
+            self._apply(ph, cache)
+            self.decode(copy, partition_size, out)
+            return
+        kc, vc = cache
+        if ph["pairs"].shape[0]:
+            copy_blocks(kc, vc, ph["pairs"])
+        decode_step(ph["key"], ph["value"], ph["slots"], self.q, kc, vc, self.tables,
+                    self.context_lens, self.w.scale, self.out if out is None else out,
+                    max_context_len=self.max_context_len, partition_size=partition_size)
 
     def decode(self, copy: int = 0, partition_size: int = PARTITION_AUTO, out=None):
         kc, vc = self.caches[copy]

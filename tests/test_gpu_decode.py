@@ -261,3 +261,31 @@ def test_full_size_shared_prefix_through_cache_is_bit_identical_to_forks():
     assert not np.array_equal(db2.bm.rows, db.bm.rows)
     assert db2.bm.pool.stats()["prefix_hits"] == 64 * 3 * 128
     assert np.array_equal(db2.out_bits(), base)
+
+
+@pytest.mark.parametrize("dtype,d,partition_size", [("bf16", 128, pa.PARTITION_AUTO),
+                                                    ("f16", 64, 64),
+                                                    ("bf16", 128, pa.PARTITION_NONE),
+                                                    ("bf16", 128, pa.PARTITION_BALANCED),
+                                                    ("f32", 64, pa.PARTITION_AUTO)])
+def test_fused_step_equals_write_then_decode(dtype, d, partition_size):
+    """decode_step (token writes in the plan's launch where it can) against
+    reshape_and_cache followed by paged_attention_decode: same cache bits,
+    same outputs, bit for bit."""
+    import torch
+    print(f"[gpu] fused step {dtype} D={d} P={partition_size}", flush=True)
+    w = workloads.make_custom([1, 5, 20, 2, 3, 40, 700, 9], hq=8, hkv=2, d=d, dtype=dtype,
+                              seed=31, prompt_lens=[21, 32, 45],
+                              prompt_of=[0, 0, 0, 1, 1, 1, 2, 2])
+    a = runner.DeviceBatch(w)
+    b = runner.DeviceBatch(w)
+    for db, fused in ((a, True), (b, False)):
+        db.prefill()
+        db.step(partition_size=partition_size, fused=fused)
+    torch.cuda.synchronize()
+    for x, y in zip(a.caches[0], b.caches[0]):
+        assert torch.equal(x.view(torch.int16) if x.element_size() == 2 else x.view(torch.int32),
+                           y.view(torch.int16) if y.element_size() == 2 else y.view(torch.int32))
+    assert np.array_equal(a.out_bits(), b.out_bits())
+    _, _, _, ref = step.run(w, NAN_BITS[dtype])
+    assert_close(a.out_bits(), ref, dtype, "fused step")
