@@ -250,7 +250,8 @@ pa_status pa_transfer_blocks(const void* src_k, const void* src_v, int32_t src_n
  * Fixed partitions (NONE or a positive size): the work list of the call (16
  * bytes per sequence and partition, rounded up to 32 entries, and 4 per
  * sequence) plus, when some sequence is split, the partial results
- * (4 * (2 + head_dim) bytes per sequence, query head and partition).
+ * (4 * (2 + head_dim) bytes per sequence, query head and partition) and
+ * 4 bytes per sequence and query head (arrival counts of the in-kernel merge).
  * PA_PARTITION_BALANCED: 16 bytes per range start (one more than ranges) and
  * two partial slots per range of min(16, num_q_heads) rows, rounded up to a
  * power of two, of 4 * (2 + head_dim) bytes each; ranges = 2048, or

@@ -59,6 +59,10 @@ namespace {
 // sequence).  Classes 0..5 are sixths of a partition, largest first; class 6
 // holds slivers below 1/64 of a partition.
 constexpr int kClasses = 8;
+#ifndef PA_FUSED_MERGE
+#define PA_FUSED_MERGE 1
+#endif
+constexpr bool kFusedMerge = PA_FUSED_MERGE != 0;
 __device__ __forceinline__ int size_class(int tokens, int part_size) {
   if (tokens <= 0) return kClasses - 1;
   if (tokens * 64 < part_size) return kClasses - 2;
@@ -77,6 +81,8 @@ struct PlanArgs {
   int* split;   // [num_seqs] sequences with more than one partition, then -1
   int* meta;    // [0] items, [1] split sequences
   int num_seqs, max_blocks, part_size, np_max;
+  int* arrivals;     // per (sequence, head group): partials stored so far (zeroed here)
+  int num_arrivals;
 };
 
 __device__ __forceinline__ int plan_len(const PlanArgs& a, int i) {
@@ -142,6 +148,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
     a.meta[0] = total;
     a.meta[1] = all[kClasses + 1];
   }
+  for (int i = threadIdx.x; i < a.num_arrivals; i += kThreads) a.arrivals[i] = 0;
 }
 
 __global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
@@ -161,6 +168,54 @@ __global__ __launch_bounds__(kThreads) void decode_prep_kernel(PlanArgs a, Cache
     return;
   }
   write_token_chunk<E>(w, static_cast<int64_t>(blockIdx.x - 1) * kThreads + threadIdx.x);
+}
+
+// Merge of a split sequence's partials by the last of its work-groups to
+// finish (running maximum / log-sum-exp rule, as decode_reduce_kernel): each
+// work-group publishes its partial at device scope and counts itself in;
+// the one that completes the count reads every partial back and writes the
+// output rows, so no second launch is needed.
+//
+// Partials are written and read with device-scope (relaxed) atomic stores
+// and loads, which go to and come from the device-coherent level instead of
+// the XCD's L2, and every store has completed (s_waitcnt) before the
+// arrival count moves; so no L2-wide write-back or invalidation is needed
+// (device-scope fences, which do both, made the kernel twice as slow).
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename Tag, int D, int W>
+__device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int s, int gh, int nparts,
+                                              size_t row0, int nh) {
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+  __syncthreads();                 // ... and every thread's
+  if (threadIdx.x == 0) {
+    const int heads = a.hkv * a.head_blocks;
+    s_last = __hip_atomic_fetch_add(a.arrivals + static_cast<size_t>(s) * heads + gh, 1,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  for (int e = threadIdx.x; e < nh * D; e += W * kWave) {
+    const int h = e / D, d = e % D;
+    const size_t row = row0 + h;
+    const float* ml = a.ws_ml + row * a.np_max * 2;
+    const float* acc = a.ws_acc + row * a.np_max * D + d;
+    float M = -INFINITY;
+    for (int i = 0; i < nparts; ++i) M = fmaxf(M, fetch(ml + 2 * i));
+    float L = 0.f, A = 0.f;
+    for (int i = 0; i < nparts; ++i) {
+      const float wgt = fast_exp2(fetch(ml + 2 * i) - M);
+      L = fmaf(wgt, fetch(ml + 2 * i + 1), L);
+      A = fmaf(wgt, fetch(acc + static_cast<size_t>(i) * D), A);
+    }
+    a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
+  }
 }
 
 // Work-group i serves item i / heads of the plan (heads = KV heads x query
@@ -207,13 +262,22 @@ __global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_ke
       a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
     } else {
       const size_t part = row * a.np_max + p;
-      a.ws_acc[part * D + d] = A;
-      if (d == 0) {
-        a.ws_ml[2 * part] = M;
-        a.ws_ml[2 * part + 1] = L;
+      if (a.arrivals) {  // merged in-kernel: stored where every XCD sees them
+        publish(a.ws_acc + part * D + d, A);
+        if (d == 0) {
+          publish(a.ws_ml + 2 * part, M);
+          publish(a.ws_ml + 2 * part + 1, L);
+        }
+      } else {
+        a.ws_acc[part * D + d] = A;
+        if (d == 0) {
+          a.ws_ml[2 * part] = M;
+          a.ws_ml[2 * part + 1] = L;
+        }
       }
     }
   }
+  if (nparts > 1 && a.arrivals) merge_if_last<Tag, D, W>(a, s, gh, nparts, row0, nh);
 }
 
 // decode_items_kernel over an INT8 cache (same items, partitions and
@@ -259,13 +323,22 @@ __global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_i8
       a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
     } else {
       const size_t part = row * a.np_max + p;
-      a.ws_acc[part * D + d] = A;
-      if (d == 0) {
-        a.ws_ml[2 * part] = M;
-        a.ws_ml[2 * part + 1] = L;
+      if (a.arrivals) {  // merged in-kernel: stored where every XCD sees them
+        publish(a.ws_acc + part * D + d, A);
+        if (d == 0) {
+          publish(a.ws_ml + 2 * part, M);
+          publish(a.ws_ml + 2 * part + 1, L);
+        }
+      } else {
+        a.ws_acc[part * D + d] = A;
+        if (d == 0) {
+          a.ws_ml[2 * part] = M;
+          a.ws_ml[2 * part + 1] = L;
+        }
       }
     }
   }
+  if (nparts > 1 && a.arrivals) merge_if_last<Tag, D, W>(a, s, gh, nparts, row0, nh);
 }
 
 // ---- generic VALU path ----
@@ -499,10 +572,12 @@ Layout workspace_layout(int num_seqs, int hq, int head_dim, const Split& sp) {
   l.ml = l.split + align_up(static_cast<size_t>(num_seqs) * sizeof(int));
   l.acc = l.ml;
   l.total = l.ml;
+  l.arrivals = l.total;
   if (sp.np > 1) {
     const size_t parts = static_cast<size_t>(num_seqs) * sp.np * hq;
     l.acc = l.ml + align_up(parts * 2 * sizeof(float));
-    l.total = l.acc + align_up(parts * head_dim * sizeof(float));
+    l.arrivals = l.acc + align_up(parts * head_dim * sizeof(float));
+    l.total = l.arrivals + align_up(static_cast<size_t>(num_seqs) * hq * sizeof(int));
   }
   return l;
 }
@@ -526,8 +601,12 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   int* split = reinterpret_cast<int*>(ws + lay.split);
   float* ws_ml = reinterpret_cast<float*>(ws + lay.ml);
   float* ws_acc = reinterpret_cast<float*>(ws + lay.acc);
+  // the matrix-core kernels merge split sequences themselves (merge_if_last)
+  const bool fused_merge = use_mfma && sp.np > 1 && kFusedMerge;
+  int* arrivals = fused_merge ? reinterpret_cast<int*>(ws + lay.arrivals) : nullptr;
   if (use_mfma || sp.np > 1) {
-    PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np};
+    PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np, arrivals,
+                fused_merge ? num_seqs * hq : 0};
     if (write) {  // the step's cache writes ride along with the plan
       const int64_t chunks =
           static_cast<int64_t>(write->num_tokens) * write->hkv * (write->head_dim * sizeof(E) / 16);
@@ -553,6 +632,7 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
                                     num_seqs, hq, hkv, max_blocks, sp, ws_ml, ws_acc);
       a.k_scale = k_scale;
       a.v_scale = v_scale;
+      a.arrivals = arrivals;
       const size_t lds = comb_floats(kItemWaves, a.nh_max, head_dim) * sizeof(float);
       const dim3 g3(static_cast<uint32_t>(grid)), b3(kItemThreads);
       if (k_scale) {  // INT8 cache
@@ -575,7 +655,7 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
     status = launch_status();
   }
   timing_stop(slot, st);
-  if (status != PA_OK || sp.np <= 1) return status;
+  if (status != PA_OK || sp.np <= 1 || fused_merge) return status;
   slot = timing_start(PA_KERNEL_DECODE_REDUCE, st);
   const int rows = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(num_seqs) * hq, 2048));
   decode_reduce_kernel<Tag><<<dim3(rows), dim3(kThreads), 0, st>>>(

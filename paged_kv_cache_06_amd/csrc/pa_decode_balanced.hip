@@ -669,6 +669,7 @@ Layout balanced_layout(int hq, int head_dim, int64_t ranges) {
   l.ml = l.items + align_up(static_cast<size_t>(ranges + 1) * sizeof(int4));
   l.acc = l.ml + align_up(rows * 2 * sizeof(float));
   l.total = l.acc + align_up(rows * head_dim * sizeof(float));
+  l.arrivals = l.total;  // unused by the balanced split
   return l;
 }
 

@@ -104,6 +104,7 @@ struct DecodeArgs {
   float* ws_acc;
   const float* k_scale;  // INT8 cache only: [Hkv][D] per-channel scales
   const float* v_scale;
+  int* arrivals;         // split sequences merged in-kernel: [S][heads] counters, else null
   float scale_log2;
   int num_seqs, hq_total, hkv, group, head_blocks, max_blocks, part_size, np_max;
   int nh_max;  // query heads of the largest head group (<= 16): LDS rows per wave
@@ -374,7 +375,7 @@ struct Split {
 
 // Byte offsets of a decode workspace's areas.
 struct Layout {
-  size_t meta, items, split, ml, acc, total;
+  size_t meta, items, split, ml, acc, arrivals, total;
 };
 
 inline bool mfma_path(pa_dtype dt, int head_dim) {
@@ -398,6 +399,7 @@ DecodeArgs mfma_args(const void* q, const void* k_cache, const void* v_cache,
   a.ws_acc = ws_acc;
   a.k_scale = nullptr;
   a.v_scale = nullptr;
+  a.arrivals = nullptr;
   a.scale_log2 = scale_log2;
   a.num_seqs = num_seqs;
   a.hq_total = hq;

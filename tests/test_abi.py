@@ -110,7 +110,8 @@ def test_host_only_calls_and_argument_errors_without_a_gpu():
 def test_workspace_size_closed_form():
     # fixed partitions: plan (256-byte meta, 16 B per list entry -- sequences x
     # partitions rounded up to 32 entries -- and 4 B per sequence), then m, l
-    # and acc of every (sequence, query head, partition), each 256-B aligned
+    # and acc of every (sequence, query head, partition) and a 4-B counter per
+    # (sequence, query head), each 256-B aligned
     def up(x):
         return -(-x // 256) * 256
 
@@ -119,7 +120,9 @@ def test_workspace_size_closed_form():
     s, hq, d, np_ = 4, 8, 128, 4
     plan = 256 + up(16 * entries(s * np_)) + up(4 * s)
     parts = s * hq * np_
-    assert pa.decode_workspace_bytes(s, hq, d, 1024, 256) == plan + up(8 * parts) + up(4 * d * parts)
+    arrivals = up(4 * s * hq)  # one counter per (sequence, query head) for the in-kernel merge
+    assert (pa.decode_workspace_bytes(s, hq, d, 1024, 256)
+            == plan + up(8 * parts) + up(4 * d * parts) + arrivals)
     fixed_none = 256 + up(16 * entries(s)) + up(4 * s)
     assert pa.decode_workspace_bytes(s, hq, d, 1024, pa.PARTITION_NONE) == fixed_none
     assert pa.decode_workspace_bytes(s, hq, d, 256, 256) == fixed_none
