@@ -395,6 +395,21 @@ pa_status pa_decode_step(const void* key, const void* value, const int64_t* slot
                          int32_t partition_size, void* workspace, size_t workspace_bytes,
                          pa_dtype dtype, void* stream);
 
+/* One decode step over an INT8 cache: pa_reshape_and_cache_int8 of the new
+ * tokens followed by pa_paged_attention_decode_int8 (arguments as there),
+ * the token writes running in the launch that builds the decode's work list.
+ * Same results as the two calls; every argument is checked before anything
+ * is launched (num_seqs = 0: only the write). */
+pa_status pa_decode_step_int8(const void* key, const void* value, const int64_t* slot_mapping,
+                              int32_t num_new_tokens, int32_t num_blocks, const void* q,
+                              void* k_cache, void* v_cache, const float* k_scale,
+                              const float* v_scale, const int32_t* block_tables,
+                              const int32_t* context_lens, float scale, void* out,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, int32_t partition_size, void* workspace,
+                              size_t workspace_bytes, pa_dtype dtype, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Kernel timing.  Between pa_timing_begin and pa_timing_end every kernel the
  * library launches is bracketed by HIP events on its own stream.

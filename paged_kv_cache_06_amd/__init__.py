@@ -27,7 +27,7 @@ __all__ = [
     "paged_attention_decode", "decode_workspace_bytes", "decode_auto_partition",
     "decode_set_max_groups", "reshape_and_cache_int8", "paged_attention_decode_int8",
     "swap_blocks", "transfer_blocks", "new_host_kv_cache", "paged_attention_prefill",
-    "decode_step",
+    "decode_step", "decode_step_int8",
     "new_kv_cache", "new_kv_cache_int8", "logical_view", "timing_begin", "timing_end", "status_string",
 ]
 
@@ -94,6 +94,9 @@ _SIGNATURES = {
     "pa_decode_step": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p,
                                 _c_f, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                 _c_i32, _c_p, _c_sz, _c_i32, _c_p]),
+    "pa_decode_step_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p,
+                                     _c_p, _c_p, _c_p, _c_f, _c_p, _c_i32, _c_i32, _c_i32,
+                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_sz, _c_i32, _c_p]),
     "pa_timing_begin": (_c_i32, [_c_i32]),
     "pa_timing_end": (_c_i32, [ctypes.POINTER(ctypes.c_double), _P_I32]),
 }
@@ -592,6 +595,40 @@ def _workspace(q, s, hq, d, mcl, partition_size, workspace):
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return ws_ptr, ws_bytes
+
+
+def decode_step_int8(key, value, slot_mapping, q, k_cache, v_cache, k_scale, v_scale,
+                     block_tables, context_lens, scale, out, *, max_context_len: int | None = None,
+                     partition_size: int = PARTITION_AUTO, workspace=None) -> None:
+    """reshape_and_cache_int8 then paged_attention_decode_int8 in fewer launches."""
+    torch = _torch()
+    _need(k_cache.dtype == torch.int8, "INT8 caches expected")
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    t = key.shape[0]
+    _need(tuple(key.shape) == (t, hkv, d) and tuple(value.shape) == (t, hkv, d),
+          "key/value must be [T, Hkv, D]")
+    _need(key.is_contiguous() and value.is_contiguous(), "key/value must be contiguous")
+    _need(key.dtype == value.dtype == q.dtype, "key/value/q dtypes differ")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == t,
+          "slot_mapping must be int64 [T]")
+    s, hq, dq = q.shape
+    _need(dq == d and tuple(out.shape) == (s, hq, d), "q/out must be [S, Hq, D]")
+    _need(q.is_contiguous() and out.is_contiguous() and q.dtype == out.dtype,
+          "q/out must be contiguous, of one dtype")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == s and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == s,
+          "context_lens must be int32 [S]")
+    mb = block_tables.shape[1]
+    mcl = mb * BLOCK_SIZE if max_context_len is None else int(max_context_len)
+    ws_ptr, ws_bytes = _workspace(q, s, hq, d, mcl, partition_size, workspace)
+    _check(load().pa_decode_step_int8(
+        _ptr(key), _ptr(value), _ptr(slot_mapping.contiguous()), t, nb, _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), _scales(k_scale, hkv, d, "k_scale"), _scales(v_scale, hkv, d, "v_scale"),
+        _ptr(block_tables), _ptr(context_lens.contiguous()), float(scale), _ptr(out), s, hq, hkv,
+        d, mb, mcl, int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q)),
+        "pa_decode_step_int8")
 
 
 def paged_attention_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_tables,

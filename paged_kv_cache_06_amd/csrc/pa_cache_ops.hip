@@ -23,48 +23,10 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs<E
   write_token_chunk<E>(w, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
 }
 
-// INT8 cache ("KV Cache for the intermediate", section "KV Cache
-// Quantization"): one thread per (token, head, 16-dimension chunk c).  Codes
-// are clamp(rint(x / s), -127, 127) in fp32 (NaN -> 0); the 16 K codes of a
-// chunk are one 16-byte store, the 16 V codes land 16 bytes apart (the V
-// layout groups 4 tokens of 4 dimension slices per lane of the decode).
+// INT8 cache: one thread per (token, head, 16-dimension chunk).
 template <typename Tag>
-__global__ __launch_bounds__(256) void reshape_and_cache_i8_kernel(
-    const typename Tag::Bits* __restrict__ key, const typename Tag::Bits* __restrict__ value,
-    int8_t* __restrict__ k_cache, int8_t* __restrict__ v_cache, const int64_t* __restrict__ slots,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int32_t num_tokens,
-    int64_t num_slots, int32_t hkv, int32_t head_dim) {
-  const int chunks = head_dim / 16;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(num_tokens) * hkv * chunks;
-  if (gid >= total) return;
-  const int c = static_cast<int>(gid % chunks);
-  const int64_t th = gid / chunks;  // token * hkv + head
-  const int h = static_cast<int>(th % hkv);
-  const int64_t t = th / hkv;
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t b = slot / kBlock;
-  const int r = static_cast<int>(slot % kBlock);
-  const int64_t src = th * head_dim + static_cast<int64_t>(c) * 16;
-  const float* ks = k_scale + static_cast<int64_t>(h) * head_dim + c * 16;
-  const float* vs = v_scale + static_cast<int64_t>(h) * head_dim + c * 16;
-  const int64_t slab = (b * hkv + h) * static_cast<int64_t>(head_dim) * kBlock + (c / 4) * 1024;
-
-  auto code = [](float x, float s) {
-    float y = rintf(__fdiv_rn(x, s));
-    y = (y != y) ? 0.f : fminf(fmaxf(y, -127.f), 127.f);
-    return static_cast<uint32_t>(static_cast<int32_t>(y)) & 0xFFu;
-  };
-  uint32_t kw[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int e = 0; e < 16; ++e) kw[e / 4] |= code(Tag::to_f32(key[src + e]), ks[e]) << (8 * (e % 4));
-  *reinterpret_cast<uint4*>(k_cache + slab + ((c % 4) * 16 + r) * 16) =
-      make_uint4(kw[0], kw[1], kw[2], kw[3]);
-  int8_t* vdst = v_cache + slab + ((r / 4) * 16) * 16 + (c % 4) * 4 + r % 4;
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    vdst[e * 16] = static_cast<int8_t>(code(Tag::to_f32(value[src + e]), vs[e]));
+__global__ __launch_bounds__(256) void reshape_and_cache_i8_kernel(CacheWriteI8Args<Tag> w) {
+  w.write(static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
 }
 
 // grid.x = pair * 2 + (0: K, 1: V); grid.y splits the block's bytes.
@@ -206,17 +168,17 @@ pa_status pa_reshape_and_cache_int8(const void* key, const void* value, void* k_
   const int slot = timing_start(PA_KERNEL_RESHAPE_AND_CACHE, st);
   const dim3 g(static_cast<uint32_t>(grid)), b(256);
   if (dtype == PA_F32)
-    reshape_and_cache_i8_kernel<F32T><<<g, b, 0, st>>>(
+    reshape_and_cache_i8_kernel<F32T><<<g, b, 0, st>>>(CacheWriteI8Args<F32T>{
         static_cast<const float*>(key), static_cast<const float*>(value), kc, vc, slot_mapping,
-        k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim);
+        k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim});
   else if (dtype == PA_BF16)
-    reshape_and_cache_i8_kernel<BF16T><<<g, b, 0, st>>>(
+    reshape_and_cache_i8_kernel<BF16T><<<g, b, 0, st>>>(CacheWriteI8Args<BF16T>{
         static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), kc, vc,
-        slot_mapping, k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim);
+        slot_mapping, k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim});
   else
-    reshape_and_cache_i8_kernel<F16T><<<g, b, 0, st>>>(
+    reshape_and_cache_i8_kernel<F16T><<<g, b, 0, st>>>(CacheWriteI8Args<F16T>{
         static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), kc, vc,
-        slot_mapping, k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim);
+        slot_mapping, k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim});
   const pa_status s = launch_status();
   timing_stop(slot, st);
   return s;

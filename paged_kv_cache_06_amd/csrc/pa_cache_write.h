@@ -21,6 +21,10 @@ struct CacheWriteArgs {
   int32_t num_tokens;
   int64_t num_slots;
   int32_t hkv, head_dim;
+  __host__ __device__ int64_t threads() const {
+    return static_cast<int64_t>(num_tokens) * hkv * (head_dim * static_cast<int>(sizeof(E)) / 16);
+  }
+  __device__ void write(int64_t gid) const;
 };
 
 template <typename E>
@@ -65,6 +69,67 @@ __device__ __forceinline__ void write_token_chunk(const CacheWriteArgs<E>& w, in
   E* vdst = w.v_cache + head_base + static_cast<int64_t>(c) * X * kBlock + r;
 #pragma unroll
   for (int i = 0; i < X; ++i) vdst[i * kBlock] = vv.e[i];
+}
+
+template <typename E>
+__device__ __forceinline__ void CacheWriteArgs<E>::write(int64_t gid) const {
+  write_token_chunk<E>(*this, gid);
+}
+
+// ---- INT8 cache ("KV Cache for the intermediate", section "KV Cache
+// Quantization") ----
+
+template <typename Tag>
+struct CacheWriteI8Args {
+  const typename Tag::Bits* key;  // [T][Hkv][D]
+  const typename Tag::Bits* value;
+  int8_t* k_cache;                // INT8 layout of include/pa.h
+  int8_t* v_cache;
+  const int64_t* slots;
+  const float* k_scale;           // [Hkv][D]
+  const float* v_scale;
+  int32_t num_tokens;
+  int64_t num_slots;
+  int32_t hkv, head_dim;
+  __host__ __device__ int64_t threads() const { return static_cast<int64_t>(num_tokens) * hkv * (head_dim / 16); }
+  __device__ void write(int64_t gid) const;
+};
+
+// Thread gid quantizes one 16-dimension chunk of one (token, head): codes
+// clamp(rint(x / s), -127, 127) in fp32 (NaN -> 0); the 16 K codes are one
+// 16-byte store, the 16 V codes land 16 bytes apart (the V layout groups 4
+// tokens of 4 dimension slices per lane of the decode).
+template <typename Tag>
+__device__ __forceinline__ void CacheWriteI8Args<Tag>::write(int64_t gid) const {
+  const int chunks = head_dim / 16;
+  if (gid >= threads()) return;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t th = gid / chunks;  // token * hkv + head
+  const int h = static_cast<int>(th % hkv);
+  const int64_t t = th / hkv;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t b = slot / kBlock;
+  const int r = static_cast<int>(slot % kBlock);
+  const int64_t src = th * head_dim + static_cast<int64_t>(c) * 16;
+  const float* ks = k_scale + static_cast<int64_t>(h) * head_dim + c * 16;
+  const float* vs = v_scale + static_cast<int64_t>(h) * head_dim + c * 16;
+  const int64_t slab = (b * hkv + h) * static_cast<int64_t>(head_dim) * kBlock + (c / 4) * 1024;
+
+  auto code = [](float x, float s) {
+    float y = rintf(__fdiv_rn(x, s));
+    y = (y != y) ? 0.f : fminf(fmaxf(y, -127.f), 127.f);
+    return static_cast<uint32_t>(static_cast<int32_t>(y)) & 0xFFu;
+  };
+  uint32_t kw[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) kw[e / 4] |= code(Tag::to_f32(key[src + e]), ks[e]) << (8 * (e % 4));
+  *reinterpret_cast<uint4*>(k_cache + slab + ((c % 4) * 16 + r) * 16) =
+      make_uint4(kw[0], kw[1], kw[2], kw[3]);
+  int8_t* vdst = v_cache + slab + ((r / 4) * 16) * 16 + (c % 4) * 4 + r % 4;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    vdst[e * 16] = static_cast<int8_t>(code(Tag::to_f32(value[src + e]), vs[e]));
 }
 
 }  // namespace

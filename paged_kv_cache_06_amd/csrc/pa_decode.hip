@@ -160,14 +160,14 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
 // others write the step's new tokens into the cache (both only read their
 // inputs, so they can run side by side); the decode kernels follow on the
 // stream.
-template <typename E>
-__global__ __launch_bounds__(kThreads) void decode_prep_kernel(PlanArgs a, CacheWriteArgs<E> w) {
+template <typename W>
+__global__ __launch_bounds__(kThreads) void decode_prep_kernel(PlanArgs a, W w) {
   __shared__ int wave_tot[kWaves * kPlanVals];
   if (blockIdx.x == 0) {
     plan_body(a, wave_tot);
     return;
   }
-  write_token_chunk<E>(w, static_cast<int64_t>(blockIdx.x - 1) * kThreads + threadIdx.x);
+  w.write(static_cast<int64_t>(blockIdx.x - 1) * kThreads + threadIdx.x);
 }
 
 // Merge of a split sequence's partials by the last of its work-groups to
@@ -582,12 +582,12 @@ Layout workspace_layout(int num_seqs, int hq, int head_dim, const Split& sp) {
   return l;
 }
 
-template <typename Tag>
+template <typename Tag, typename W = CacheWriteArgs<typename Tag::Bits>>
 pa_status launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* tables,
                  const int32_t* lens, float scale_log2, void* out, int num_seqs, int hq, int hkv,
                  int head_dim, int max_blocks, const Split& sp, char* ws, bool use_mfma,
                  hipStream_t st, const float* k_scale = nullptr, const float* v_scale = nullptr,
-                 const CacheWriteArgs<typename Tag::Bits>* write = nullptr) {
+                 const W* write = nullptr) {
   using E = typename Tag::Bits;
   const int group = hq / hkv;
   const int head_blocks = use_mfma ? (group + 15) / 16 : 1;
@@ -608,11 +608,9 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
     PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np, arrivals,
                 fused_merge ? num_seqs * hq : 0};
     if (write) {  // the step's cache writes ride along with the plan
-      const int64_t chunks =
-          static_cast<int64_t>(write->num_tokens) * write->hkv * (write->head_dim * sizeof(E) / 16);
-      const int64_t wgs = 1 + (chunks + kThreads - 1) / kThreads;
+      const int64_t wgs = 1 + (write->threads() + kThreads - 1) / kThreads;
       const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);
-      decode_prep_kernel<E><<<dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), 0, st>>>(pa, *write);
+      decode_prep_kernel<W><<<dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), 0, st>>>(pa, *write);
       const pa_status ps = launch_status();
       timing_stop(pslot, st);
       if (ps != PA_OK) return ps;
@@ -669,47 +667,6 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
 }  // namespace pa
 
 extern "C" {
-
-pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, const void* v_cache,
-                                         const float* k_scale, const float* v_scale,
-                                         const int32_t* block_tables,
-                                         const int32_t* context_lens, float scale, void* out,
-                                         int32_t num_seqs, int32_t num_q_heads,
-                                         int32_t num_kv_heads, int32_t head_dim,
-                                         int32_t max_blocks_per_seq, int32_t max_context_len,
-                                         int32_t partition_size, void* workspace,
-                                         size_t workspace_bytes, pa_dtype dtype, void* stream) {
-  using namespace pa;
-  if (dtype != PA_BF16 && dtype != PA_F16) return PA_ERR_UNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (partition_size == PA_PARTITION_BALANCED) return PA_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
-      max_context_len < 0)
-    return PA_ERR_INVALID_ARG;
-  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
-    return PA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
-  if (num_seqs == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !context_lens || !out)
-    return PA_ERR_INVALID_ARG;
-  Split sp;
-  if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp, 1))
-    return PA_ERR_INVALID_ARG;
-  const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
-  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
-    return PA_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  const float scale_log2 = scale * kLog2e;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == PA_BF16)
-    return launch<BF16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
-                         num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
-                         ws, true, st, k_scale, v_scale);
-  return launch<F16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out, num_seqs,
-                      num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp, ws, true, st,
-                      k_scale, v_scale);
-}
 
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype) {
@@ -825,6 +782,56 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   }
 }
 
+pa_status decode_int8_impl(const void* q, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           pa_dtype dtype, void* stream, const StepWrite& wr) {
+  if (dtype != PA_BF16 && dtype != PA_F16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (partition_size == PA_PARTITION_BALANCED) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
+    return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !context_lens || !out)
+    return PA_ERR_INVALID_ARG;
+  Split sp;
+  if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp, 1))
+    return PA_ERR_INVALID_ARG;
+  const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return PA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const float scale_log2 = scale * kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool fused = wr.key != nullptr && wr.num_tokens > 0;
+  const int64_t num_slots = static_cast<int64_t>(wr.num_blocks) * kBlock;
+  int8_t* kc = static_cast<int8_t*>(const_cast<void*>(k_cache));
+  int8_t* vc = static_cast<int8_t*>(const_cast<void*>(v_cache));
+  if (dtype == PA_BF16) {
+    const CacheWriteI8Args<BF16T> w{static_cast<const uint16_t*>(wr.key),
+                                    static_cast<const uint16_t*>(wr.value), kc, vc, wr.slots,
+                                    k_scale, v_scale, wr.num_tokens, num_slots, num_kv_heads,
+                                    head_dim};
+    return launch<BF16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
+                         ws, true, st, k_scale, v_scale, fused ? &w : nullptr);
+  }
+  const CacheWriteI8Args<F16T> w{static_cast<const uint16_t*>(wr.key),
+                                 static_cast<const uint16_t*>(wr.value), kc, vc, wr.slots, k_scale,
+                                 v_scale, wr.num_tokens, num_slots, num_kv_heads, head_dim};
+  return launch<F16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out, num_seqs,
+                      num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp, ws, true, st,
+                      k_scale, v_scale, fused ? &w : nullptr);
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -867,6 +874,48 @@ pa_status pa_decode_step(const void* key, const void* value, const int64_t* slot
                      num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, max_context_len,
                      partition_size, workspace, workspace_bytes, dtype, stream,
                      StepWrite{key, value, slot_mapping, num_new_tokens, num_blocks});
+}
+
+pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, const void* v_cache,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_tables,
+                                         const int32_t* context_lens, float scale, void* out,
+                                         int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         int32_t partition_size, void* workspace,
+                                         size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  return pa::decode_int8_impl(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                              scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              max_blocks_per_seq, max_context_len, partition_size, workspace,
+                              workspace_bytes, dtype, stream,
+                              pa::StepWrite{nullptr, nullptr, nullptr, 0, 0});
+}
+
+pa_status pa_decode_step_int8(const void* key, const void* value, const int64_t* slot_mapping,
+                              int32_t num_new_tokens, int32_t num_blocks, const void* q,
+                              void* k_cache, void* v_cache, const float* k_scale,
+                              const float* v_scale, const int32_t* block_tables,
+                              const int32_t* context_lens, float scale, void* out,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, int32_t partition_size, void* workspace,
+                              size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  using namespace pa;
+  if (num_new_tokens < 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (num_new_tokens > 0 && (!key || !value || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  if ((static_cast<int64_t>(num_new_tokens) * num_kv_heads * head_dim / 16 + 255) / 256 >
+      0x7fffffff)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0)  // nothing to attend: only the write
+    return pa_reshape_and_cache_int8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale,
+                                     num_new_tokens, num_blocks, num_kv_heads, head_dim, dtype,
+                                     stream);
+  return decode_int8_impl(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                          scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          max_blocks_per_seq, max_context_len, partition_size, workspace,
+                          workspace_bytes, dtype, stream,
+                          StepWrite{key, value, slot_mapping, num_new_tokens, num_blocks});
 }
 
 }  // extern "C"

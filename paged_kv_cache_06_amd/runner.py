@@ -20,7 +20,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import (BLOCK_SIZE, PARTITION_AUTO, BlockManager, Pool, copy_blocks, decode_step,
-               new_kv_cache,
+               decode_step_int8, new_kv_cache,
                new_kv_cache_int8, paged_attention_decode, paged_attention_decode_int8,
                paged_attention_prefill, reshape_and_cache, reshape_and_cache_int8)
 
@@ -190,20 +190,26 @@ class DeviceBatch:
     def step(self, copy: int = 0, partition_size: int = PARTITION_AUTO, out=None,
              fused: bool = True):
         """The step: block copies (if any), then the new tokens' cache writes and
-        the decode -- through decode_step (one launch fewer) unless ``fused``
-        is False or the cache is INT8."""
+        the decode -- through decode_step / decode_step_int8 (one launch fewer)
+        unless ``fused`` is False."""
         cache = self.caches[copy]
         ph = self.dev_phases[2]
-        if not fused or self.int8 or ph["slots"].shape[0] == 0:
+        if not fused or ph["slots"].shape[0] == 0:
             self._apply(ph, cache)
             self.decode(copy, partition_size, out)
             return
         kc, vc = cache
         if ph["pairs"].shape[0]:
             copy_blocks(kc, vc, ph["pairs"])
+        o = self.out if out is None else out
+        if self.int8:
+            decode_step_int8(ph["key"], ph["value"], ph["slots"], self.q, kc, vc, self.k_scale,
+                             self.v_scale, self.tables, self.context_lens, self.w.scale, o,
+                             max_context_len=self.max_context_len, partition_size=partition_size)
+            return
         decode_step(ph["key"], ph["value"], ph["slots"], self.q, kc, vc, self.tables,
-                    self.context_lens, self.w.scale, self.out if out is None else out,
-                    max_context_len=self.max_context_len, partition_size=partition_size)
+                    self.context_lens, self.w.scale, o, max_context_len=self.max_context_len,
+                    partition_size=partition_size)
 
     def decode(self, copy: int = 0, partition_size: int = PARTITION_AUTO, out=None):
         kc, vc = self.caches[copy]

@@ -165,3 +165,23 @@ def test_full_size_split_equals_unsplit_and_is_deterministic():
         c = to_f64(bits_of(out2), w.dtype)
         ratio = np.abs(c - b) / (ulp * np.abs(b) + 1e-5)
         assert ratio.max() <= 1.0, f"partition {ps}: {ratio.max():.2f} ulp"
+
+
+@pytest.mark.parametrize("partition_size", [pa.PARTITION_AUTO, pa.PARTITION_NONE, 64])
+def test_fused_step_equals_write_then_decode(partition_size):
+    import torch
+    print(f"[gpu] int8 fused step P={partition_size}", flush=True)
+    w = workloads.make_custom([1, 5, 20, 2, 3, 40, 700, 9], hq=8, hkv=2, d=128, dtype="bf16",
+                              seed=33, prompt_lens=[21, 32, 45],
+                              prompt_of=[0, 0, 0, 1, 1, 1, 2, 2])
+    a = runner.DeviceBatch(w, int8=True)
+    b = runner.DeviceBatch(w, int8=True)
+    for db, fused in ((a, True), (b, False)):
+        db.prefill()
+        db.step(partition_size=partition_size, fused=fused)
+    torch.cuda.synchronize()
+    for x, y in zip(a.caches[0], b.caches[0]):
+        assert torch.equal(x, y)
+    assert np.array_equal(a.out_bits(), b.out_bits())
+    _, _, _, ref = step.run_int8(w)
+    assert_close(a.out_bits(), ref, "bf16", "int8 fused step")
