@@ -109,21 +109,30 @@ __device__ __forceinline__ void read_block<64>(uint32_t ka, uint32_t va, BlockRe
 // maximum is raised only when a score exceeds it by more than 2^8 (the
 // weights then stay below 2^8, which fp32 sums and bf16/fp16 weights hold),
 // so that the accumulator is rescaled on few blocks instead of on every one.
+// `masked`: some position of the block may lie past a column's limit (the
+// caller knows when none can, and the comparisons are skipped).  The cross-
+// lane maximum is only formed when some lane's own scores outgrow the
+// running maximum by the slack; otherwise the block needs no exchange.
 template <typename Tag, int D>
 __device__ __forceinline__ void prefill_update(uint2* vf, f32x4_t sc, float sl2, int blk, int len,
-                                               int lim, WaveState<D>& st) {
+                                               int lim, bool masked, WaveState<D>& st) {
   constexpr int kSlices = D / 16;
   constexpr float kSlack = 8.f;  // log2 units
   const int lane = threadIdx.x & (kWave - 1);
   const int kg = lane >> 4;
   const int pos0 = blk * kBlock + kg * 4;
   float s4[4];
+  if (masked) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s4[i] = (pos0 + i < lim) ? sc[i] * sl2 : -INFINITY;
-  float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  if (__builtin_amdgcn_ballot_w64(mx > st.m + kSlack) != 0) {  // some column outgrew its max
+    for (int i = 0; i < 4; ++i) s4[i] = (pos0 + i < lim) ? sc[i] * sl2 : -INFINITY;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[i] = sc[i] * sl2;
+  }
+  const float own = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+  if (__builtin_amdgcn_ballot_w64(own > st.m + kSlack) != 0) {  // some column outgrew its max
+    float mx = fmaxf(own, __shfl_xor(own, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(st.m, mx);
     const float alpha = fast_exp2(st.m - m_new);
     st.l *= alpha;
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
   const int nh = min(a.cols_heads, a.group - h_base);
   const int ci = n / a.cols_heads, ch = n % a.cols_heads;
   // tile t of this wave: queries i0[t] .. i0[t] + nq[t] - 1
-  int i0[T], col_pos[T];
+  int i0[T], col_pos[T], first_pos[T];
   bool col_ok[T];
   int wave_last = 0;
 #pragma unroll
@@ -191,9 +200,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
     i0[t] = i_wg + (wave * T + t) * a.qpw;
     const int nq = max(0, min(a.qpw, nchunk - i0[t]));
     col_ok[t] = ci < nq && ch < nh;
-    const int first_pos = len - nchunk + i0[t];
-    col_pos[t] = nq > 0 ? first_pos + (col_ok[t] ? ci : nq - 1) : 0;
-    if (nq > 0) wave_last = first_pos + nq - 1;
+    first_pos[t] = nq > 0 ? len - nchunk + i0[t] : 0;
+    col_pos[t] = nq > 0 ? first_pos[t] + (col_ok[t] ? ci : nq - 1) : 0;
+    if (nq > 0) wave_last = first_pos[t] + nq - 1;
   }
   const int wg_last = len - nchunk + min(nchunk, i_wg + runs_per_wg * a.qpw) - 1;
   const int nblk = wg_last / kBlock + 1;     // blocks the work-group walks
@@ -260,7 +269,10 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
           f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int k = 0; k < D / 32; ++k) sc = Mfma<Tag>::qk(rb.kf[k], qf[t][k], sc);
-          prefill_update<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos[t] + 1, st[t]);
+          // every position of the block is at or before the tile's first query
+          const bool masked = (blk + 1) * kBlock > first_pos[t] + 1;
+          prefill_update<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos[t] + 1, masked,
+                                 st[t]);
         }
       }
     }
