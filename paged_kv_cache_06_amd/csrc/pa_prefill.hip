@@ -51,7 +51,14 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 constexpr int kPrefillWaves = 4;
-constexpr int kPrefillDepth = 4;  // K/V blocks in flight per work-group
+#ifndef PA_PREFILL_ROUND
+#define PA_PREFILL_ROUND 1
+#endif
+// blocks per barrier (2 measured 4 % slower on MI355X: fewer barriers, but
+// the waves then wait on longer rounds) and LDS stages: a round in use and
+// at least two blocks loading
+constexpr int kPrefillRound = PA_PREFILL_ROUND;
+constexpr int kPrefillDepth = kPrefillRound == 1 ? 4 : 3 * kPrefillRound;
 #ifndef PA_PREFILL_TILES
 #define PA_PREFILL_TILES 2
 #endif
@@ -250,29 +257,35 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
                                                  16, lane * 16 + byte, 0, 0, 0);
       }
     };
+    // rounds of kPrefillRound blocks: one wait and one barrier per round
+    constexpr int R = kPrefillRound;
 #pragma unroll
-    for (int j = 0; j < kPrefillDepth - 1; ++j) issue(j);
-    for (int j = 0; j < cn; ++j) {
-      wait_vm<(kPrefillDepth - 2) * kChunksPerWave>();  // this wave's part of block j is in
+    for (int j = 0; j < kPrefillDepth - R; ++j) issue(j);
+    for (int j = 0; j < cn; j += R) {
+      wait_vm<(kPrefillDepth - 2 * R) * kChunksPerWave>();  // this wave's part of the round
       // ... and every other wave's: a bare barrier (a fenced one would wait for
       // every load in flight); the loads are counted in by the waits, and LDS
       // reads of earlier rounds end with their own wait
       __builtin_amdgcn_s_barrier();
-      issue(j + kPrefillDepth - 1);                      // into the stage read last round
-      const int blk = c0 + j;
-      if (blk < my_blk) {
-        const char* stg = ring + (j % kPrefillDepth) * kStage;
-        BlockRegs<D> rb;
-        read_block<D>(lds_addr(stg) + lane * 16, lds_addr(stg + D * kBlock * 2) + va_lane, rb);
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < R; ++i) issue(j + kPrefillDepth - R + i);  // stages read last round
 #pragma unroll
-          for (int k = 0; k < D / 32; ++k) sc = Mfma<Tag>::qk(rb.kf[k], qf[t][k], sc);
-          // every position of the block is at or before the tile's first query
-          const bool masked = (blk + 1) * kBlock > first_pos[t] + 1;
-          prefill_update<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos[t] + 1, masked,
-                                 st[t]);
+      for (int i = 0; i < R; ++i) {
+        const int blk = c0 + j + i;
+        if (j + i < cn && blk < my_blk) {
+          const char* stg = ring + ((j + i) % kPrefillDepth) * kStage;
+          BlockRegs<D> rb;
+          read_block<D>(lds_addr(stg) + lane * 16, lds_addr(stg + D * kBlock * 2) + va_lane, rb);
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < D / 32; ++k) sc = Mfma<Tag>::qk(rb.kf[k], qf[t][k], sc);
+            // every position of the block is at or before the tile's first query
+            const bool masked = (blk + 1) * kBlock > first_pos[t] + 1;
+            prefill_update<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos[t] + 1, masked,
+                                   st[t]);
+          }
         }
       }
     }
