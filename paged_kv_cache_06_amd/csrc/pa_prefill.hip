@@ -5,17 +5,18 @@
 // cache?").  The chunk's K/V are in the cache before the call, as for decode,
 // so one token per sequence is exactly decode.
 //
-// One wave per run of consecutive chunk queries of one (sequence, KV head,
+// A tile is a run of consecutive chunk queries of one (sequence, KV head,
 // group of up to 16 query heads); the 16 columns of its matrix-core products
-// are (query, head) pairs, query-major: with G query heads per
-// KV head (G <= 16) a wave serves 16 / G queries of that KV head at once, so
-// every K/V block it loads is multiplied against 16 query rows.  Per 16-token
-// block, as in decode:
+// are (query, head) pairs, query-major: with G query heads per KV head
+// (G <= 16) a tile holds 16 / G queries of that KV head, so every K/V block
+// is multiplied against 16 query rows at once.  Per 16-token block and tile:
 //   scores[16 tok x 16 cols] = K . Q^T          (MFMA 16x16x32, K as A)
 //   online softmax per column, masked causally: token t counts for the column
 //   of the query at position p iff t <= p
 //   acc^T[D x 16 cols] += V^T . P^T             (MFMA 16x16x16)
-// Units are ordered so that the queries with the most positions start first.
+// A work-group (4 waves x 2 tiles each) walks the K/V blocks its 8 tiles
+// need through an LDS ring that every block enters once (prefill_kernel);
+// work-groups with the latest queries (the most positions) start first.
 #include "pa_decode_common.h"
 
 namespace pa {
