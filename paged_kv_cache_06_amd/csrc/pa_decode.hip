@@ -10,9 +10,11 @@
 //
 // Work items: (sequence, partition of P positions, KV head, group of up to 16
 // query heads).  Sequences longer than P are cut into partitions whose partial
-// results (running max m, sum l, unnormalised acc) are merged by a second
-// kernel with the running-max rule (Milakov and Gimelshein 2018); a sequence
-// with one partition is normalised and written directly.  A work-group of 4
+// results (running max m, sum l, unnormalised acc) are merged with the
+// running-max rule (Milakov and Gimelshein 2018) -- on the matrix-core path by
+// the last of a sequence's work-groups to finish (merge_if_last), on the VALU
+// path by a second kernel; a sequence with one partition is normalised and
+// written directly.  A work-group of 4
 // waves serves one item: the waves take the item's 16-token blocks
 // round-robin and merge their partials through LDS at the end.
 //
@@ -24,7 +26,9 @@
 // that list, so the hardware dispatcher hands out big items first and the
 // last ones to start are the smallest: a short tail with no atomics and no
 // idle work-groups besides the trailing ones past the list's end, which exit
-// at once.  The merge kernel walks only the split sequences.
+// at once.  The VALU path's merge kernel walks only the split sequences.
+// pa_decode_step builds the list in the same launch as it writes the step's
+// new tokens into the cache (decode_prep_kernel).
 //
 // Matrix-core path (bf16/fp16, head_dim 64 or 128), per 16-token block:
 //   scores[16 tok x 16 heads] = K[16 tok x D] . Q^T[D x 16 heads]
