@@ -64,6 +64,10 @@ constexpr int kPrefillDepth = kPrefillRound == 1 ? 4 : 3 * kPrefillRound;
 #define PA_PREFILL_TILES 2
 #endif
 constexpr int kPrefillTiles = PA_PREFILL_TILES;  // 16-column tiles per wave
+#ifndef PA_PREFILL_32
+#define PA_PREFILL_32 1
+#endif
+constexpr bool kPrefill32 = PA_PREFILL_32 != 0;  // 32-column tiles (prefill32_kernel)
 
 // One block's MFMA operands from an LDS stage (K: 16 bytes per lane per
 // k-step, 1 KiB apart; V: 8 bytes per lane per slice, 512 bytes apart), in one
@@ -310,9 +314,298 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
   }
 }
 
+// ---- 32-column tiles ----
+//
+// The same computation on v_mfma_f32_32x32x16: a wave's tile is 32 (query,
+// head) columns and a round is 32 positions (two blocks), so each lane holds
+// 16 scores of one column and the per-score vector work (scale, mask, running
+// maximum, exponential, sum, packing) is amortised over twice the products.
+//   QK: rows = the round's 32 tokens (A = K, lane l: token l%32, 8 dims of
+//       k-step st from chunk 2*st + l/32), columns = the tile (B = Q^T);
+//       lane l then holds column l%32, tokens 8j + 4(l/32) + i (j, i < 4);
+//   PV: per block b and 32-dimension slice dt, A = V^T (lane l: dimension
+//       dt*32 + l%32, the block's tokens 4(l/32)..+3 and 8 + 4(l/32)..+3, 8
+//       bytes each in the transposed V rows) and B = P^T (lane l: column l%32,
+//       its 8 scores of block b, in the same token order).
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <typename Tag>
+struct Mfma32;
+
+template <>
+struct Mfma32<BF16T> {
+  __device__ static f32x16_t mma(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma32<F16T> {
+  __device__ static f32x16_t mma(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+// K operands of one round (D / 16 k-steps, 512 bytes apart) from LDS, one
+// block of reads ending with its wait.
+template <int D>
+__device__ __forceinline__ void read_k32(uint32_t ka, uint4* kf);
+
+template <>
+__device__ __forceinline__ void read_k32<128>(uint32_t ka, uint4* kf) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %8 offset:512\n"
+      "ds_read_b128 %2, %8 offset:1024\n"
+      "ds_read_b128 %3, %8 offset:1536\n"
+      "ds_read_b128 %4, %8 offset:2048\n"
+      "ds_read_b128 %5, %8 offset:2560\n"
+      "ds_read_b128 %6, %8 offset:3072\n"
+      "ds_read_b128 %7, %8 offset:3584\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]),
+        "=&v"(kf[6]), "=&v"(kf[7])
+      : "v"(ka)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_k32<64>(uint32_t ka, uint4* kf) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %4 offset:512\n"
+      "ds_read_b128 %2, %4 offset:1024\n"
+      "ds_read_b128 %3, %4 offset:1536\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3])
+      : "v"(ka)
+      : "memory");
+}
+
+// V operands of one block (D / 32 slices, 1 KiB apart; two 8-byte pieces 16
+// bytes apart each), one block of reads ending with its wait.
+template <int D>
+__device__ __forceinline__ void read_v32(uint32_t va, uint4* vf);
+
+template <>
+__device__ __forceinline__ void read_v32<128>(uint32_t va, uint4* vf) {
+  uint2 x[8];
+  asm volatile(
+      "ds_read_b64 %0, %8\n"
+      "ds_read_b64 %1, %8 offset:16\n"
+      "ds_read_b64 %2, %8 offset:1024\n"
+      "ds_read_b64 %3, %8 offset:1040\n"
+      "ds_read_b64 %4, %8 offset:2048\n"
+      "ds_read_b64 %5, %8 offset:2064\n"
+      "ds_read_b64 %6, %8 offset:3072\n"
+      "ds_read_b64 %7, %8 offset:3088\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+        "=&v"(x[6]), "=&v"(x[7])
+      : "v"(va)
+      : "memory");
+#pragma unroll
+  for (int d = 0; d < 4; ++d) vf[d] = make_uint4(x[2 * d].x, x[2 * d].y, x[2 * d + 1].x, x[2 * d + 1].y);
+}
+
+template <>
+__device__ __forceinline__ void read_v32<64>(uint32_t va, uint4* vf) {
+  uint2 x[4];
+  asm volatile(
+      "ds_read_b64 %0, %4\n"
+      "ds_read_b64 %1, %4 offset:16\n"
+      "ds_read_b64 %2, %4 offset:1024\n"
+      "ds_read_b64 %3, %4 offset:1040\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(va)
+      : "memory");
+#pragma unroll
+  for (int d = 0; d < 2; ++d) vf[d] = make_uint4(x[2 * d].x, x[2 * d].y, x[2 * d + 1].x, x[2 * d + 1].y);
+}
+
+template <typename Tag>
+__device__ __forceinline__ uint4 pack8(const float* p) {
+  const uint2 lo = Mfma<Tag>::pack(p[0], p[1], p[2], p[3]);
+  const uint2 hi = Mfma<Tag>::pack(p[4], p[5], p[6], p[7]);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+constexpr int kPrefill32Depth = 3;  // rounds (pairs of blocks) in the LDS ring
+
+template <typename Tag, int D>
+__global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill32_kernel(PrefillArgs a) {
+  constexpr int kBlk = D * kBlock * 2;      // K (or V) of one block-head
+  constexpr int kStage = 4 * kBlk;          // [K b0][K b1][V b0][V b1]
+  constexpr int kChunks = kBlk / 1024;      // 1 KiB loads per block part = per wave
+  constexpr int kSteps = D / 16;            // QK k-steps
+  constexpr int kSlices = D / 32;           // PV dimension slices
+  constexpr float kSlack = 8.f;             // log2 units
+  extern __shared__ char ring[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane & 31, h = lane >> 5;
+  const int per_run = a.num_seqs * a.hkv * a.head_blocks;
+  const int u = blockIdx.x;
+  const int run_groups = (a.groups_max + kPrefillWaves - 1) / kPrefillWaves;
+  const int rg = run_groups - 1 - u / per_run;
+  const int r = u % per_run;
+  const int s = r / (a.hkv * a.head_blocks);
+  const int g = (r / a.head_blocks) % a.hkv;
+  const int hb = r % a.head_blocks;
+  const int q0 = uniform_load(a.qstart, s), q1 = uniform_load(a.qstart, s + 1);
+  const int len = min(max(uniform_load(a.lens, s), q1 - q0), a.max_blocks * kBlock);
+  const int nchunk = min(q1 - q0, len);
+  const int i_wg = rg * kPrefillWaves * a.qpw;
+  if (i_wg >= nchunk) return;  // uniform over the work-group
+  const int i0 = i_wg + wave * a.qpw;
+  const int nq = max(0, min(a.qpw, nchunk - i0));
+  const int h_base = hb * 32;
+  const int nh = min(a.cols_heads, a.group - h_base);
+  const int ci = c / a.cols_heads, ch = c % a.cols_heads;
+  const bool col_ok = ci < nq && ch < nh;
+  const int first_pos = nq > 0 ? len - nchunk + i0 : 0;
+  const int col_pos = nq > 0 ? first_pos + (col_ok ? ci : nq - 1) : 0;
+  const int wave_last = nq > 0 ? first_pos + nq - 1 : 0;
+  const int wg_last = len - nchunk + min(nchunk, i_wg + kPrefillWaves * a.qpw) - 1;
+  const int nblk = wg_last / kBlock + 1;
+  const int my_rounds = nq > 0 ? wave_last / (2 * kBlock) + 1 : 0;
+
+  uint4 qf[kSteps];
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) qf[st] = make_uint4(0, 0, 0, 0);
+  if (col_ok) {
+    const size_t row = static_cast<size_t>(q0 + i0 + ci) * a.hq + g * a.group + h_base + ch;
+    const uint4* qrow = reinterpret_cast<const uint4*>(a.q + row * D);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) qf[st] = qrow[2 * st + h];
+  }
+  float m = -INFINITY, l = 0.f;
+  f32x16_t acc[kSlices];
+#pragma unroll
+  for (int dt = 0; dt < kSlices; ++dt) acc[dt] = f32x16_t{};
+
+  const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
+  const uint32_t k_lane = ((c >> 4) * kBlk) + ((h * 16 + (c & 15)) * 16);
+  const uint32_t v_lane = 2 * kBlk + ((c * kBlock + 4 * h) * 2);
+  for (int c0 = 0; c0 < nblk; c0 += 64) {
+    const int cn = min(64, nblk - c0);
+    const int ids = load_ids<1>(trow, c0, cn);
+    // wave w moves part w of round j: K of its first block, K of its second,
+    // V of its first, V of its second; blocks past the chunk read nothing
+    auto issue = [&](int j) {
+      const int b = 2 * j + (wave & 1);
+      const bool real = b < cn;
+      const int phys = __builtin_amdgcn_readlane(ids, real ? b : 0);
+      const size_t off = (static_cast<size_t>(phys) * a.hkv + g) * (D * kBlock);
+      const auto rsrc = buffer_of((wave < 2 ? a.k_cache : a.v_cache) + off, real ? kBlk : 0u);
+      char* dst = ring + (j % kPrefill32Depth) * kStage + wave * kBlk;
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t)(dst + q * 1024), 16,
+                                                 lane * 16 + q * 1024, 0, 0, 0);
+    };
+    const int rounds = (cn + 1) / 2;
+#pragma unroll
+    for (int j = 0; j < kPrefill32Depth - 1; ++j) issue(j);
+    for (int j = 0; j < rounds; ++j) {
+      wait_vm<(kPrefill32Depth - 2) * kChunks>();  // this wave's part of round j is in
+      __builtin_amdgcn_s_barrier();                // ... and every other wave's (bare: see above)
+      issue(j + kPrefill32Depth - 1);               // into the stage read last round
+      const int round = c0 / 2 + j;                 // rounds from the sequence start
+      if (round < my_rounds) {
+        const char* stg = ring + (j % kPrefill32Depth) * kStage;
+        uint4 kf[kSteps];
+        read_k32<D>(lds_addr(stg) + k_lane, kf);
+        f32x16_t sc = f32x16_t{};
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) sc = Mfma32<Tag>::mma(kf[st], qf[st], sc);
+        const int base = round * 2 * kBlock;  // position of the round's first token
+        float p[16];
+        if (base + 2 * kBlock - 1 > first_pos) {  // some position may pass a column's limit
+#pragma unroll
+          for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int pos = base + 8 * j4 + 4 * h + i;
+              p[4 * j4 + i] = pos <= col_pos ? sc[4 * j4 + i] * a.scale_log2 : -INFINITY;
+            }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) p[e] = sc[e] * a.scale_log2;
+        }
+        float own = p[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) own = fmaxf(own, p[e]);
+        if (__builtin_amdgcn_ballot_w64(own > m + kSlack) != 0) {
+          const float m_new = fmaxf(m, fmaxf(own, __shfl_xor(own, 32)));
+          const float alpha = fast_exp2(m - m_new);
+          l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < kSlices; ++dt) acc[dt] *= alpha;
+          m = m_new;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          p[e] = fast_exp2(p[e] - m);
+          l += p[e];
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          uint4 vf[kSlices];
+          read_v32<D>(lds_addr(stg) + v_lane + b * kBlk, vf);
+          const int bstart = base + b * kBlock;
+          if (bstart + kBlock > len) {  // zero V of positions past the end (stale bits)
+            const int t0 = bstart + 4 * h, t1 = bstart + 8 + 4 * h;
+            const uint32_t m0 = (t0 + 0 < len ? 0x0000FFFFu : 0u) | (t0 + 1 < len ? 0xFFFF0000u : 0u);
+            const uint32_t m1 = (t0 + 2 < len ? 0x0000FFFFu : 0u) | (t0 + 3 < len ? 0xFFFF0000u : 0u);
+            const uint32_t m2 = (t1 + 0 < len ? 0x0000FFFFu : 0u) | (t1 + 1 < len ? 0xFFFF0000u : 0u);
+            const uint32_t m3 = (t1 + 2 < len ? 0x0000FFFFu : 0u) | (t1 + 3 < len ? 0xFFFF0000u : 0u);
+#pragma unroll
+            for (int dt = 0; dt < kSlices; ++dt) {
+              vf[dt].x &= m0;
+              vf[dt].y &= m1;
+              vf[dt].z &= m2;
+              vf[dt].w &= m3;
+            }
+          }
+          const uint4 pb = pack8<Tag>(p + 8 * b);
+#pragma unroll
+          for (int dt = 0; dt < kSlices; ++dt) acc[dt] = Mfma32<Tag>::mma(vf[dt], pb, acc[dt]);
+        }
+      }
+    }
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // the next chunk's first stages may be overwritten
+  }
+  const float l_tot = l + __shfl_xor(l, 32);
+  if (!col_ok) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  uint16_t* orow = a.out + (static_cast<size_t>(q0 + i0 + ci) * a.hq + g * a.group + h_base + ch) * D;
+#pragma unroll
+  for (int dt = 0; dt < kSlices; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const f32x16_t& v = acc[dt];
+      const uint2 packed = Mfma<Tag>::pack(v[4 * j4] * inv, v[4 * j4 + 1] * inv,
+                                           v[4 * j4 + 2] * inv, v[4 * j4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * j4 + 4 * h) = packed;
+    }
+}
+
 template <typename Tag>
 pa_status launch_prefill(const PrefillArgs& a, int head_dim, int64_t units, hipStream_t st) {
   const dim3 g3(static_cast<uint32_t>(units)), b3(kPrefillWaves * kWave);
+  if (kPrefill32) {
+    const size_t lds = static_cast<size_t>(kPrefill32Depth) * 4 * head_dim * kBlock * 2;
+    if (head_dim == 128)
+      prefill32_kernel<Tag, 128><<<g3, b3, lds, st>>>(a);
+    else
+      prefill32_kernel<Tag, 64><<<g3, b3, lds, st>>>(a);
+    return launch_status();
+  }
   const size_t lds = static_cast<size_t>(kPrefillDepth) * 2 * head_dim * kBlock * 2;
   if (head_dim == 128)
     prefill_kernel<Tag, 128><<<g3, b3, lds, st>>>(a);
@@ -356,12 +649,13 @@ pa_status pa_paged_attention_prefill(const void* q, const void* k_cache, const v
   a.hq = num_q_heads;
   a.hkv = num_kv_heads;
   a.group = num_q_heads / num_kv_heads;
-  a.head_blocks = (a.group + 15) / 16;
+  const int cols = kPrefill32 ? 32 : 16;  // columns of a tile
+  a.head_blocks = (a.group + cols - 1) / cols;
   a.max_blocks = max_blocks_per_seq;
-  a.cols_heads = std::min(a.group, 16);
-  a.qpw = 16 / a.cols_heads;
+  a.cols_heads = std::min(a.group, cols);
+  a.qpw = cols / a.cols_heads;
   a.groups_max = (max_chunk_len + a.qpw - 1) / a.qpw;
-  const int runs_per_wg = kPrefillWaves * kPrefillTiles;
+  const int runs_per_wg = kPrefillWaves * (kPrefill32 ? 1 : kPrefillTiles);
   const int64_t units = static_cast<int64_t>((a.groups_max + runs_per_wg - 1) / runs_per_wg) *
                         num_seqs * num_kv_heads * a.head_blocks;
   if (units > 0x7fffffff) return PA_ERR_INVALID_ARG;
