@@ -35,6 +35,7 @@ struct PrefillArgs {
   int cols_heads;           // query heads per column group: min(G, 16)
   int qpw;                  // queries per wave: 16 / cols_heads
   int groups_max;           // query runs of the longest chunk: ceil(max_chunk / qpw)
+  int largest_first;        // order work-groups by their work (num_seqs <= kOrderMaxSeqs)
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
@@ -320,13 +321,17 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
 // head) columns and a round is 32 positions (two blocks), so each lane holds
 // 16 scores of one column and the per-score vector work (scale, mask, running
 // maximum, exponential, sum, packing) is amortised over twice the products.
-//   QK: rows = the round's 32 tokens (A = K, lane l: token l%32, 8 dims of
-//       k-step st from chunk 2*st + l/32), columns = the tile (B = Q^T);
-//       lane l then holds column l%32, tokens 8j + 4(l/32) + i (j, i < 4);
+//   QK: rows = the round's 32 tokens, columns = the tile (A = K, B = Q^T).
+//       Row r carries token pi(r), r with bits 2 and 3 swapped, so that lane
+//       l (column l%32, rows 8j + 4(l/32) + i) ends up holding, for block b,
+//       the scores of tokens 8(l/32) + e, e < 8, as elements 8b + e;
 //   PV: per block b and 32-dimension slice dt, A = V^T (lane l: dimension
-//       dt*32 + l%32, the block's tokens 4(l/32)..+3 and 8 + 4(l/32)..+3, 8
-//       bytes each in the transposed V rows) and B = P^T (lane l: column l%32,
-//       its 8 scores of block b, in the same token order).
+//       dt*32 + l%32, tokens 8(l/32)..+7: one 16-byte piece of a transposed V
+//       row) and B = P^T (lane l: column l%32, elements 8b..8b+7).
+// The V copy into LDS places the piece lane l reads at 16*l within the slice
+// (the DMA lanes gather rows' halves), so the wave's V reads are one
+// contiguous KiB per slice, as its K reads are 256 contiguous bytes per
+// 16 lanes: no bank conflicts.
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <typename Tag>
@@ -384,46 +389,33 @@ __device__ __forceinline__ void read_k32<64>(uint32_t ka, uint4* kf) {
       : "memory");
 }
 
-// V operands of one block (D / 32 slices, 1 KiB apart; two 8-byte pieces 16
-// bytes apart each), one block of reads ending with its wait.
+// V operands of one block (D / 32 slices, 1 KiB apart), one block of reads
+// ending with its wait.
 template <int D>
 __device__ __forceinline__ void read_v32(uint32_t va, uint4* vf);
 
 template <>
 __device__ __forceinline__ void read_v32<128>(uint32_t va, uint4* vf) {
-  uint2 x[8];
   asm volatile(
-      "ds_read_b64 %0, %8\n"
-      "ds_read_b64 %1, %8 offset:16\n"
-      "ds_read_b64 %2, %8 offset:1024\n"
-      "ds_read_b64 %3, %8 offset:1040\n"
-      "ds_read_b64 %4, %8 offset:2048\n"
-      "ds_read_b64 %5, %8 offset:2064\n"
-      "ds_read_b64 %6, %8 offset:3072\n"
-      "ds_read_b64 %7, %8 offset:3088\n"
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %4 offset:1024\n"
+      "ds_read_b128 %2, %4 offset:2048\n"
+      "ds_read_b128 %3, %4 offset:3072\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
-        "=&v"(x[6]), "=&v"(x[7])
+      : "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3])
       : "v"(va)
       : "memory");
-#pragma unroll
-  for (int d = 0; d < 4; ++d) vf[d] = make_uint4(x[2 * d].x, x[2 * d].y, x[2 * d + 1].x, x[2 * d + 1].y);
 }
 
 template <>
 __device__ __forceinline__ void read_v32<64>(uint32_t va, uint4* vf) {
-  uint2 x[4];
   asm volatile(
-      "ds_read_b64 %0, %4\n"
-      "ds_read_b64 %1, %4 offset:16\n"
-      "ds_read_b64 %2, %4 offset:1024\n"
-      "ds_read_b64 %3, %4 offset:1040\n"
+      "ds_read_b128 %0, %2\n"
+      "ds_read_b128 %1, %2 offset:1024\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "=&v"(vf[0]), "=&v"(vf[1])
       : "v"(va)
       : "memory");
-#pragma unroll
-  for (int d = 0; d < 2; ++d) vf[d] = make_uint4(x[2 * d].x, x[2 * d].y, x[2 * d + 1].x, x[2 * d + 1].y);
 }
 
 template <typename Tag>
@@ -431,6 +423,102 @@ __device__ __forceinline__ uint4 pack8(const float* p) {
   const uint2 lo = Mfma<Tag>::pack(p[0], p[1], p[2], p[3]);
   const uint2 hi = Mfma<Tag>::pack(p[4], p[5], p[6], p[7]);
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// ---- largest-first work-group order ----
+//
+// A work-group of the 32-column kernel covers query group rg (queries
+// rg*pw .. rg*pw + pw - 1 of its chunk, pw = 4 * qpw) of sequence s for one
+// KV head, and walks 32-position rounds up to its last query's position,
+// c_s + min(n_s, (rg + 1) * pw) - 1 (c_s = tokens before the chunk, n_s = its
+// length).  That count W(s, rg) grows with rg, so the groups of s with W >= V
+// are the top ones and their number has a closed form; summed over the
+// sequences and searched over V, it gives the pair of any rank in the order
+// of decreasing W (ties by sequence, then group).  Work-groups are
+// dispatched in index order, so handing out the longest first keeps the
+// long ones from starting last.
+constexpr int kOrderMaxSeqs = 256;   // sequences one wave ranks (4 per lane)
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
+  return x;
+}
+
+// groups rg < G of one sequence whose round count is at least V (V >= 1)
+__device__ __forceinline__ int groups_at_least(int c, int n, int G, int pw, int V) {
+  const int t = 32 * (V - 1) - c + 1;  // the group must reach min(n, (rg+1)pw) >= t
+  if (t <= 1) return G;
+  if (n < t) return 0;
+  return max(0, G - max(0, (t + pw - 1) / pw - 1));
+}
+
+// Pair (s, rg) of rank q, or false if q is past the last non-empty group.
+// Wave-uniform; every wave of the work-group computes the same answer.
+__device__ bool largest_first(const PrefillArgs& a, int q, int R, int pw, int& s_out,
+                              int& rg_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int kPer = kOrderMaxSeqs / kWave;
+  int c[kPer], n[kPer], G[kPer];
+  int total = 0, vmax = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int s = lane + k * kWave;
+    c[k] = 0, n[k] = 0, G[k] = 0;
+    if (s < a.num_seqs) {
+      const int q0 = a.qstart[s], q1 = a.qstart[s + 1];
+      const int len = min(max(a.lens[s], q1 - q0), a.max_blocks * kBlock);
+      n[k] = max(0, min(q1 - q0, len));
+      c[k] = len - n[k];
+      G[k] = min((n[k] + pw - 1) / pw, R);
+      if (G[k] > 0) vmax = max(vmax, (c[k] + n[k] - 1) / 32 + 1);
+    }
+    total += G[k];
+  }
+  total = wave_sum(total);
+  if (q >= total) return false;
+  vmax = wave_max(vmax);
+  auto count = [&](int V) {
+    int x = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) x += groups_at_least(c[k], n[k], G[k], pw, V);
+    return wave_sum(x);
+  };
+  int lo = 1, hi = vmax + 1;  // count(lo) > q >= count(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (count(mid) > q)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  int r = q - count(lo + 1);  // rank among the pairs of exactly lo rounds
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int at = groups_at_least(c[k], n[k], G[k], pw, lo);
+    const int e = at - groups_at_least(c[k], n[k], G[k], pw, lo + 1);
+    int incl = e;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > r);
+    if (hit != 0) {
+      const int f = static_cast<int>(__builtin_ctzll(hit));
+      s_out = f + k * kWave;
+      rg_out = __builtin_amdgcn_readlane(G[k] - at + r - (incl - e), f);
+      return true;
+    }
+    r -= __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
+  return false;  // not reached: the ranks below total are all covered
 }
 
 constexpr int kPrefill32Depth = 3;  // rounds (pairs of blocks) in the LDS ring
@@ -447,14 +535,20 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill32_kernel(Pre
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 31, h = lane >> 5;
-  const int per_run = a.num_seqs * a.hkv * a.head_blocks;
+  const int inner = a.hkv * a.head_blocks;  // work-groups of one (sequence, query group)
   const int u = blockIdx.x;
   const int run_groups = (a.groups_max + kPrefillWaves - 1) / kPrefillWaves;
-  const int rg = run_groups - 1 - u / per_run;
-  const int r = u % per_run;
-  const int s = r / (a.hkv * a.head_blocks);
-  const int g = (r / a.head_blocks) % a.hkv;
-  const int hb = r % a.head_blocks;
+  const int g = (u % inner) / a.head_blocks;
+  const int hb = u % a.head_blocks;
+  int s, rg;
+  if (a.largest_first) {
+    if (!largest_first(a, u / inner, run_groups, kPrefillWaves * a.qpw, s, rg)) return;
+    s = __builtin_amdgcn_readfirstlane(s);
+    rg = __builtin_amdgcn_readfirstlane(rg);
+  } else {  // later query groups (more positions) first
+    rg = run_groups - 1 - u / (a.num_seqs * inner);
+    s = (u / inner) % a.num_seqs;
+  }
   const int q0 = uniform_load(a.qstart, s), q1 = uniform_load(a.qstart, s + 1);
   const int len = min(max(uniform_load(a.lens, s), q1 - q0), a.max_blocks * kBlock);
   const int nchunk = min(q1 - q0, len);
@@ -488,8 +582,13 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill32_kernel(Pre
   for (int dt = 0; dt < kSlices; ++dt) acc[dt] = f32x16_t{};
 
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
-  const uint32_t k_lane = ((c >> 4) * kBlk) + ((h * 16 + (c & 15)) * 16);
-  const uint32_t v_lane = 2 * kBlk + ((c * kBlock + 4 * h) * 2);
+  const int tok = (c & 0x13) | ((c & 4) << 1) | ((c & 8) >> 1);  // token of row c
+  const uint32_t k_lane = ((tok >> 4) * kBlk) + ((h * 16 + (tok & 15)) * 16);
+  const uint32_t v_lane = 2 * kBlk + lane * 16;
+  // source offset of this lane's 16 bytes within a KiB: K pieces stay in
+  // place, V pieces (dimension lane%32, half lane/32) are gathered
+  const uint32_t dma_lane = wave < 2 ? lane * 16 : c * 32 + h * 16;
+  const bool pos_scale = a.scale_log2 >= 0.f;
   for (int c0 = 0; c0 < nblk; c0 += 64) {
     const int cn = min(64, nblk - c0);
     const int ids = load_ids<1>(trow, c0, cn);
@@ -505,7 +604,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill32_kernel(Pre
 #pragma unroll
       for (int q = 0; q < kChunks; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t)(dst + q * 1024), 16,
-                                                 lane * 16 + q * 1024, 0, 0, 0);
+                                                 dma_lane + q * 1024, 0, 0, 0);
     };
     const int rounds = (cn + 1) / 2;
 #pragma unroll
@@ -523,22 +622,29 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill32_kernel(Pre
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) sc = Mfma32<Tag>::mma(kf[st], qf[st], sc);
         const int base = round * 2 * kBlock;  // position of the round's first token
+        // element e of sc is the score of position base + 16(e/8) + 8h + e%8
         float p[16];
-        if (base + 2 * kBlock - 1 > first_pos) {  // some position may pass a column's limit
+        float own;
+        const bool masked = base + 2 * kBlock - 1 > first_pos;  // some position may pass a limit
+        if (masked) {
+          const int lim = col_pos - base - 8 * h;  // element e is in range if its offset <= lim
 #pragma unroll
-          for (int j4 = 0; j4 < 4; ++j4)
+          for (int e = 0; e < 16; ++e)
+            p[e] = 16 * (e >> 3) + (e & 7) <= lim ? sc[e] * a.scale_log2 : -INFINITY;
+          own = p[0];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int pos = base + 8 * j4 + 4 * h + i;
-              p[4 * j4 + i] = pos <= col_pos ? sc[4 * j4 + i] * a.scale_log2 : -INFINITY;
-            }
-        } else {
+          for (int e = 1; e < 16; ++e) own = fmaxf(own, p[e]);
+        } else {  // every position is real and in range: scale inside the exponent
+          float hi = sc[0];
+          if (pos_scale) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) p[e] = sc[e] * a.scale_log2;
+            for (int e = 1; e < 16; ++e) hi = fmaxf(hi, sc[e]);
+          } else {
+#pragma unroll
+            for (int e = 1; e < 16; ++e) hi = fminf(hi, sc[e]);
+          }
+          own = hi * a.scale_log2;
         }
-        float own = p[0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) own = fmaxf(own, p[e]);
         if (__builtin_amdgcn_ballot_w64(own > m + kSlack) != 0) {
           const float m_new = fmaxf(m, fmaxf(own, __shfl_xor(own, 32)));
           const float alpha = fast_exp2(m - m_new);
@@ -547,22 +653,25 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill32_kernel(Pre
           for (int dt = 0; dt < kSlices; ++dt) acc[dt] *= alpha;
           m = m_new;
         }
+        if (masked) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p[e] = fast_exp2(p[e] - m);
-          l += p[e];
+          for (int e = 0; e < 16; ++e) p[e] = fast_exp2(p[e] - m);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) p[e] = fast_exp2(fmaf(sc[e], a.scale_log2, -m));
         }
 #pragma unroll
+        for (int e = 0; e < 16; ++e) l += p[e];
         for (int b = 0; b < 2; ++b) {
           uint4 vf[kSlices];
           read_v32<D>(lds_addr(stg) + v_lane + b * kBlk, vf);
           const int bstart = base + b * kBlock;
           if (bstart + kBlock > len) {  // zero V of positions past the end (stale bits)
-            const int t0 = bstart + 4 * h, t1 = bstart + 8 + 4 * h;
-            const uint32_t m0 = (t0 + 0 < len ? 0x0000FFFFu : 0u) | (t0 + 1 < len ? 0xFFFF0000u : 0u);
-            const uint32_t m1 = (t0 + 2 < len ? 0x0000FFFFu : 0u) | (t0 + 3 < len ? 0xFFFF0000u : 0u);
-            const uint32_t m2 = (t1 + 0 < len ? 0x0000FFFFu : 0u) | (t1 + 1 < len ? 0xFFFF0000u : 0u);
-            const uint32_t m3 = (t1 + 2 < len ? 0x0000FFFFu : 0u) | (t1 + 3 < len ? 0xFFFF0000u : 0u);
+            const int rem = len - bstart - 8 * h;  // this lane's tokens below the end
+            const uint32_t m0 = (0 < rem ? 0x0000FFFFu : 0u) | (1 < rem ? 0xFFFF0000u : 0u);
+            const uint32_t m1 = (2 < rem ? 0x0000FFFFu : 0u) | (3 < rem ? 0xFFFF0000u : 0u);
+            const uint32_t m2 = (4 < rem ? 0x0000FFFFu : 0u) | (5 < rem ? 0xFFFF0000u : 0u);
+            const uint32_t m3 = (6 < rem ? 0x0000FFFFu : 0u) | (7 < rem ? 0xFFFF0000u : 0u);
 #pragma unroll
             for (int dt = 0; dt < kSlices; ++dt) {
               vf[dt].x &= m0;
@@ -655,6 +764,7 @@ pa_status pa_paged_attention_prefill(const void* q, const void* k_cache, const v
   a.cols_heads = std::min(a.group, cols);
   a.qpw = cols / a.cols_heads;
   a.groups_max = (max_chunk_len + a.qpw - 1) / a.qpw;
+  a.largest_first = kPrefill32 && num_seqs <= kOrderMaxSeqs;
   const int runs_per_wg = kPrefillWaves * (kPrefill32 ? 1 : kPrefillTiles);
   const int64_t units = static_cast<int64_t>((a.groups_max + runs_per_wg - 1) / runs_per_wg) *
                         num_seqs * num_kv_heads * a.head_blocks;

@@ -21,19 +21,29 @@ CASES = [
     ([19, 40], [3, 77], 4, 4, 64, "bf16"),                              # MHA, 16 queries a wave
     ([25, 9], [100, 7], 12, 4, 128, "bf16"),                            # G = 3
     ([70, 1], [0, 2000], 16, 8, 64, "f16"),                             # G = 2, whole prompt
+    # many sequences of mixed lengths: work-groups handed out longest first
+    (np.random.default_rng(5).integers(1, 70, 40).tolist(),
+     np.random.default_rng(6).integers(0, 600, 40).tolist(), 8, 2, 128, "bf16"),
+    # more sequences than the longest-first order ranks: plain order
+    (np.random.default_rng(7).integers(1, 5, 260).tolist(),
+     np.random.default_rng(8).integers(0, 100, 260).tolist(), 8, 2, 64, "bf16"),
 ]
 
 
 @pytest.mark.parametrize("chunks,cached,hq,hkv,d,dtype", CASES)
 def test_small_cases_against_oracle(chunks, cached, hq, hkv, d, dtype):
-    print(f"[gpu] prefill {chunks} after {cached} {hq}/{hkv} D={d} {dtype}", flush=True)
+    import torch
+    print(f"[gpu] prefill of {len(chunks)} chunks, {sum(chunks)} tokens, {hq}/{hkv} D={d} {dtype}",
+          flush=True)
     w = workloads.make_prefill(chunks, cached, hq=hq, hkv=hkv, d=d, dtype=dtype,
                                seed=sum(chunks) + d)
     _, _, _, ref = step.run_prefill(w, NAN_BITS[dtype])
     db = runner.DeviceBatch(w)
     db.prefill()
     db._apply(db.dev_phases[2], db.caches[0])
-    out = db.attend_chunks()
+    db.attend_chunks()  # allocates the output; then every row is written over NaN
+    out = torch.full_like(db.chunk_out, float("nan"))
+    db.attend_chunks(out=out)
     assert_close(bits_of(out), ref, dtype, f"prefill {chunks}")
 
 
