@@ -389,32 +389,54 @@ __device__ __forceinline__ void read_k32<64>(uint32_t ka, uint4* kf) {
       : "memory");
 }
 
-// V operands of one block (D / 32 slices, 1 KiB apart), one block of reads
-// ending with its wait.
+// K operands of the next round and V operands of the current one (two blocks,
+// D / 32 slices each: vf[b * D / 32 + dt]), one block of reads ending with
+// its wait.
 template <int D>
-__device__ __forceinline__ void read_v32(uint32_t va, uint4* vf);
+__device__ __forceinline__ void read_kv32(uint32_t ka, uint32_t va, uint4* kf, uint4* vf);
 
 template <>
-__device__ __forceinline__ void read_v32<128>(uint32_t va, uint4* vf) {
+__device__ __forceinline__ void read_kv32<128>(uint32_t ka, uint32_t va, uint4* kf, uint4* vf) {
   asm volatile(
-      "ds_read_b128 %0, %4\n"
-      "ds_read_b128 %1, %4 offset:1024\n"
-      "ds_read_b128 %2, %4 offset:2048\n"
-      "ds_read_b128 %3, %4 offset:3072\n"
+      "ds_read_b128 %0, %16\n"
+      "ds_read_b128 %1, %16 offset:512\n"
+      "ds_read_b128 %2, %16 offset:1024\n"
+      "ds_read_b128 %3, %16 offset:1536\n"
+      "ds_read_b128 %4, %16 offset:2048\n"
+      "ds_read_b128 %5, %16 offset:2560\n"
+      "ds_read_b128 %6, %16 offset:3072\n"
+      "ds_read_b128 %7, %16 offset:3584\n"
+      "ds_read_b128 %8, %17\n"
+      "ds_read_b128 %9, %17 offset:1024\n"
+      "ds_read_b128 %10, %17 offset:2048\n"
+      "ds_read_b128 %11, %17 offset:3072\n"
+      "ds_read_b128 %12, %17 offset:4096\n"
+      "ds_read_b128 %13, %17 offset:5120\n"
+      "ds_read_b128 %14, %17 offset:6144\n"
+      "ds_read_b128 %15, %17 offset:7168\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3])
-      : "v"(va)
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]),
+        "=&v"(kf[6]), "=&v"(kf[7]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]),
+        "=&v"(vf[4]), "=&v"(vf[5]), "=&v"(vf[6]), "=&v"(vf[7])
+      : "v"(ka), "v"(va)
       : "memory");
 }
 
 template <>
-__device__ __forceinline__ void read_v32<64>(uint32_t va, uint4* vf) {
+__device__ __forceinline__ void read_kv32<64>(uint32_t ka, uint32_t va, uint4* kf, uint4* vf) {
   asm volatile(
-      "ds_read_b128 %0, %2\n"
-      "ds_read_b128 %1, %2 offset:1024\n"
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %8 offset:512\n"
+      "ds_read_b128 %2, %8 offset:1024\n"
+      "ds_read_b128 %3, %8 offset:1536\n"
+      "ds_read_b128 %4, %9\n"
+      "ds_read_b128 %5, %9 offset:1024\n"
+      "ds_read_b128 %6, %9 offset:2048\n"
+      "ds_read_b128 %7, %9 offset:3072\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(vf[0]), "=&v"(vf[1])
-      : "v"(va)
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(vf[0]), "=&v"(vf[1]),
+        "=&v"(vf[2]), "=&v"(vf[3])
+      : "v"(ka), "v"(va)
       : "memory");
 }
 
@@ -521,10 +543,13 @@ __device__ bool largest_first(const PrefillArgs& a, int q, int R, int pw, int& s
   return false;  // not reached: the ranks below total are all covered
 }
 
-constexpr int kPrefill32Depth = 3;  // rounds (pairs of blocks) in the LDS ring
+#ifndef PA_PREFILL32_OCC
+#define PA_PREFILL32_OCC 2
+#endif
+constexpr int kPrefill32Depth = 4;  // rounds (pairs of blocks) in the LDS ring
 
 template <typename Tag, int D>
-__global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill32_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillWaves * kWave, PA_PREFILL32_OCC) void prefill32_kernel(PrefillArgs a) {
   constexpr int kBlk = D * kBlock * 2;      // K (or V) of one block-head
   constexpr int kStage = 4 * kBlk;          // [K b0][K b1][V b0][V b1]
   constexpr int kChunks = kBlk / 1024;      // 1 KiB loads per block part = per wave
@@ -589,106 +614,130 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill32_kernel(Pre
   // place, V pieces (dimension lane%32, half lane/32) are gathered
   const uint32_t dma_lane = wave < 2 ? lane * 16 : c * 32 + h * 16;
   const bool pos_scale = a.scale_log2 >= 0.f;
-  for (int c0 = 0; c0 < nblk; c0 += 64) {
-    const int cn = min(64, nblk - c0);
-    const int ids = load_ids<1>(trow, c0, cn);
-    // wave w moves part w of round j: K of its first block, K of its second,
-    // V of its first, V of its second; blocks past the chunk read nothing
-    auto issue = [&](int j) {
-      const int b = 2 * j + (wave & 1);
-      const bool real = b < cn;
-      const int phys = __builtin_amdgcn_readlane(ids, real ? b : 0);
-      const size_t off = (static_cast<size_t>(phys) * a.hkv + g) * (D * kBlock);
-      const auto rsrc = buffer_of((wave < 2 ? a.k_cache : a.v_cache) + off, real ? kBlk : 0u);
-      char* dst = ring + (j % kPrefill32Depth) * kStage + wave * kBlk;
+  const int total = wg_last / (2 * kBlock) + 1;  // rounds of the work-group
+  // Wave w moves part w of each round (K of its first block, K of its
+  // second, V of its first, V of its second) into the ring; blocks past the
+  // work-group's last are issued with an empty range (they write zeros), so
+  // that every issue counts the same in vmcnt.  The block id of the wave's
+  // next issue is loaded one issue ahead.
+  int next_id = wave % 2 < nblk ? uniform_load(trow, wave % 2) : 0;
+  auto issue = [&](int j) {
+    const int b = 2 * j + (wave & 1);
+    const size_t off = (static_cast<size_t>(next_id) * a.hkv + g) * (D * kBlock);
+    const auto rsrc = buffer_of((wave < 2 ? a.k_cache : a.v_cache) + off, b < nblk ? kBlk : 0u);
+    char* dst = ring + (j % kPrefill32Depth) * kStage + wave * kBlk;
 #pragma unroll
-      for (int q = 0; q < kChunks; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t)(dst + q * 1024), 16,
-                                                 dma_lane + q * 1024, 0, 0, 0);
-    };
-    const int rounds = (cn + 1) / 2;
+    for (int q = 0; q < kChunks; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t)(dst + q * 1024), 16,
+                                               dma_lane + q * 1024, 0, 0, 0);
+    // scalar loads return out of order: issued after this one's use, so that
+    // waiting for it never waits for the next
+    next_id = b + 2 < nblk ? uniform_load(trow, b + 2) : 0;
+  };
+  auto qk = [&](const uint4* kf) {
+    f32x16_t sc = f32x16_t{};
 #pragma unroll
-    for (int j = 0; j < kPrefill32Depth - 1; ++j) issue(j);
-    for (int j = 0; j < rounds; ++j) {
-      wait_vm<(kPrefill32Depth - 2) * kChunks>();  // this wave's part of round j is in
-      __builtin_amdgcn_s_barrier();                // ... and every other wave's (bare: see above)
-      issue(j + kPrefill32Depth - 1);               // into the stage read last round
-      const int round = c0 / 2 + j;                 // rounds from the sequence start
-      if (round < my_rounds) {
-        const char* stg = ring + (j % kPrefill32Depth) * kStage;
-        uint4 kf[kSteps];
-        read_k32<D>(lds_addr(stg) + k_lane, kf);
-        f32x16_t sc = f32x16_t{};
+    for (int st = 0; st < kSteps; ++st) sc = Mfma32<Tag>::mma(kf[st], qf[st], sc);
+    return sc;
+  };
+  auto grow = [&](float own) {  // lazy running maximum: rescale only when it moves by > slack
+    if (__builtin_amdgcn_ballot_w64(own > m + kSlack) != 0) {
+      const float m_new = fmaxf(m, fmaxf(own, __shfl_xor(own, 32)));
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) sc = Mfma32<Tag>::mma(kf[st], qf[st], sc);
-        const int base = round * 2 * kBlock;  // position of the round's first token
-        // element e of sc is the score of position base + 16(e/8) + 8h + e%8
-        float p[16];
-        float own;
-        const bool masked = base + 2 * kBlock - 1 > first_pos;  // some position may pass a limit
-        if (masked) {
-          const int lim = col_pos - base - 8 * h;  // element e is in range if its offset <= lim
+      for (int dt = 0; dt < kSlices; ++dt) acc[dt] *= alpha;
+      m = m_new;
+    }
+  };
+  auto pv = [&](const uint4* vf, const float* p) {
+    const uint4 pb0 = pack8<Tag>(p), pb1 = pack8<Tag>(p + 8);
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            p[e] = 16 * (e >> 3) + (e & 7) <= lim ? sc[e] * a.scale_log2 : -INFINITY;
-          own = p[0];
+    for (int dt = 0; dt < kSlices; ++dt) acc[dt] = Mfma32<Tag>::mma(vf[dt], pb0, acc[dt]);
 #pragma unroll
-          for (int e = 1; e < 16; ++e) own = fmaxf(own, p[e]);
-        } else {  // every position is real and in range: scale inside the exponent
-          float hi = sc[0];
-          if (pos_scale) {
+    for (int dt = 0; dt < kSlices; ++dt)
+      acc[dt] = Mfma32<Tag>::mma(vf[kSlices + dt], pb1, acc[dt]);
+  };
+
+  // Software pipeline: iteration j reads round j+1's K and round j's V,
+  // issues round j+1's QK products and, beside them, round j's softmax, then
+  // round j's PV products.  The ring holds rounds j-1 (free once every wave
+  // is past iteration j-1), j, j+1 and j+2 in flight.
 #pragma unroll
-            for (int e = 1; e < 16; ++e) hi = fmaxf(hi, sc[e]);
-          } else {
+  for (int j = 0; j < kPrefill32Depth - 1; ++j) issue(j);
+  wait_vm<(kPrefill32Depth - 2) * kChunks>();  // round 0 in, for this wave ...
+  __builtin_amdgcn_s_barrier();                // ... and every other (bare: see above)
+  f32x16_t sc_cur = f32x16_t{};
+  if (my_rounds > 0) {
+    uint4 kf[kSteps];
+    read_k32<D>(lds_addr(ring) + k_lane, kf);
+    sc_cur = qk(kf);
+  }
+  for (int j = 0; j < total; ++j) {
+    wait_vm<(kPrefill32Depth - 3) * kChunks>();  // round j+1 in
+    __builtin_amdgcn_s_barrier();
+    issue(j + kPrefill32Depth - 1);  // into the stage of round j-1
+    if (j >= my_rounds) continue;
+    const char* cur = ring + (j % kPrefill32Depth) * kStage;
+    const char* nxt = ring + ((j + 1) % kPrefill32Depth) * kStage;
+    uint4 kf[kSteps], vf[2 * kSlices];
+    read_kv32<D>(lds_addr(nxt) + k_lane, lds_addr(cur) + v_lane, kf, vf);
+    const int base = j * 2 * kBlock;  // position of the round's first token
+    if (base + 2 * kBlock > len) {    // zero V of positions past the end (stale bits)
 #pragma unroll
-            for (int e = 1; e < 16; ++e) hi = fminf(hi, sc[e]);
-          }
-          own = hi * a.scale_log2;
-        }
-        if (__builtin_amdgcn_ballot_w64(own > m + kSlack) != 0) {
-          const float m_new = fmaxf(m, fmaxf(own, __shfl_xor(own, 32)));
-          const float alpha = fast_exp2(m - m_new);
-          l *= alpha;
+      for (int b = 0; b < 2; ++b) {
+        const int rem = len - base - b * kBlock - 8 * h;  // this lane's tokens below the end
+        const uint32_t m0 = (0 < rem ? 0x0000FFFFu : 0u) | (1 < rem ? 0xFFFF0000u : 0u);
+        const uint32_t m1 = (2 < rem ? 0x0000FFFFu : 0u) | (3 < rem ? 0xFFFF0000u : 0u);
+        const uint32_t m2 = (4 < rem ? 0x0000FFFFu : 0u) | (5 < rem ? 0xFFFF0000u : 0u);
+        const uint32_t m3 = (6 < rem ? 0x0000FFFFu : 0u) | (7 < rem ? 0xFFFF0000u : 0u);
 #pragma unroll
-          for (int dt = 0; dt < kSlices; ++dt) acc[dt] *= alpha;
-          m = m_new;
-        }
-        if (masked) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) p[e] = fast_exp2(p[e] - m);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) p[e] = fast_exp2(fmaf(sc[e], a.scale_log2, -m));
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) l += p[e];
-        for (int b = 0; b < 2; ++b) {
-          uint4 vf[kSlices];
-          read_v32<D>(lds_addr(stg) + v_lane + b * kBlk, vf);
-          const int bstart = base + b * kBlock;
-          if (bstart + kBlock > len) {  // zero V of positions past the end (stale bits)
-            const int rem = len - bstart - 8 * h;  // this lane's tokens below the end
-            const uint32_t m0 = (0 < rem ? 0x0000FFFFu : 0u) | (1 < rem ? 0xFFFF0000u : 0u);
-            const uint32_t m1 = (2 < rem ? 0x0000FFFFu : 0u) | (3 < rem ? 0xFFFF0000u : 0u);
-            const uint32_t m2 = (4 < rem ? 0x0000FFFFu : 0u) | (5 < rem ? 0xFFFF0000u : 0u);
-            const uint32_t m3 = (6 < rem ? 0x0000FFFFu : 0u) | (7 < rem ? 0xFFFF0000u : 0u);
-#pragma unroll
-            for (int dt = 0; dt < kSlices; ++dt) {
-              vf[dt].x &= m0;
-              vf[dt].y &= m1;
-              vf[dt].z &= m2;
-              vf[dt].w &= m3;
-            }
-          }
-          const uint4 pb = pack8<Tag>(p + 8 * b);
-#pragma unroll
-          for (int dt = 0; dt < kSlices; ++dt) acc[dt] = Mfma32<Tag>::mma(vf[dt], pb, acc[dt]);
+        for (int dt = 0; dt < kSlices; ++dt) {
+          uint4& v = vf[b * kSlices + dt];
+          v.x &= m0;
+          v.y &= m1;
+          v.z &= m2;
+          v.w &= m3;
         }
       }
     }
-    wait_vm<0>();
-    __builtin_amdgcn_s_barrier();  // the next chunk's first stages may be overwritten
+    // element e of sc_cur is the score of position base + 16(e/8) + 8h + e%8;
+    // its exponent is sc_cur[e] * mul - m
+    float mul, own;
+    if (base + 2 * kBlock - 1 <= first_pos) {
+      // every position is real and in range: no masks, scale inside the exponent
+      float hi = sc_cur[0];
+      if (pos_scale) {
+#pragma unroll
+        for (int e = 1; e < 16; ++e) hi = fmaxf(hi, sc_cur[e]);
+      } else {
+#pragma unroll
+        for (int e = 1; e < 16; ++e) hi = fminf(hi, sc_cur[e]);
+      }
+      own = hi * a.scale_log2;
+      mul = a.scale_log2;
+    } else {
+      const int lim = col_pos - base - 8 * h;  // element e is in range if its offset <= lim
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sc_cur[e] = 16 * (e >> 3) + (e & 7) <= lim ? sc_cur[e] * a.scale_log2 : -INFINITY;
+      own = sc_cur[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) own = fmaxf(own, sc_cur[e]);
+      mul = 1.f;
+    }
+    grow(own);
+    // round j+1's QK products with round j's exponentials beside them, then
+    // round j's PV products
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p[e] = fast_exp2(fmaf(sc_cur[e], mul, -m));
+    sc_cur = qk(kf);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) l += p[e];
+    pv(vf, p);
   }
+  wait_vm<0>();
   const float l_tot = l + __shfl_xor(l, 32);
   if (!col_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
