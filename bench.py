@@ -38,11 +38,15 @@ DECODE_KERNELS = {
     "decode_generic_kernel": ("pa_decode.hip", "pa_decode_common.h"),
     "decode_items_i8_kernel": ("pa_decode.hip", "pa_decode_int8.h", "pa_decode_common.h"),
 }
+# kernels with counter-measured traffic files and the sources each is built from
+KERNEL_SOURCES = dict(DECODE_KERNELS, prefill_kernel=("pa_prefill.hip", "pa_decode_common.h"))
 
 
 def traffic_file(kernel):
     if kernel == "decode_items_kernel":
         return TRAFFIC_FILE
+    if kernel == "prefill_kernel":
+        return os.path.join(ROOT, "profiles", "prefill_traffic.json")
     return os.path.join(ROOT, "profiles", f"decode_traffic_{kernel}.json")
 
 
@@ -76,7 +80,7 @@ def step_bytes(w, db, int8=False):
 
 def source_hash(kernel):
     h = hashlib.sha256()
-    for name in DECODE_KERNELS[kernel]:
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -299,7 +303,7 @@ def prefill_bench(args):
     k_ms = k["ms"] / max(1, k["launches"])
     achieved = flops / (k_ms * 1e-3) / 1e12
     tokens = int(np.sum(w.step_lens))
-    print(json.dumps({
+    result = {
         "metric": "chunked-prefill paged attention TFLOP/s; prefill tokens/s",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -313,8 +317,24 @@ def prefill_bench(args):
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops,
-                     "avg_launch_ms": round(k_ms, 5), "traffic": None},
-    }), flush=True)
+                     "avg_launch_ms": round(k_ms, 5),
+                     "traffic": load_traffic(w.name, "prefill_kernel")},
+    }
+    if args.calibrate_copy > 0:
+        calibration_copies(args.calibrate_copy)
+        result["calibration_copy_bytes"] = args.calibrate_copy << 20
+    print(json.dumps(result), flush=True)
+
+
+def calibration_copies(mib):
+    """Three plain device copies of `mib` MiB: a known-size reference for the
+    HBM byte counters."""
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -340,8 +360,8 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 plain device copies of MIB MiB (a known-size "
                          "reference for HBM byte counters)")
-    ap.add_argument("--kernel", default="decode_items_kernel", choices=sorted(DECODE_KERNELS),
-                    help="main decode kernel the --pmc-summary counters belong to")
+    ap.add_argument("--kernel", default="decode_items_kernel", choices=sorted(KERNEL_SOURCES),
+                    help="kernel the --pmc-summary counters belong to")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench, taken with --calibrate-copy 1024, into profiles/ "
@@ -351,9 +371,12 @@ def main():
 
     if args.pmc_summary:
         import workloads
-        name = workloads.CONFIG_NAMES[int(args.config) if args.config.isdigit() else args.config]
-        pmc_summary(*args.pmc_summary, name + ("-int8kv" if args.kv == "int8" else ""),
-                    args.kernel)
+        if args.prefill:
+            name = workloads.CONFIG_NAMES["prefill"]
+        else:
+            name = workloads.CONFIG_NAMES[int(args.config) if args.config.isdigit() else args.config]
+            name += "-int8kv" if args.kv == "int8" else ""
+        pmc_summary(*args.pmc_summary, name, args.kernel)
         return
 
     if args.gpus != 1:
@@ -466,13 +489,8 @@ def main():
                      "traffic": traffic},
     }
     if args.calibrate_copy > 0:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["calibration_copy_bytes"] = n
+        calibration_copies(args.calibrate_copy)
+        result["calibration_copy_bytes"] = args.calibrate_copy << 20
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, int8)
     print(json.dumps(result), flush=True)

@@ -5,18 +5,19 @@
 // cache?").  The chunk's K/V are in the cache before the call, as for decode,
 // so one token per sequence is exactly decode.
 //
-// A tile is a run of consecutive chunk queries of one (sequence, KV head,
-// group of up to 16 query heads); the 16 columns of its matrix-core products
-// are (query, head) pairs, query-major: with G query heads per KV head
-// (G <= 16) a tile holds 16 / G queries of that KV head, so every K/V block
-// is multiplied against 16 query rows at once.  Per 16-token block and tile:
-//   scores[16 tok x 16 cols] = K . Q^T          (MFMA 16x16x32, K as A)
-//   online softmax per column, masked causally: token t counts for the column
-//   of the query at position p iff t <= p
-//   acc^T[D x 16 cols] += V^T . P^T             (MFMA 16x16x16)
-// A work-group (4 waves x 2 tiles each) walks the K/V blocks its 8 tiles
-// need through an LDS ring that every block enters once (prefill_kernel);
-// work-groups with the latest queries (the most positions) start first.
+// A tile is 32 matrix-core columns: (query, head) pairs of consecutive chunk
+// queries of one sequence and KV head, query-major, so with G query heads per
+// KV head (G <= 32) a tile holds 32 / G queries and every K/V position is
+// multiplied against 32 query rows at once.  Per 32-position round (two
+// 16-token blocks) and tile:
+//   scores[32 pos x 32 cols] = K . Q^T          (MFMA 32x32x16, K as A)
+//   online softmax per column, masked causally: position t counts for the
+//   column of the query at position p iff t <= p
+//   acc^T[D x 32 cols] += V^T . P^T             (MFMA 32x32x16, per block)
+// A work-group (4 waves, one tile each) walks the rounds its tiles need
+// through an LDS ring that each round enters once, software-pipelined so
+// that one round's QK products run beside the previous round's softmax; the
+// work-groups with the most rounds are handed out first.
 #include "pa_decode_common.h"
 
 namespace pa {
@@ -32,8 +33,8 @@ struct PrefillArgs {
   uint16_t* out;            // [T][Hq][D]
   float scale_log2;
   int num_seqs, hq, hkv, group, head_blocks, max_blocks;
-  int cols_heads;           // query heads per column group: min(G, 16)
-  int qpw;                  // queries per wave: 16 / cols_heads
+  int cols_heads;           // query heads per tile: min(G, 32)
+  int qpw;                  // queries per wave: 32 / cols_heads
   int groups_max;           // query runs of the longest chunk: ceil(max_chunk / qpw)
   int largest_first;        // order work-groups by their work (num_seqs <= kOrderMaxSeqs)
 };
@@ -52,275 +53,13 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-constexpr int kPrefillWaves = 4;
-#ifndef PA_PREFILL_ROUND
-#define PA_PREFILL_ROUND 1
-#endif
-// blocks per barrier (2 measured 4 % slower on MI355X: fewer barriers, but
-// the waves then wait on longer rounds) and LDS stages: a round in use and
-// at least two blocks loading
-constexpr int kPrefillRound = PA_PREFILL_ROUND;
-constexpr int kPrefillDepth = kPrefillRound == 1 ? 4 : 3 * kPrefillRound;
-#ifndef PA_PREFILL_TILES
-#define PA_PREFILL_TILES 2
-#endif
-constexpr int kPrefillTiles = PA_PREFILL_TILES;  // 16-column tiles per wave
-#ifndef PA_PREFILL_32
-#define PA_PREFILL_32 1
-#endif
-constexpr bool kPrefill32 = PA_PREFILL_32 != 0;  // 32-column tiles (prefill32_kernel)
+constexpr int kPrefillWaves = 4;  // one 32-column tile each
 
-// One block's MFMA operands from an LDS stage (K: 16 bytes per lane per
-// k-step, 1 KiB apart; V: 8 bytes per lane per slice, 512 bytes apart), in one
-// block of LDS reads that ends with their wait.
-template <int D>
-__device__ __forceinline__ void read_block(uint32_t ka, uint32_t va, BlockRegs<D>& r);
-
-template <>
-__device__ __forceinline__ void read_block<128>(uint32_t ka, uint32_t va, BlockRegs<128>& r) {
-  asm volatile(
-      "ds_read_b128 %0, %12\n"
-      "ds_read_b128 %1, %12 offset:1024\n"
-      "ds_read_b128 %2, %12 offset:2048\n"
-      "ds_read_b128 %3, %12 offset:3072\n"
-      "ds_read_b64 %4, %13\n"
-      "ds_read_b64 %5, %13 offset:512\n"
-      "ds_read_b64 %6, %13 offset:1024\n"
-      "ds_read_b64 %7, %13 offset:1536\n"
-      "ds_read_b64 %8, %13 offset:2048\n"
-      "ds_read_b64 %9, %13 offset:2560\n"
-      "ds_read_b64 %10, %13 offset:3072\n"
-      "ds_read_b64 %11, %13 offset:3584\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.kf[0]), "=&v"(r.kf[1]), "=&v"(r.kf[2]), "=&v"(r.kf[3]), "=&v"(r.vf[0]),
-        "=&v"(r.vf[1]), "=&v"(r.vf[2]), "=&v"(r.vf[3]), "=&v"(r.vf[4]), "=&v"(r.vf[5]),
-        "=&v"(r.vf[6]), "=&v"(r.vf[7])
-      : "v"(ka), "v"(va)
-      : "memory");
-}
-
-template <>
-__device__ __forceinline__ void read_block<64>(uint32_t ka, uint32_t va, BlockRegs<64>& r) {
-  asm volatile(
-      "ds_read_b128 %0, %6\n"
-      "ds_read_b128 %1, %6 offset:1024\n"
-      "ds_read_b64 %2, %7\n"
-      "ds_read_b64 %3, %7 offset:512\n"
-      "ds_read_b64 %4, %7 offset:1024\n"
-      "ds_read_b64 %5, %7 offset:1536\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.kf[0]), "=&v"(r.kf[1]), "=&v"(r.vf[0]), "=&v"(r.vf[1]), "=&v"(r.vf[2]),
-        "=&v"(r.vf[3])
-      : "v"(ka), "v"(va)
-      : "memory");
-}
-
-// Online-softmax step of one block for the prefill kernel.  Two departures
-// from decode's block_update, both for the matrix cores' sake (prefill is
-// bound by arithmetic, not by HBM): P enters PV as one value in the storage
-// dtype (decode's hi + lo pair doubles the PV products), and the running
-// maximum is raised only when a score exceeds it by more than 2^8 (the
-// weights then stay below 2^8, which fp32 sums and bf16/fp16 weights hold),
-// so that the accumulator is rescaled on few blocks instead of on every one.
-// `masked`: some position of the block may lie past a column's limit (the
-// caller knows when none can, and the comparisons are skipped).  The cross-
-// lane maximum is only formed when some lane's own scores outgrow the
-// running maximum by the slack; otherwise the block needs no exchange.
-template <typename Tag, int D>
-__device__ __forceinline__ void prefill_update(uint2* vf, f32x4_t sc, float sl2, int blk, int len,
-                                               int lim, bool masked, WaveState<D>& st) {
-  constexpr int kSlices = D / 16;
-  constexpr float kSlack = 8.f;  // log2 units
-  const int lane = threadIdx.x & (kWave - 1);
-  const int kg = lane >> 4;
-  const int pos0 = blk * kBlock + kg * 4;
-  float s4[4];
-  if (masked) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s4[i] = (pos0 + i < lim) ? sc[i] * sl2 : -INFINITY;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s4[i] = sc[i] * sl2;
-  }
-  const float own = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-  if (__builtin_amdgcn_ballot_w64(own > st.m + kSlack) != 0) {  // some column outgrew its max
-    float mx = fmaxf(own, __shfl_xor(own, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = fast_exp2(st.m - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int sl = 0; sl < kSlices; ++sl) st.acc[sl] *= alpha;
-    st.m = m_new;
-  }
-  float p4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p4[i] = fast_exp2(s4[i] - st.m);
-  st.l += (p4[0] + p4[1]) + (p4[2] + p4[3]);
-  if ((blk + 1) * kBlock > len) {  // last block: zero V of positions past the end
-    const uint32_t lo = (pos0 + 0 < len ? 0x0000FFFFu : 0u) | (pos0 + 1 < len ? 0xFFFF0000u : 0u);
-    const uint32_t hi = (pos0 + 2 < len ? 0x0000FFFFu : 0u) | (pos0 + 3 < len ? 0xFFFF0000u : 0u);
-#pragma unroll
-    for (int sl = 0; sl < kSlices; ++sl) {
-      vf[sl].x &= lo;
-      vf[sl].y &= hi;
-    }
-  }
-  const uint2 ph = Mfma<Tag>::pack(p4[0], p4[1], p4[2], p4[3]);
-#pragma unroll
-  for (int sl = 0; sl < kSlices; ++sl) st.acc[sl] = Mfma<Tag>::pv(vf[sl], ph, st.acc[sl]);
-}
-
-// Work-group = 4 waves x kPrefillTiles consecutive runs of chunk queries of
-// one (sequence, KV head, head block).  They walk the same K/V blocks, so
-// each block is brought into LDS once for all of them by direct
-// buffer-to-LDS loads (each wave moves 1/4 of it) through a ring of
-// kPrefillDepth stages; every wave reads the block's operands from there once
-// and multiplies them against its kPrefillTiles column tiles.
-template <typename Tag, int D>
-__global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(PrefillArgs a) {
-  constexpr int kStage = 2 * D * kBlock * 2;         // K then V of one block-head
-  constexpr int kChunksPerWave = D / 64;              // 1 KiB loads per wave per stage
-  constexpr int T = kPrefillTiles;
-  extern __shared__ char ring[];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int n = lane & 15, kg = lane >> 4;
-  // unit = (run group, sequence, KV head, head block), from the last runs
-  const int per_run = a.num_seqs * a.hkv * a.head_blocks;
-  const int u = blockIdx.x;
-  const int runs_per_wg = kPrefillWaves * T;
-  const int run_groups = (a.groups_max + runs_per_wg - 1) / runs_per_wg;
-  const int rg = run_groups - 1 - u / per_run;
-  const int r = u % per_run;
-  const int s = r / (a.hkv * a.head_blocks);
-  const int g = (r / a.head_blocks) % a.hkv;
-  const int hb = r % a.head_blocks;
-  const int q0 = uniform_load(a.qstart, s), q1 = uniform_load(a.qstart, s + 1);
-  const int len = min(max(uniform_load(a.lens, s), q1 - q0), a.max_blocks * kBlock);
-  const int nchunk = min(q1 - q0, len);
-  const int i_wg = rg * runs_per_wg * a.qpw;  // first query of the work-group
-  if (i_wg >= nchunk) return;                  // uniform over the work-group
-  const int h_base = hb * 16;
-  const int nh = min(a.cols_heads, a.group - h_base);
-  const int ci = n / a.cols_heads, ch = n % a.cols_heads;
-  // tile t of this wave: queries i0[t] .. i0[t] + nq[t] - 1
-  int i0[T], col_pos[T], first_pos[T];
-  bool col_ok[T];
-  int wave_last = 0;
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    i0[t] = i_wg + (wave * T + t) * a.qpw;
-    const int nq = max(0, min(a.qpw, nchunk - i0[t]));
-    col_ok[t] = ci < nq && ch < nh;
-    first_pos[t] = nq > 0 ? len - nchunk + i0[t] : 0;
-    col_pos[t] = nq > 0 ? first_pos[t] + (col_ok[t] ? ci : nq - 1) : 0;
-    if (nq > 0) wave_last = first_pos[t] + nq - 1;
-  }
-  const int wg_last = len - nchunk + min(nchunk, i_wg + runs_per_wg * a.qpw) - 1;
-  const int nblk = wg_last / kBlock + 1;     // blocks the work-group walks
-  const int my_blk = wave_last / kBlock + 1;  // blocks this wave needs
-
-  uint4 qf[T][D / 32];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) qf[t][j] = make_uint4(0, 0, 0, 0);
-    if (col_ok[t]) {
-      const size_t row = static_cast<size_t>(q0 + i0[t] + ci) * a.hq + g * a.group + h_base + ch;
-      const uint4* qrow = reinterpret_cast<const uint4*>(a.q + row * D);
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j) qf[t][j] = qrow[j * 4 + kg];
-    }
-  }
-
-  WaveState<D> st[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) st[t].reset();
-  const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
-  const uint32_t va_lane = ((lane & 15) * kBlock + (lane >> 4) * 4) * 2;
-  for (int c0 = 0; c0 < nblk; c0 += 64) {
-    const int cn = min(64, nblk - c0);
-    const int ids = load_ids<1>(trow, c0, cn);
-    // this wave's share of block j of the chunk into its stage; blocks past
-    // the chunk are issued with an empty range (they write zeros), so that
-    // every wave always has the same number of loads in flight
-    auto issue = [&](int j) {
-      const bool real = j < cn;
-      const int phys = __builtin_amdgcn_readlane(ids, real ? j : 0);
-      const size_t off = (static_cast<size_t>(phys) * a.hkv + g) * (D * kBlock);
-      const uint32_t range = real ? D * kBlock * 2 : 0u;
-      const auto rk = buffer_of(a.k_cache + off, range);
-      const auto rv = buffer_of(a.v_cache + off, range);
-      char* dst = ring + (j % kPrefillDepth) * kStage;
-#pragma unroll
-      for (int c = 0; c < kChunksPerWave; ++c) {
-        const int chunk = wave * kChunksPerWave + c;  // of the stage's 2 * D / 32 KiBs
-        const bool is_v = chunk >= D / 32;
-        const int byte = (is_v ? chunk - D / 32 : chunk) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? rv : rk,
-                                                 (lds_void_t)(dst + (is_v ? D * kBlock * 2 : 0) + byte),
-                                                 16, lane * 16 + byte, 0, 0, 0);
-      }
-    };
-    // rounds of kPrefillRound blocks: one wait and one barrier per round
-    constexpr int R = kPrefillRound;
-#pragma unroll
-    for (int j = 0; j < kPrefillDepth - R; ++j) issue(j);
-    for (int j = 0; j < cn; j += R) {
-      wait_vm<(kPrefillDepth - 2 * R) * kChunksPerWave>();  // this wave's part of the round
-      // ... and every other wave's: a bare barrier (a fenced one would wait for
-      // every load in flight); the loads are counted in by the waits, and LDS
-      // reads of earlier rounds end with their own wait
-      __builtin_amdgcn_s_barrier();
-#pragma unroll
-      for (int i = 0; i < R; ++i) issue(j + kPrefillDepth - R + i);  // stages read last round
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int blk = c0 + j + i;
-        if (j + i < cn && blk < my_blk) {
-          const char* stg = ring + ((j + i) % kPrefillDepth) * kStage;
-          BlockRegs<D> rb;
-          read_block<D>(lds_addr(stg) + lane * 16, lds_addr(stg + D * kBlock * 2) + va_lane, rb);
-#pragma unroll
-          for (int t = 0; t < T; ++t) {
-            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < D / 32; ++k) sc = Mfma<Tag>::qk(rb.kf[k], qf[t][k], sc);
-            // every position of the block is at or before the tile's first query
-            const bool masked = (blk + 1) * kBlock > first_pos[t] + 1;
-            prefill_update<Tag, D>(rb.vf, sc, a.scale_log2, blk, len, col_pos[t] + 1, masked,
-                                   st[t]);
-          }
-        }
-      }
-    }
-    wait_vm<0>();
-    __builtin_amdgcn_s_barrier();  // the next chunk's first stages may be overwritten
-  }
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    float l_tot = st[t].l + __shfl_xor(st[t].l, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (!col_ok[t]) continue;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow =
-        a.out + (static_cast<size_t>(q0 + i0[t] + ci) * a.hq + g * a.group + h_base + ch) * D;
-#pragma unroll
-    for (int sl = 0; sl < D / 16; ++sl) {
-      const f32x4_t v = st[t].acc[sl];
-      const uint2 packed = Mfma<Tag>::pack(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-      *reinterpret_cast<uint2*>(orow + sl * 16 + kg * 4) = packed;
-    }
-  }
-}
-
-// ---- 32-column tiles ----
+// ---- operand layout ----
 //
-// The same computation on v_mfma_f32_32x32x16: a wave's tile is 32 (query,
-// head) columns and a round is 32 positions (two blocks), so each lane holds
-// 16 scores of one column and the per-score vector work (scale, mask, running
-// maximum, exponential, sum, packing) is amortised over twice the products.
+// With a 32-column tile and 32-position rounds each lane holds 16 scores of
+// one column, so the per-score vector work (scale, mask, running maximum,
+// exponential, sum, packing) is amortised over 32x32x16 products.
 //   QK: rows = the round's 32 tokens, columns = the tile (A = K, B = Q^T).
 //       Row r carries token pi(r), r with bits 2 and 3 swapped, so that lane
 //       l (column l%32, rows 8j + 4(l/32) + i) ends up holding, for block b,
@@ -543,20 +282,20 @@ __device__ bool largest_first(const PrefillArgs& a, int q, int R, int pw, int& s
   return false;  // not reached: the ranks below total are all covered
 }
 
-#ifndef PA_PREFILL32_OCC
-#define PA_PREFILL32_OCC 2
-#endif
-constexpr int kPrefill32Depth = 4;  // rounds (pairs of blocks) in the LDS ring
+// Rounds in the LDS ring: the one being multiplied, the next (its QK
+// products run in the same iteration) and three in flight.  80 KiB at D = 128:
+// two work-groups (8 waves, 2 per SIMD at up to 256 registers) fill a CU.
+constexpr int kRingDepth = 5;
 
 template <typename Tag, int D>
-__global__ __launch_bounds__(kPrefillWaves * kWave, PA_PREFILL32_OCC) void prefill32_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int kBlk = D * kBlock * 2;      // K (or V) of one block-head
   constexpr int kStage = 4 * kBlk;          // [K b0][K b1][V b0][V b1]
   constexpr int kChunks = kBlk / 1024;      // 1 KiB loads per block part = per wave
   constexpr int kSteps = D / 16;            // QK k-steps
   constexpr int kSlices = D / 32;           // PV dimension slices
   constexpr float kSlack = 8.f;             // log2 units
-  extern __shared__ char ring[];
+  __shared__ __attribute__((aligned(1024))) char ring[kRingDepth * kStage];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 31, h = lane >> 5;
@@ -625,7 +364,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, PA_PREFILL32_OCC) void prefi
     const int b = 2 * j + (wave & 1);
     const size_t off = (static_cast<size_t>(next_id) * a.hkv + g) * (D * kBlock);
     const auto rsrc = buffer_of((wave < 2 ? a.k_cache : a.v_cache) + off, b < nblk ? kBlk : 0u);
-    char* dst = ring + (j % kPrefill32Depth) * kStage + wave * kBlk;
+    char* dst = ring + (j % kRingDepth) * kStage + wave * kBlk;
 #pragma unroll
     for (int q = 0; q < kChunks; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t)(dst + q * 1024), 16,
@@ -661,12 +400,16 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, PA_PREFILL32_OCC) void prefi
 
   // Software pipeline: iteration j reads round j+1's K and round j's V,
   // issues round j+1's QK products and, beside them, round j's softmax, then
-  // round j's PV products.  The ring holds rounds j-1 (free once every wave
-  // is past iteration j-1), j, j+1 and j+2 in flight.
+  // round j's PV products.  The ring holds rounds j and j+1, rounds j+2 and
+  // j+3 in flight, and the stage of round j-1, refilled with round j+4 once
+  // every wave is past iteration j-1.
 #pragma unroll
-  for (int j = 0; j < kPrefill32Depth - 1; ++j) issue(j);
-  wait_vm<(kPrefill32Depth - 2) * kChunks>();  // round 0 in, for this wave ...
-  __builtin_amdgcn_s_barrier();                // ... and every other (bare: see above)
+  for (int j = 0; j < kRingDepth - 1; ++j) issue(j);
+  // Each wave waits for its own copies (vmcnt counts them in issue order) and
+  // the barrier for everyone's.  A bare s_barrier: __syncthreads would also
+  // wait for every copy still in flight.
+  wait_vm<(kRingDepth - 2) * kChunks>();  // round 0 in, for this wave ...
+  __builtin_amdgcn_s_barrier();           // ... and for every other
   f32x16_t sc_cur = f32x16_t{};
   if (my_rounds > 0) {
     uint4 kf[kSteps];
@@ -674,12 +417,12 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, PA_PREFILL32_OCC) void prefi
     sc_cur = qk(kf);
   }
   for (int j = 0; j < total; ++j) {
-    wait_vm<(kPrefill32Depth - 3) * kChunks>();  // round j+1 in
+    wait_vm<(kRingDepth - 3) * kChunks>();  // round j+1 in
     __builtin_amdgcn_s_barrier();
-    issue(j + kPrefill32Depth - 1);  // into the stage of round j-1
+    issue(j + kRingDepth - 1);  // into the stage of round j-1
     if (j >= my_rounds) continue;
-    const char* cur = ring + (j % kPrefill32Depth) * kStage;
-    const char* nxt = ring + ((j + 1) % kPrefill32Depth) * kStage;
+    const char* cur = ring + (j % kRingDepth) * kStage;
+    const char* nxt = ring + ((j + 1) % kRingDepth) * kStage;
     uint4 kf[kSteps], vf[2 * kSlices];
     read_kv32<D>(lds_addr(nxt) + k_lane, lds_addr(cur) + v_lane, kf, vf);
     const int base = j * 2 * kBlock;  // position of the round's first token
@@ -756,19 +499,10 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, PA_PREFILL32_OCC) void prefi
 template <typename Tag>
 pa_status launch_prefill(const PrefillArgs& a, int head_dim, int64_t units, hipStream_t st) {
   const dim3 g3(static_cast<uint32_t>(units)), b3(kPrefillWaves * kWave);
-  if (kPrefill32) {
-    const size_t lds = static_cast<size_t>(kPrefill32Depth) * 4 * head_dim * kBlock * 2;
-    if (head_dim == 128)
-      prefill32_kernel<Tag, 128><<<g3, b3, lds, st>>>(a);
-    else
-      prefill32_kernel<Tag, 64><<<g3, b3, lds, st>>>(a);
-    return launch_status();
-  }
-  const size_t lds = static_cast<size_t>(kPrefillDepth) * 2 * head_dim * kBlock * 2;
-  if (head_dim == 128)
-    prefill_kernel<Tag, 128><<<g3, b3, lds, st>>>(a);
+  if (head_dim == 128)  // the ring is static LDS
+    prefill_kernel<Tag, 128><<<g3, b3, 0, st>>>(a);
   else
-    prefill_kernel<Tag, 64><<<g3, b3, lds, st>>>(a);
+    prefill_kernel<Tag, 64><<<g3, b3, 0, st>>>(a);
   return launch_status();
 }
 
@@ -807,15 +541,13 @@ pa_status pa_paged_attention_prefill(const void* q, const void* k_cache, const v
   a.hq = num_q_heads;
   a.hkv = num_kv_heads;
   a.group = num_q_heads / num_kv_heads;
-  const int cols = kPrefill32 ? 32 : 16;  // columns of a tile
-  a.head_blocks = (a.group + cols - 1) / cols;
+  a.head_blocks = (a.group + 31) / 32;
   a.max_blocks = max_blocks_per_seq;
-  a.cols_heads = std::min(a.group, cols);
-  a.qpw = cols / a.cols_heads;
+  a.cols_heads = std::min(a.group, 32);
+  a.qpw = 32 / a.cols_heads;
   a.groups_max = (max_chunk_len + a.qpw - 1) / a.qpw;
-  a.largest_first = kPrefill32 && num_seqs <= kOrderMaxSeqs;
-  const int runs_per_wg = kPrefillWaves * (kPrefill32 ? 1 : kPrefillTiles);
-  const int64_t units = static_cast<int64_t>((a.groups_max + runs_per_wg - 1) / runs_per_wg) *
+  a.largest_first = num_seqs <= kOrderMaxSeqs;
+  const int64_t units = static_cast<int64_t>((a.groups_max + kPrefillWaves - 1) / kPrefillWaves) *
                         num_seqs * num_kv_heads * a.head_blocks;
   if (units > 0x7fffffff) return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
