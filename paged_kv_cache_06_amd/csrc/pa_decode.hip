@@ -222,45 +222,22 @@ __device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int s, int gh
   }
 }
 
-// Work-group i serves item i / heads of the plan (heads = KV heads x query
-// head groups); work-groups past the list's end exit at once.  The waves take
-// the item's blocks round-robin and merge through LDS; a sequence with one
-// partition is normalised and stored, a split one leaves its partial (m, l,
-// acc) for the merge kernel.
-template <typename Tag, int D>
-__global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_kernel(
-    DecodeArgs a, const int4* __restrict__ items) {
-  constexpr int W = kItemWaves;
-  extern __shared__ float comb[];
-  const int heads = a.hkv * a.head_blocks;
-  const int4 it = items[blockIdx.x / heads];
-  if (it.x < 0) return;
-  const int gh = blockIdx.x % heads;
-  const int s = it.x, p = it.y, len = it.z;
-  const int g = gh / a.head_blocks, h0 = (gh % a.head_blocks) * 16;
-  const int nh = min(16, a.group - h0);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int start = p * a.part_size;
-  const int end = min(len, start + a.part_size);
-  const int nblk = max(end - start + kBlock - 1, 0) / kBlock;
-  const int b_first = start / kBlock + wave;
-  const int count = nblk > wave ? (nblk - wave + W - 1) / W : 0;
-  const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
-  const int ids = load_ids<W>(trow, b_first, count);
-  uint4 qf[D / 32];
-  load_q<D>(a, s, g, h0, nh, qf);
-  WaveState<D> st;
-  st.reset();
-  attend_blocks<Tag, D, W>(a, trow, ids, b_first, count, end, g, qf, st);
-  stage_partials<D, W>(comb, a.nh_max, nh, st);
-  __syncthreads();
-
+// The end of an item: the waves' partials are combined through LDS; a
+// sequence with one partition is normalised and stored, a split one leaves
+// its partial (m, l, acc) for the merge (in-kernel when a.arrivals is set,
+// else by the merge kernel).  vs: INT8 cache only, the V scales of head g,
+// applied to each combined accumulator.
+template <typename Tag, int D, int W>
+__device__ __forceinline__ void finish_item(const DecodeArgs& a, float* comb, int s, int p,
+                                            int len, int g, int h0, int nh, int gh,
+                                            const float* vs) {
   const int nparts = min((len + a.part_size - 1) / a.part_size, a.np_max);
   const size_t row0 = static_cast<size_t>(s) * a.hq_total + g * a.group + h0;
   for (int e = threadIdx.x; e < nh * D; e += W * kWave) {
     const int h = e / D, d = e % D;
     float M, L, A;
     combine_waves<W>(comb, a.nh_max, D, h, d, M, L, A);
+    if (vs) A *= vs[d];
     const size_t row = row0 + h;
     if (nparts <= 1) {
       a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
@@ -284,17 +261,12 @@ __global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_ke
   if (nparts > 1 && a.arrivals) merge_if_last<Tag, D, W>(a, s, gh, nparts, row0, nh);
 }
 
-// decode_items_kernel over an INT8 cache (same items, partitions and
-// partials); the V scale multiplies each merged result before it is stored.
-template <typename Tag, int D>
-__global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_i8_kernel(
-    DecodeArgs a, const int4* __restrict__ items) {
+// One work item (sequence it.x, partition it.y, length it.z) for head group
+// gh (KV head x query head block): the waves take the item's blocks
+// round-robin, then finish_item.
+template <typename Tag, int D, bool kInt8>
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, int4 it, int gh, float* comb) {
   constexpr int W = kItemWaves;
-  extern __shared__ float comb[];
-  const int heads = a.hkv * a.head_blocks;
-  const int4 it = items[blockIdx.x / heads];
-  if (it.x < 0) return;
-  const int gh = blockIdx.x % heads;
   const int s = it.x, p = it.y, len = it.z;
   const int g = gh / a.head_blocks, h0 = (gh % a.head_blocks) * 16;
   const int nh = min(16, a.group - h0);
@@ -307,42 +279,46 @@ __global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_i8
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
   const int ids = load_ids<W>(trow, b_first, count);
   uint4 qf[D / 32];
-  const float back = load_q_i8<Tag, D>(a, s, g, h0, nh, qf);
   WaveState<D> st;
   st.reset();
-  attend_blocks_i8<D, W>(a, trow, ids, b_first, count, end, g, qf, a.scale_log2 * back, st);
+  if constexpr (kInt8) {
+    const float back = load_q_i8<Tag, D>(a, s, g, h0, nh, qf);
+    attend_blocks_i8<D, W>(a, trow, ids, b_first, count, end, g, qf, a.scale_log2 * back, st);
+  } else {
+    load_q<D>(a, s, g, h0, nh, qf);
+    attend_blocks<Tag, D, W>(a, trow, ids, b_first, count, end, g, qf, st);
+  }
   stage_partials<D, W>(comb, a.nh_max, nh, st);
   __syncthreads();
+  finish_item<Tag, D, W>(a, comb, s, p, len, g, h0, nh, gh,
+                         kInt8 ? a.v_scale + static_cast<size_t>(g) * D : nullptr);
+}
 
-  const int nparts = min((len + a.part_size - 1) / a.part_size, a.np_max);
-  const size_t row0 = static_cast<size_t>(s) * a.hq_total + g * a.group + h0;
-  const float* vs = a.v_scale + static_cast<size_t>(g) * D;
-  for (int e = threadIdx.x; e < nh * D; e += W * kWave) {
-    const int h = e / D, d = e % D;
-    float M, L, A;
-    combine_waves<W>(comb, a.nh_max, D, h, d, M, L, A);
-    A *= vs[d];
-    const size_t row = row0 + h;
-    if (nparts <= 1) {
-      a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
-    } else {
-      const size_t part = row * a.np_max + p;
-      if (a.arrivals) {  // merged in-kernel: stored where every XCD sees them
-        publish(a.ws_acc + part * D + d, A);
-        if (d == 0) {
-          publish(a.ws_ml + 2 * part, M);
-          publish(a.ws_ml + 2 * part + 1, L);
-        }
-      } else {
-        a.ws_acc[part * D + d] = A;
-        if (d == 0) {
-          a.ws_ml[2 * part] = M;
-          a.ws_ml[2 * part + 1] = L;
-        }
-      }
-    }
-  }
-  if (nparts > 1 && a.arrivals) merge_if_last<Tag, D, W>(a, s, gh, nparts, row0, nh);
+// Work-group b serves item b / heads of the plan for head group b % heads
+// (heads = KV heads x query head blocks); work-groups past the list's end
+// exit at once.  (A persistent form -- a resident-size grid taking items from
+// a ticket counter -- measured slower on the mixed batch: the ticket's
+// atomic sits between items, and the loop kept ~20 more registers live.)
+template <typename Tag, int D>
+__global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_kernel(
+    DecodeArgs a, const int4* __restrict__ items) {
+  extern __shared__ float comb[];
+  const int heads = a.hkv * a.head_blocks;
+  const int4 it = items[blockIdx.x / heads];
+  if (it.x < 0) return;
+  decode_item<Tag, D, false>(a, it, blockIdx.x % heads, comb);
+}
+
+// decode_items_kernel over an INT8 cache (same items, partitions and
+// partials); the V scale multiplies each merged result before it is stored.
+template <typename Tag, int D>
+__global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_i8_kernel(
+    DecodeArgs a, const int4* __restrict__ items) {
+  extern __shared__ float comb[];
+  const int heads = a.hkv * a.head_blocks;
+  const int4 it = items[blockIdx.x / heads];
+  if (it.x < 0) return;
+  decode_item<Tag, D, true>(a, it, blockIdx.x % heads, comb);
 }
 
 // ---- generic VALU path ----
@@ -610,7 +586,7 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   int* arrivals = fused_merge ? reinterpret_cast<int*>(ws + lay.arrivals) : nullptr;
   if (use_mfma || sp.np > 1) {
     PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np, arrivals,
-                fused_merge ? num_seqs * hq : 0};
+                fused_merge ? num_seqs * hkv * head_blocks : 0};  // one per (sequence, head group)
     if (write) {  // the step's cache writes ride along with the plan
       const int64_t wgs = 1 + (write->threads() + kThreads - 1) / kThreads;
       const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);

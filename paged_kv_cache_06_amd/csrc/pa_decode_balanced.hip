@@ -5,6 +5,8 @@
 #include "pa_decode_balanced.h"
 #include "pa_decode_common.h"
 
+#include <mutex>
+
 namespace pa {
 namespace {
 
@@ -693,10 +695,12 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
     size_t lds;
     int n;
   };
+  static std::mutex mu;  // host threads may launch concurrently
   static Entry cache[32];
   static int used = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
   for (int i = 0; i < used; ++i)
     if (cache[i].dev == dev && cache[i].fn == kernel && cache[i].lds == lds) return cache[i].n;
   int cus = 0, per_cu = 0;
