@@ -57,7 +57,7 @@ typedef int32_t pa_status;
 #define PA_ERR_INVALID_ARG (-1)   /* bad shape, pointer, position or size */
 #define PA_ERR_OUT_OF_BLOCKS (-2) /* the pool cannot serve the request; nothing changed */
 #define PA_ERR_BAD_BLOCK (-3)     /* block id out of range or not held */
-#define PA_ERR_UNSUPPORTED (-4)   /* valid request this build does not implement */
+#define PA_ERR_UNSUPPORTED (-4)   /* valid request the library does not implement */
 #define PA_ERR_DEVICE (-5)        /* HIP launch or runtime error */
 #define PA_ERR_WORKSPACE (-6)     /* workspace missing or too small */
 #define PA_ERR_HOST_MEMORY (-7)   /* a host allocation failed; nothing changed */

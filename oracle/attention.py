@@ -11,7 +11,7 @@ bytes, not results: the output equals attention over the sequence laid out
 contiguously ("What PagedAttention is and what it changed in LLM serving",
 sections "PagedAttention simply" and "FAQ").
 
-Readings (the pages print no attention formula; listed in the design doc):
+Readings (the pages print no attention formula):
 * textbook scaled dot-product attention, softmax over positions 0..len-1;
   the scale is an argument (the workloads use 1/sqrt(head_dim));
 * query head h reads KV head h // (num_q_heads // num_kv_heads);

@@ -14,7 +14,7 @@ slows down", section "How PagedAttention fixes this"; "PagedAttention for the
 professional", results list: parallel sampling with n=4 costs about the memory
 of n=1).
 
-Readings where the pages leave a step open (listed in the design doc):
+Readings where the pages leave a step open:
 * the pool is a stack seeded from ``free_order``: the first ``alloc`` returns
   ``free_order[0]``; a block whose count drops to 0 is pushed back and is the
   next one handed out (in the shelves example a returned shelf is reused

@@ -6,7 +6,7 @@ the intermediate", section "KV Cache Quantization"; the same page's trade-offs
 list the extra dequantization latency, and its next-step list says to try INT8
 before INT4).
 
-Readings where the page leaves the scheme open (listed in the design doc):
+Readings where the page leaves the scheme open:
 * symmetric quantization with one fp32 scale s > 0 per (KV head, channel),
   one scale array for K and one for V, supplied by the caller (calibration is
   the caller's business);

@@ -1,6 +1,6 @@
 """Reference run of one workload: allocate, write, copy, attend (oracle; tests only).
 
-Order of a batch (the reading taken of the pages' serving story; DESIGN.md):
+Order of a batch (the reading taken of the pages' serving story):
 
   A1  for each sequence in index order: the first sequence of a shared prompt
       allocates and writes the prompt; every later sequence of that prompt

@@ -21,6 +21,8 @@ CASES = [
     ([19, 40], [3, 77], 4, 4, 64, "bf16"),                              # MHA, 16 queries a wave
     ([25, 9], [100, 7], 12, 4, 128, "bf16"),                            # G = 3
     ([70, 1], [0, 2000], 16, 8, 64, "f16"),                             # G = 2, whole prompt
+    ([11, 3], [50, 400], 48, 1, 128, "bf16"),                           # G = 48: 2 head blocks, 2nd half full
+    ([6, 17], [90, 3], 64, 1, 64, "f16"),                               # G = 64: 2 full head blocks
     # many sequences of mixed lengths: work-groups handed out longest first
     (np.random.default_rng(5).integers(1, 70, 40).tolist(),
      np.random.default_rng(6).integers(0, 600, 40).tolist(), 8, 2, 128, "bf16"),
