@@ -143,3 +143,24 @@ def test_workspace_size_closed_form():
             == pa.decode_workspace_bytes(s, hq, d, 4096, auto_p))
     with pytest.raises(ValueError):
         pa.Pool(4, free_order=[0, 1])
+
+
+def test_c_client_links_and_runs_against_the_header_alone(tmp_path):
+    """A C99 program that sees only include/pa.h and links libpa.so drives the
+    host-side pool through the ABI (no device calls)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib = pa.lib_path()
+    exe = tmp_path / "c_client"
+    cmd = [cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_client.c"),
+           "-L", os.path.dirname(lib), "-l:" + os.path.basename(lib),
+           "-Wl,-rpath," + os.path.dirname(lib), "-o", str(exe)]
+    built = subprocess.run(cmd, capture_output=True, text=True)
+    assert built.returncode == 0, built.stderr
+    ran = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert ran.returncode == 0, ran.stdout + ran.stderr
+    assert "0 failure(s)" in ran.stdout
