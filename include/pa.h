@@ -240,7 +240,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
  * may be device memory or pinned host memory (hipHostMalloc; torch
  * pin_memory), reached through its device mapping; PA_ERR_INVALID_ARG for
  * memory the device cannot reach.  Pairs with an id out of range are
- * skipped.  The dsts must be distinct. */
+ * skipped.  The dsts must be distinct.  Like every call here it is only
+ * enqueued on `stream`: host memory it reads (pairs, a host cache) must stay
+ * allocated and unchanged until the stream has passed it. */
 pa_status pa_transfer_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks,
                              void* dst_k, void* dst_v, int32_t dst_num_blocks,
                              const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,

@@ -477,9 +477,28 @@ def new_host_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype):
             torch.empty(vshape, dtype=dtype, pin_memory=True))
 
 
+# Host tensors read by an enqueued transfer, kept alive (with an event
+# recorded after the launch) until the stream has passed it: torch's pinned
+# allocator would otherwise hand a freed pinned buffer to the next
+# pin_memory() while the transfer still reads it.
+_host_inflight: list = []
+
+
+def _keep_host_alive(tensors, stream) -> None:
+    torch = _torch()
+    _host_inflight[:] = [(e, ts) for e, ts in _host_inflight if not e.query()]
+    host = [t for t in tensors if not t.is_cuda]
+    if host:
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        _host_inflight.append((ev, host))
+
+
 def transfer_blocks(src_k, src_v, dst_k, dst_v, block_pairs) -> None:
     """Copy blocks between two caches of one shape (device or pinned host):
-    block_pairs int64 [n, 2] of (src, dst), on the device or pinned."""
+    block_pairs int64 [n, 2] of (src, dst), on the device or pinned.  The copy
+    is enqueued on the current stream; host tensors among the arguments are
+    kept alive until the stream has passed it."""
     torch = _torch()
     nbs, hkv, d = _cache_dims(src_k, src_v)
     nbd, hkv2, d2 = _cache_dims(dst_k, dst_v)
@@ -492,10 +511,12 @@ def transfer_blocks(src_k, src_v, dst_k, dst_v, block_pairs) -> None:
           "block_pairs must be contiguous int64 [n, 2], on the device or pinned")
     dev = next(t for t in (src_k, dst_k, block_pairs) if t.is_cuda) \
         if any(t.is_cuda for t in (src_k, dst_k, block_pairs)) else None
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    cur = torch.cuda.current_stream(dev)
+    stream = ctypes.c_void_p(cur.cuda_stream)
     _check(load().pa_transfer_blocks(_ptr(src_k), _ptr(src_v), nbs, _ptr(dst_k), _ptr(dst_v), nbd,
                                      _ptr(block_pairs), block_pairs.shape[0], hkv, d,
                                      _dtype_code(src_k), stream), "pa_transfer_blocks")
+    _keep_host_alive((src_k, src_v, dst_k, dst_v, block_pairs), cur)
 
 
 def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
