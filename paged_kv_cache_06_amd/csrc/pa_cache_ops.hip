@@ -125,21 +125,18 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   if (num_tokens == 0) return PA_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int x = 16 / elem_bytes(dtype);
-  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / x);
-  const int64_t grid = (total + 255) / 256;
-  if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * kBlock;
+  const auto w32 = cache_write_args<float>(key, value, k_cache, v_cache, slot_mapping,
+                                           num_tokens, num_slots, num_kv_heads, head_dim);
+  const auto w16 = cache_write_args<uint16_t>(key, value, k_cache, v_cache, slot_mapping,
+                                              num_tokens, num_slots, num_kv_heads, head_dim);
+  const int64_t grid = ((dtype == PA_F32 ? w32.threads() : w16.threads()) + 255) / 256;
+  if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
   const int slot = timing_start(PA_KERNEL_RESHAPE_AND_CACHE, st);
-  if (dtype == PA_F32) {
-    reshape_and_cache_kernel<float><<<dim3(grid), dim3(256), 0, st>>>(cache_write_args<float>(
-        key, value, k_cache, v_cache, slot_mapping, num_tokens, num_slots, num_kv_heads,
-        head_dim));
-  } else {
-    reshape_and_cache_kernel<uint16_t><<<dim3(grid), dim3(256), 0, st>>>(
-        cache_write_args<uint16_t>(key, value, k_cache, v_cache, slot_mapping, num_tokens,
-                                   num_slots, num_kv_heads, head_dim));
-  }
+  if (dtype == PA_F32)
+    reshape_and_cache_kernel<float><<<dim3(grid), dim3(256), 0, st>>>(w32);
+  else
+    reshape_and_cache_kernel<uint16_t><<<dim3(grid), dim3(256), 0, st>>>(w16);
   const pa_status s = launch_status();
   timing_stop(slot, st);
   return s;
@@ -159,10 +156,14 @@ pa_status pa_reshape_and_cache_int8(const void* key, const void* value, void* k_
   if (!key || !value || !k_cache || !v_cache || !slot_mapping || !k_scale || !v_scale)
     return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / 16);
-  const int64_t grid = (total + 255) / 256;
-  if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * kBlock;
+  // thread count: every CacheWriteI8Args<Tag> of these sizes has the same one
+  const int64_t threads = CacheWriteI8Args<F32T>{nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                 nullptr, nullptr, num_tokens, num_slots,
+                                                 num_kv_heads, head_dim}
+                              .threads();
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
   int8_t* kc = static_cast<int8_t*>(k_cache);
   int8_t* vc = static_cast<int8_t*>(v_cache);
   const int slot = timing_start(PA_KERNEL_RESHAPE_AND_CACHE, st);

@@ -675,6 +675,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 namespace pa {
 namespace {
 
+// Thread layout of a fused step's cache writes: one new token per sequence
+// (plain decode) shares no block with another, so window 1; more tokens than
+// sequences (a sequence appending a run) interleave windows of tokens.
+inline int step_window(int32_t num_tokens, int32_t num_seqs) {
+  return num_tokens <= num_seqs ? 1 : kWindow;
+}
+
 // The new tokens of a fused decode step (pa_decode_step); key == nullptr: none.
 struct StepWrite {
   const void* key;
@@ -740,17 +747,19 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   const int64_t num_slots = static_cast<int64_t>(wr.num_blocks) * kBlock;
   switch (dtype) {
     case PA_BF16: {
-      const auto w = cache_write_args<uint16_t>(wr.key, wr.value, const_cast<void*>(k_cache),
-                                                const_cast<void*>(v_cache), wr.slots,
-                                                wr.num_tokens, num_slots, num_kv_heads, head_dim);
+      auto w = cache_write_args<uint16_t>(wr.key, wr.value, const_cast<void*>(k_cache),
+                                          const_cast<void*>(v_cache), wr.slots, wr.num_tokens,
+                                          num_slots, num_kv_heads, head_dim);
+      w.window = step_window(wr.num_tokens, num_seqs);
       return launch<BF16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                            num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
                            ws, use_mfma, st, nullptr, nullptr, fused ? &w : nullptr);
     }
     case PA_F16: {
-      const auto w = cache_write_args<uint16_t>(wr.key, wr.value, const_cast<void*>(k_cache),
-                                                const_cast<void*>(v_cache), wr.slots,
-                                                wr.num_tokens, num_slots, num_kv_heads, head_dim);
+      auto w = cache_write_args<uint16_t>(wr.key, wr.value, const_cast<void*>(k_cache),
+                                          const_cast<void*>(v_cache), wr.slots, wr.num_tokens,
+                                          num_slots, num_kv_heads, head_dim);
+      w.window = step_window(wr.num_tokens, num_seqs);
       return launch<F16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
                           ws, use_mfma, st, nullptr, nullptr, fused ? &w : nullptr);
@@ -796,17 +805,19 @@ pa_status decode_int8_impl(const void* q, const void* k_cache, const void* v_cac
   int8_t* kc = static_cast<int8_t*>(const_cast<void*>(k_cache));
   int8_t* vc = static_cast<int8_t*>(const_cast<void*>(v_cache));
   if (dtype == PA_BF16) {
-    const CacheWriteI8Args<BF16T> w{static_cast<const uint16_t*>(wr.key),
-                                    static_cast<const uint16_t*>(wr.value), kc, vc, wr.slots,
-                                    k_scale, v_scale, wr.num_tokens, num_slots, num_kv_heads,
-                                    head_dim};
+    CacheWriteI8Args<BF16T> w{static_cast<const uint16_t*>(wr.key),
+                              static_cast<const uint16_t*>(wr.value), kc, vc, wr.slots,
+                              k_scale, v_scale, wr.num_tokens, num_slots, num_kv_heads,
+                              head_dim};
+    w.window = step_window(wr.num_tokens, num_seqs);
     return launch<BF16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                          num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
                          ws, true, st, k_scale, v_scale, fused ? &w : nullptr);
   }
-  const CacheWriteI8Args<F16T> w{static_cast<const uint16_t*>(wr.key),
-                                 static_cast<const uint16_t*>(wr.value), kc, vc, wr.slots, k_scale,
-                                 v_scale, wr.num_tokens, num_slots, num_kv_heads, head_dim};
+  CacheWriteI8Args<F16T> w{static_cast<const uint16_t*>(wr.key),
+                           static_cast<const uint16_t*>(wr.value), kc, vc, wr.slots, k_scale,
+                           v_scale, wr.num_tokens, num_slots, num_kv_heads, head_dim};
+  w.window = step_window(wr.num_tokens, num_seqs);
   return launch<F16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out, num_seqs,
                       num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp, ws, true, st,
                       k_scale, v_scale, fused ? &w : nullptr);
