@@ -50,14 +50,30 @@ def traffic_file(kernel):
     return os.path.join(ROOT, "profiles", f"decode_traffic_{kernel}.json")
 
 
-def decode_bytes(w, int8=False):
+def unique_kv_tokens(lens, rows):
+    """Cached positions of distinct physical blocks that one decode call reads:
+    a block shared by several tables counts once, with the most positions any
+    of them attends in it (shared prefixes are read from HBM once)."""
+    import numpy as np
+    used = {}
+    for s, n in enumerate(np.asarray(lens, dtype=np.int64)):
+        for i in range(int(-(-n // 16))):
+            b = int(rows[s][i])
+            used[b] = max(used.get(b, 0), int(min(16, n - 16 * i)))
+    return sum(used.values())
+
+
+def decode_bytes(w, int8=False, rows=None):
     """Algorithmic bytes of one decode call: every cached K and V element of every
-    (sequence, KV head) once, q and out once, table entries in use and lengths
-    (INT8 cache: 1-byte elements plus the two [Hkv, D] fp32 scale arrays)."""
+    (sequence, KV head) once -- with `rows` (the block tables), every element of
+    every distinct physical block once, so that shared prefix blocks count once
+    -- q and out once, table entries in use and lengths (INT8 cache: 1-byte
+    elements plus the two [Hkv, D] fp32 scale arrays)."""
     import numpy as np
     lens = np.asarray(w.context_lens, dtype=np.int64)
     e = w.elem_bytes
-    kv = int(lens.sum()) * 2 * w.num_kv_heads * w.head_dim * (1 if int8 else e)
+    kv_tokens = int(lens.sum()) if rows is None else unique_kv_tokens(lens, rows)
+    kv = kv_tokens * 2 * w.num_kv_heads * w.head_dim * (1 if int8 else e)
     qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * e
     tables = 4 * int((-(-lens // 16)).sum())
     scales = 2 * w.num_kv_heads * w.head_dim * 4 if int8 else 0
@@ -65,7 +81,8 @@ def decode_bytes(w, int8=False):
 
 
 def step_bytes(w, db, int8=False):
-    """decode bytes + the step's token writes (read + write + slots) + block copies."""
+    """decode bytes (shared blocks once) + the step's token writes (read + write
+    + slots) + block copies."""
     B = db.phases[2]
     e = w.elem_bytes
     ec = 1 if int8 else e
@@ -75,7 +92,7 @@ def step_bytes(w, db, int8=False):
         writes += 2 * w.num_kv_heads * w.head_dim * 4
     block = w.num_kv_heads * 16 * w.head_dim * ec
     copies = B.pairs.shape[0] * 2 * (2 * block) + 16 * B.pairs.shape[0]
-    return decode_bytes(w, int8) + writes + copies
+    return decode_bytes(w, int8, db.bm.rows) + writes + copies
 
 
 def source_hash(kernel):
@@ -441,7 +458,8 @@ def main():
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     sbytes = step_bytes(w, db, int8)
-    dbytes = decode_bytes(w, int8)
+    dbytes = decode_bytes(w, int8, db.bm.rows)      # shared blocks once: the roofline's bytes
+    logical = decode_bytes(w, int8)                 # every sequence's blocks, shared or not
     tokens = int(np.sum(w.context_lens))
     dec = kt["decode"]
     dec_ms = dec["ms"] / max(1, dec["launches"])
@@ -488,6 +506,9 @@ def main():
                      "avg_launch_ms": round(dec_ms, 5),
                      "traffic": traffic},
     }
+    if logical != dbytes:  # shared prefixes: also the per-sequence (logical) figure
+        result["logical_bytes_per_launch"] = logical
+        result["logical_gb_per_s"] = round(logical / (dec_ms * 1e-3) / 1e9, 2)
     if args.calibrate_copy > 0:
         calibration_copies(args.calibrate_copy)
         result["calibration_copy_bytes"] = args.calibrate_copy << 20
