@@ -81,19 +81,60 @@ __host__ __device__ inline int plan_capacity(int num_seqs, int np_max) {
 
 struct PlanArgs {
   const int32_t* lens;
-  int4* items;  // [num_seqs * np_max] (sequence, partition, length, 0); sequence -1 past the end
+  // [num_seqs * np_max] (sequence, partition, length, partition size);
+  // sequence -1 past the end
+  int4* items;
   int* split;   // [num_seqs] sequences with more than one partition, then -1
   int* meta;    // [0] items, [1] split sequences
   int num_seqs, max_blocks, part_size, np_max;
   int* arrivals;     // per (sequence, head group): partials stored so far (zeroed here)
   int num_arrivals;
+  int max_items;     // items the decode grid serves (see plan_partition)
 };
 
 __device__ __forceinline__ int plan_len(const PlanArgs& a, int i) {
   return min(max(a.lens[i], 0), a.max_blocks * kBlock);
 }
-__device__ __forceinline__ int plan_parts(const PlanArgs& a, int len) {
-  return min((len + a.part_size - 1) / a.part_size, a.np_max);
+__device__ __forceinline__ int plan_parts(const PlanArgs& a, int len, int part) {
+  return min((len + part - 1) / part, a.np_max);
+}
+
+// The partition size of a list longer than max_items.  The decode grid is
+// sized for max_items items -- the list's full capacity (every sequence at the
+// longest length) would dispatch thousands of work-groups that find only an
+// end marker -- so such a list takes part_size doubled, up to kDoublings
+// times, until it fits, else one partition per sequence.  Larger partitions
+// are fewer, longer items over the same blocks.  Sequences hold at least one
+// item each (an empty one too), and max_items >= num_seqs.
+constexpr int kDoublings = 6;
+
+__device__ __forceinline__ int plan_partition(const PlanArgs& a, int* wave_tot) {
+  const int S = a.num_seqs;
+  const int whole = a.max_blocks * kBlock;
+  const int per = (S + kThreads - 1) / kThreads;
+  const int i0 = threadIdx.x * per;
+  const int i1 = min(S, i0 + per);
+  int cnt[kDoublings + 1];
+#pragma unroll
+  for (int k = 0; k <= kDoublings; ++k) cnt[k] = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int len = plan_len(a, i);
+#pragma unroll
+    for (int k = 0; k <= kDoublings; ++k) {
+      const int part = static_cast<int>(min(static_cast<int64_t>(a.part_size) << k,
+                                            static_cast<int64_t>(whole)));
+      cnt[k] += max(plan_parts(a, len, part), 1);
+    }
+  }
+  int excl[kDoublings + 1], all[kDoublings + 1];
+  block_scan<kDoublings + 1>(cnt, excl, all, wave_tot);
+  __syncthreads();  // wave_tot is written again by the caller's scan
+#pragma unroll
+  for (int k = 0; k <= kDoublings; ++k)
+    if (all[k] <= a.max_items)
+      return static_cast<int>(min(static_cast<int64_t>(a.part_size) << k,
+                                  static_cast<int64_t>(whole)));
+  return whole;
 }
 
 // The item list, largest first (see the file header).  One work-group; each
@@ -101,26 +142,39 @@ __device__ __forceinline__ int plan_parts(const PlanArgs& a, int len) {
 // per-class counts places every item, in sequence order within a class.
 constexpr int kPlanVals = kClasses + 2;  // classes, full partitions, split sequences
 
+// Per-class item counts of this thread's sequences i0 .. i1-1 at partition
+// size `part`, then full partitions, then split sequences.
+__device__ __forceinline__ void plan_count(const PlanArgs& a, int part, int i0, int i1,
+                                           int* cnt) {
+#pragma unroll
+  for (int c = 0; c < kPlanVals; ++c) cnt[c] = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int len = plan_len(a, i);
+    const int np = plan_parts(a, len, part);
+    const int cls = size_class(np > 0 ? len - (np - 1) * part : 0, part);
+#pragma unroll
+    for (int c = 0; c < kClasses; ++c) cnt[c] += cls == c;
+    cnt[kClasses] += max(np - 1, 0);
+    cnt[kClasses + 1] += np > 1;
+  }
+}
+
 __device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
   constexpr int kVals = kPlanVals;
   const int S = a.num_seqs;
   const int per = (S + kThreads - 1) / kThreads;
   const int i0 = threadIdx.x * per;
   const int i1 = min(S, i0 + per);
-  int cnt[kVals];
-#pragma unroll
-  for (int c = 0; c < kVals; ++c) cnt[c] = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int len = plan_len(a, i);
-    const int np = plan_parts(a, len);
-    const int cls = size_class(np > 0 ? len - (np - 1) * a.part_size : 0, a.part_size);
-#pragma unroll
-    for (int c = 0; c < kClasses; ++c) cnt[c] += cls == c;
-    cnt[kClasses] += max(np - 1, 0);
-    cnt[kClasses + 1] += np > 1;
-  }
-  int excl[kVals], all[kVals];
+  int part = a.part_size;
+  int cnt[kVals], excl[kVals], all[kVals];
+  plan_count(a, part, i0, i1, cnt);
   block_scan<kVals>(cnt, excl, all, wave_tot);
+  if (all[kClasses] + S > a.max_items) {  // the same on every thread
+    __syncthreads();  // the scan's totals are read before they are rewritten
+    part = plan_partition(a, wave_tot);
+    plan_count(a, part, i0, i1, cnt);
+    block_scan<kVals>(cnt, excl, all, wave_tot);
+  }
   // item positions: full partitions from 0, then classes in order
   const int num_full = all[kClasses];
   int pos[kClasses];
@@ -134,14 +188,14 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
   int split_pos = excl[kClasses + 1];
   for (int i = i0; i < i1; ++i) {
     const int len = plan_len(a, i);
-    const int np = plan_parts(a, len);
-    for (int p = 0; p + 1 < np; ++p) a.items[full_pos++] = make_int4(i, p, len, 0);
-    const int cls = size_class(np > 0 ? len - (np - 1) * a.part_size : 0, a.part_size);
+    const int np = plan_parts(a, len, part);
+    for (int p = 0; p + 1 < np; ++p) a.items[full_pos++] = make_int4(i, p, len, part);
+    const int cls = size_class(np > 0 ? len - (np - 1) * part : 0, part);
     int at = 0;
 #pragma unroll
     for (int c = 0; c < kClasses; ++c)
       if (cls == c) at = pos[c]++;
-    a.items[at] = make_int4(i, max(np - 1, 0), len, 0);
+    a.items[at] = make_int4(i, max(np - 1, 0), len, part);
     if (np > 1) a.split[split_pos++] = i;
   }
   const int total = num_full + S;
@@ -229,9 +283,9 @@ __device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int s, int gh
 // applied to each combined accumulator.
 template <typename Tag, int D, int W>
 __device__ __forceinline__ void finish_item(const DecodeArgs& a, float* comb, int s, int p,
-                                            int len, int g, int h0, int nh, int gh,
+                                            int len, int part, int g, int h0, int nh, int gh,
                                             const float* vs) {
-  const int nparts = min((len + a.part_size - 1) / a.part_size, a.np_max);
+  const int nparts = min((len + part - 1) / part, a.np_max);
   const size_t row0 = static_cast<size_t>(s) * a.hq_total + g * a.group + h0;
   for (int e = threadIdx.x; e < nh * D; e += W * kWave) {
     const int h = e / D, d = e % D;
@@ -261,18 +315,19 @@ __device__ __forceinline__ void finish_item(const DecodeArgs& a, float* comb, in
   if (nparts > 1 && a.arrivals) merge_if_last<Tag, D, W>(a, s, gh, nparts, row0, nh);
 }
 
-// One work item (sequence it.x, partition it.y, length it.z) for head group
+// One work item (sequence it.x, partition it.y of it.w positions, length
+// it.z) for head group
 // gh (KV head x query head block): the waves take the item's blocks
 // round-robin, then finish_item.
 template <typename Tag, int D, bool kInt8>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int4 it, int gh, float* comb) {
   constexpr int W = kItemWaves;
-  const int s = it.x, p = it.y, len = it.z;
+  const int s = it.x, p = it.y, len = it.z, part = it.w;
   const int g = gh / a.head_blocks, h0 = (gh % a.head_blocks) * 16;
   const int nh = min(16, a.group - h0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int start = p * a.part_size;
-  const int end = min(len, start + a.part_size);
+  const int start = p * part;
+  const int end = min(len, start + part);
   const int nblk = max(end - start + kBlock - 1, 0) / kBlock;
   const int b_first = start / kBlock + wave;
   const int count = nblk > wave ? (nblk - wave + W - 1) / W : 0;
@@ -290,7 +345,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int4 it, int gh
   }
   stage_partials<D, W>(comb, a.nh_max, nh, st);
   __syncthreads();
-  finish_item<Tag, D, W>(a, comb, s, p, len, g, h0, nh, gh,
+  finish_item<Tag, D, W>(a, comb, s, p, len, part, g, h0, nh, gh,
                          kInt8 ? a.v_scale + static_cast<size_t>(g) * D : nullptr);
 }
 
@@ -572,8 +627,16 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   const int group = hq / hkv;
   const int head_blocks = use_mfma ? (group + 15) / 16 : 1;
   if (static_cast<int64_t>(sp.np) * num_seqs * hq > 0x7fffffff / 2) return PA_ERR_INVALID_ARG;
-  const int64_t grid = use_mfma ? static_cast<int64_t>(plan_capacity(num_seqs, sp.np)) * hkv *
-                                      head_blocks
+  // the matrix-core path's grid: items for two per sequence and at least 2048
+  // work-groups, or the list's whole capacity when that is smaller; a longer
+  // list takes larger partitions (plan_partition).  The merge kernel of the
+  // other paths reads partitions of sp.part, so their plan keeps it.
+  const bool fused_merge = use_mfma && sp.np > 1 && kFusedMerge;
+  const int cap = plan_capacity(num_seqs, sp.np);
+  const int heads = hkv * head_blocks;
+  const int item_grid =
+      fused_merge ? std::min(cap, std::max(2 * num_seqs, (2048 + heads - 1) / heads)) : cap;
+  const int64_t grid = use_mfma ? static_cast<int64_t>(item_grid) * heads
                                 : static_cast<int64_t>(sp.np) * num_seqs * hq;
   const Layout lay = workspace_layout(num_seqs, hq, head_dim, sp);
   int* meta = reinterpret_cast<int*>(ws + lay.meta);
@@ -582,11 +645,11 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   float* ws_ml = reinterpret_cast<float*>(ws + lay.ml);
   float* ws_acc = reinterpret_cast<float*>(ws + lay.acc);
   // the matrix-core kernels merge split sequences themselves (merge_if_last)
-  const bool fused_merge = use_mfma && sp.np > 1 && kFusedMerge;
   int* arrivals = fused_merge ? reinterpret_cast<int*>(ws + lay.arrivals) : nullptr;
   if (use_mfma || sp.np > 1) {
     PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np, arrivals,
-                fused_merge ? num_seqs * hkv * head_blocks : 0};  // one per (sequence, head group)
+                fused_merge ? num_seqs * hkv * head_blocks : 0,  // one per (sequence, head group)
+                item_grid};
     if (write) {  // the step's cache writes ride along with the plan
       const int64_t wgs = 1 + (write->threads() + kThreads - 1) / kThreads;
       const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);
