@@ -299,7 +299,11 @@ pa_status pa_decode_set_max_groups(int32_t max_groups);
  *                 second pass (running max / log-sum-exp rule);
  *                 a positive multiple of 16: sequences longer than it are
  *                 split into partitions of that many positions, merged the
- *                 same way;
+ *                 same way (on the matrix-core path, when that would make
+ *                 more than max(2 * num_seqs, ceil(2048 / (num_kv_heads *
+ *                 ceil(group / 16)))) partitions in all, the size is doubled
+ *                 until it does not, at most 6 times, else one partition per
+ *                 sequence);
  *                 PA_PARTITION_NONE: one pass over each whole sequence;
  *                 PA_PARTITION_AUTO: the partition size
  *                 pa_decode_auto_partition gives
