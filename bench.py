@@ -103,6 +103,17 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
+def launch_percentiles(kind):
+    """p10, median and p90 of the launch times (ms, HIP events) of one kernel
+    kind over the timed pass just ended."""
+    import numpy as np
+    import paged_kv_cache_06_amd as pa
+    ms = pa.timing_launches(kind)
+    if not ms:
+        return None
+    return [round(float(v), 5) for v in np.percentile(np.asarray(ms), [10, 50, 90])]
+
+
 def load_traffic(workload, kernel):
     """Counter-measured HBM bytes per launch of `kernel`, if taken on its current source."""
     try:
@@ -335,6 +346,7 @@ def prefill_bench(args):
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops,
                      "avg_launch_ms": round(k_ms, 5),
+                     "launch_ms_p10_p50_p90": launch_percentiles("prefill"),
                      "traffic": load_traffic(w.name, "prefill_kernel")},
     }
     if args.calibrate_copy > 0:
@@ -504,6 +516,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": dbytes,
                      "avg_launch_ms": round(dec_ms, 5),
+                     "launch_ms_p10_p50_p90": launch_percentiles("decode"),
                      "traffic": traffic},
     }
     if logical != dbytes:  # shared prefixes: also the per-sequence (logical) figure

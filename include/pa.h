@@ -437,6 +437,16 @@ pa_status pa_timing_begin(int32_t capacity);
 pa_status pa_timing_end(double* ms_out /* [PA_NUM_KERNEL_KINDS] */,
                         int32_t* launches_out /* [PA_NUM_KERNEL_KINDS] */);
 
+/* The milliseconds of each launch of kernel kind `kind` that the last
+ * pa_timing_end measured, in launch order (for medians and percentiles):
+ * the first `capacity` of them into ms_out (host memory, which may be NULL
+ * when capacity is 0), their count into *count_out (which may exceed
+ * capacity).  Valid until the next pa_timing_end.  PA_ERR_INVALID_ARG for a
+ * kind outside [0, PA_NUM_KERNEL_KINDS), a negative capacity or a NULL
+ * pointer that is needed. */
+pa_status pa_timing_launches(int32_t kind, double* ms_out, int32_t capacity,
+                             int32_t* count_out);
+
 #ifdef __cplusplus
 }
 #endif

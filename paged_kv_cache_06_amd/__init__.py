@@ -28,7 +28,7 @@ __all__ = [
     "decode_set_max_groups", "reshape_and_cache_int8", "paged_attention_decode_int8",
     "swap_blocks", "transfer_blocks", "new_host_kv_cache", "paged_attention_prefill",
     "decode_step", "decode_step_int8",
-    "new_kv_cache", "new_kv_cache_int8", "logical_view", "timing_begin", "timing_end", "status_string",
+    "new_kv_cache", "new_kv_cache_int8", "logical_view", "timing_begin", "timing_end", "timing_launches", "status_string",
 ]
 
 BLOCK_SIZE = 16
@@ -99,6 +99,7 @@ _SIGNATURES = {
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_sz, _c_i32, _c_p]),
     "pa_timing_begin": (_c_i32, [_c_i32]),
     "pa_timing_end": (_c_i32, [ctypes.POINTER(ctypes.c_double), _P_I32]),
+    "pa_timing_launches": (_c_i32, [_c_i32, ctypes.POINTER(ctypes.c_double), _c_i32, _P_I32]),
 }
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "out of blocks", -3: "bad block id",
@@ -714,3 +715,14 @@ def timing_end() -> dict:
     n = (ctypes.c_int32 * len(KERNEL_KINDS))()
     _check(load().pa_timing_end(ms, n), "pa_timing_end")
     return {k: {"ms": ms[i], "launches": n[i]} for i, k in enumerate(KERNEL_KINDS)}
+
+
+def timing_launches(kind: str) -> list:
+    """Milliseconds of each launch of `kind` (a name of KERNEL_KINDS) that the
+    last timing_end measured, in launch order."""
+    i = KERNEL_KINDS.index(kind)
+    n = ctypes.c_int32(0)
+    _check(load().pa_timing_launches(i, None, 0, ctypes.byref(n)), "pa_timing_launches")
+    ms = (ctypes.c_double * max(1, n.value))()
+    _check(load().pa_timing_launches(i, ms, n.value, ctypes.byref(n)), "pa_timing_launches")
+    return [ms[j] for j in range(n.value)]

@@ -3,6 +3,7 @@
 // Events are recorded on the launch's own stream, so the measured interval is
 // the kernel's run time on that stream (plus the event overhead, a few
 // microseconds at most).  Single-threaded use, like the rest of the library.
+#include <utility>
 #include <vector>
 
 #include "pa_common.h"
@@ -18,6 +19,7 @@ struct Timing {
   bool active = false;
   int used = 0;
   std::vector<Record> recs;
+  std::vector<std::pair<int, double>> last;  // (kind, ms) of the last pa_timing_end
 };
 
 Timing& state() {
@@ -73,6 +75,7 @@ pa_status pa_timing_end(double* ms_out, int32_t* launches_out) {
     launches_out[k] = 0;
   }
   pa_status st = PA_OK;
+  t.last.clear();
   for (int i = 0; i < t.used; ++i) {
     Record& r = t.recs[i];
     if (r.kind < 0 || r.kind >= PA_NUM_KERNEL_KINDS) continue;
@@ -84,10 +87,26 @@ pa_status pa_timing_end(double* ms_out, int32_t* launches_out) {
     }
     ms_out[r.kind] += ms;
     launches_out[r.kind] += 1;
+    t.last.emplace_back(r.kind, static_cast<double>(ms));
   }
   t.active = false;
   t.used = 0;
   return st;
+}
+
+pa_status pa_timing_launches(int32_t kind, double* ms_out, int32_t capacity,
+                             int32_t* count_out) {
+  if (kind < 0 || kind >= PA_NUM_KERNEL_KINDS || capacity < 0 || !count_out ||
+      (capacity > 0 && !ms_out))
+    return PA_ERR_INVALID_ARG;
+  int32_t n = 0;
+  for (const auto& e : state().last) {
+    if (e.first != kind) continue;
+    if (n < capacity) ms_out[n] = e.second;
+    ++n;
+  }
+  *count_out = n;
+  return PA_OK;
 }
 
 }  // extern "C"

@@ -107,6 +107,24 @@ def test_host_only_calls_and_argument_errors_without_a_gpu():
     assert dec8(part=256) == -6  # no workspace
 
 
+def test_timing_launch_list_without_launches():
+    # an empty timed pass records no events (no device call): every kind then
+    # reports no launches, and bad arguments are refused
+    lib = pa.load()
+    assert lib.pa_timing_begin(0) == 0
+    ms = (ctypes.c_double * len(pa.KERNEL_KINDS))()
+    n = (ctypes.c_int32 * len(pa.KERNEL_KINDS))()
+    assert lib.pa_timing_end(ms, n) == 0
+    assert list(n) == [0] * len(pa.KERNEL_KINDS)
+    for kind in pa.KERNEL_KINDS:
+        assert pa.timing_launches(kind) == []
+    count = ctypes.c_int32(-1)
+    assert lib.pa_timing_launches(len(pa.KERNEL_KINDS), None, 0, ctypes.byref(count)) == -1
+    assert lib.pa_timing_launches(-1, None, 0, ctypes.byref(count)) == -1
+    assert lib.pa_timing_launches(0, None, 1, ctypes.byref(count)) == -1
+    assert lib.pa_timing_launches(0, None, 0, None) == -1
+
+
 def test_workspace_size_closed_form():
     # fixed partitions: plan (256-byte meta, 16 B per list entry -- sequences x
     # partitions rounded up to 32 entries -- and 4 B per sequence), then m, l

@@ -9,6 +9,7 @@ rest.
 """
 import numpy as np
 import pytest
+import torch
 
 import paged_kv_cache_06_amd as pa
 import workloads
@@ -157,6 +158,25 @@ def test_stale_workspace_does_not_matter():
                                   workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(bits_of(out), db.out_bits())
+
+
+def test_timing_records_every_launch():
+    print("[gpu] timing launch list", flush=True)
+    w = workloads.make_custom([5, 300, 1000, 2], hq=8, hkv=2, d=128, dtype="bf16", seed=4)
+    db, _ = _run_small(w, 64)
+    kc, vc = db.caches[0]
+    pa.timing_begin(16)
+    for _ in range(3):
+        pa.paged_attention_decode(db.q, kc, vc, db.tables, db.context_lens, w.scale,
+                                  torch.empty_like(db.out), max_context_len=db.max_context_len,
+                                  partition_size=64)
+    torch.cuda.synchronize()
+    kt = pa.timing_end()
+    ms = pa.timing_launches("decode")
+    assert kt["decode"]["launches"] == 3 and len(ms) == 3
+    assert all(v > 0 for v in ms)
+    assert abs(sum(ms) - kt["decode"]["ms"]) <= 1e-9 * max(1.0, kt["decode"]["ms"])
+    assert len(pa.timing_launches("decode_plan")) == 3
 
 
 def test_nan_in_table_padding_and_block_tails_does_not_leak():
