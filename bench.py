@@ -366,6 +366,26 @@ def calibration_copies(mib):
     torch.cuda.synchronize()
 
 
+def measured_copy_gbs(mib=1024, reps=10):
+    """HBM rate of a plain 1 GiB device-to-device copy on this machine (bytes read
+    plus bytes written per second, HIP events on the copy's stream): the
+    measured streaming reference beside the 8 TB/s specification."""
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record()
+    stop.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    del src, dst
+    return round(2 * (mib << 20) / (ms * 1e-3) / 1e9, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -519,6 +539,9 @@ def main():
                      "launch_ms_p10_p50_p90": launch_percentiles("decode"),
                      "traffic": traffic},
     }
+    copy_gbs = measured_copy_gbs()
+    result["roofline"]["measured_copy_gbs"] = copy_gbs
+    result["roofline"]["frac_of_measured_copy"] = round(achieved / copy_gbs, 4)
     if logical != dbytes:  # shared prefixes: also the per-sequence (logical) figure
         result["logical_bytes_per_launch"] = logical
         result["logical_gb_per_s"] = round(logical / (dec_ms * 1e-3) / 1e9, 2)
