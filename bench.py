@@ -166,6 +166,24 @@ def pmc_summary(fetch_dir, write_dir, workload, kernel, out_path=None):
     print(json.dumps(result))
 
 
+def host_cpu():
+    """The host's CPU model and the logical CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "usable_cpus": usable}
+
+
 def cpu_baseline(w, budget_s, int8=False):
     """The oracle (fp64 NumPy) on the first sequences of the batch, ~budget_s of work
     (INT8 cache: the oracle's quantization of each sequence's K/V, then attention
@@ -207,6 +225,7 @@ def cpu_baseline(w, budget_s, int8=False):
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "tokens_per_s": round(done_tokens / dt, 1),
+            "host": host_cpu(),
             "sample": f"{seqs} sequence decodes in {passes} pass(es) over the {w.num_seqs}-sequence "
                       f"batch ({done_tokens} attended tokens), oracle decode (fp64 NumPy "
                       f"gather{' + INT8 quantize/dequantize' if int8 else ''} + softmax "
