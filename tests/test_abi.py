@@ -107,6 +107,28 @@ def test_host_only_calls_and_argument_errors_without_a_gpu():
     assert dec8(part=256) == -6  # no workspace
 
 
+def test_empty_batches_are_no_ops_without_a_gpu():
+    # zero sequences / tokens / pairs: argument checks, then PA_OK before any
+    # pointer is read or anything is launched (NULL pointers are fine)
+    lib = pa.load()
+    for part in (pa.PARTITION_AUTO, pa.PARTITION_NONE, 256, pa.PARTITION_BALANCED):
+        assert lib.pa_paged_attention_decode(None, None, None, None, None, 1.0, None, 0, 8, 4,
+                                             128, 1, 16, part, None, 0, 2, None) == 0
+        assert lib.pa_paged_attention_decode_int8(None, None, None, None, None, None, None, 1.0,
+                                                  None, 0, 8, 4, 128, 1, 16,
+                                                  part if part != pa.PARTITION_BALANCED else 0,
+                                                  None, 0, 2, None) == 0
+    assert lib.pa_paged_attention_prefill(None, None, None, None, None, None, 1.0, None, 0, 8,
+                                          4, 128, 1, 16, 2, None) == 0
+    assert lib.pa_decode_step(None, None, None, 0, 4, None, None, None, None, None, 1.0, None,
+                              0, 8, 4, 128, 1, 16, pa.PARTITION_AUTO, None, 0, 2, None) == 0
+    assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 4, 4, 128, 2, None) == 0
+    assert lib.pa_copy_blocks(None, None, None, 0, 4, 4, 128, 2, None) == 0
+    # still checked when empty: a head count that does not divide
+    assert lib.pa_paged_attention_decode(None, None, None, None, None, 1.0, None, 0, 6, 4, 128,
+                                         1, 16, 0, None, 0, 2, None) == -1
+
+
 def test_timing_launch_list_without_launches():
     # an empty timed pass records no events (no device call): every kind then
     # reports no launches, and bad arguments are refused

@@ -37,6 +37,7 @@ CASES = [
     ([5, 48, 511, 512, 513, 1025], 32, 8, 128, "bf16"),   # G = 4
     ([7, 100, 300], 64, 8, 128, "bf16"),                    # G = 8
     ([9, 200], 32, 1, 128, "f16"),                          # MQA, G = 32 (2 head blocks)
+    ([9, 300, 1100], 64, 1, 128, "bf16"),                   # MQA, G = 64 (4 head blocks)
     ([31, 90], 4, 4, 128, "bf16"),                          # MHA, G = 1
     ([5, 77, 400], 4, 2, 64, "f16"),                        # G = 2
     ([20, 300, 1000], 12, 4, 128, "bf16"),                  # G = 3 (4-row head group)

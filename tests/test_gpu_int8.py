@@ -70,6 +70,7 @@ CASES = [
     ([3, 64, 129, 700, 1100], 16, 2, 64, "bf16"),
     ([7, 100, 300], 64, 8, 128, "bf16"),                    # G = 8
     ([9, 200], 32, 1, 128, "f16"),                          # MQA, 2 head blocks
+    ([9, 300, 1100], 64, 1, 64, "bf16"),                    # MQA, 4 head blocks
     ([31, 90], 4, 4, 64, "bf16"),                           # MHA
     ([20, 300, 1000], 12, 4, 128, "bf16"),                  # G = 3
     (list(range(600, 1000, 10)), 32, 8, 64, "bf16"),       # partition doubled by the plan
