@@ -15,7 +15,7 @@
 // the last of a sequence's work-groups to finish (merge_if_last), on the VALU
 // path by a second kernel; a sequence with one partition is normalised and
 // written directly.  A work-group of 4
-// waves serves one item: the waves take the item's 16-token blocks
+// waves (8 for the long partitions of long contexts) serves one item: the waves take the item's 16-token blocks
 // round-robin and merge their partials through LDS at the end.
 //
 // Scheduling.  Item sizes vary by two orders of magnitude in a mixed batch
@@ -315,13 +315,15 @@ __device__ __forceinline__ void finish_item(const DecodeArgs& a, float* comb, in
   if (nparts > 1 && a.arrivals) merge_if_last<Tag, D, W>(a, s, gh, nparts, row0, nh);
 }
 
+// Waves of a decode work-group: 4, or 8 for long partitions (item_waves).
+__host__ __device__ constexpr int item_threads(int waves) { return waves * kWave; }
+
 // One work item (sequence it.x, partition it.y of it.w positions, length
 // it.z) for head group
 // gh (KV head x query head block): the waves take the item's blocks
 // round-robin, then finish_item.
-template <typename Tag, int D, bool kInt8>
+template <typename Tag, int D, bool kInt8, int W>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int4 it, int gh, float* comb) {
-  constexpr int W = kItemWaves;
   const int s = it.x, p = it.y, len = it.z, part = it.w;
   const int g = gh / a.head_blocks, h0 = (gh % a.head_blocks) * 16;
   const int nh = min(16, a.group - h0);
@@ -354,26 +356,26 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int4 it, int gh
 // exit at once.  (A persistent form -- a resident-size grid taking items from
 // a ticket counter -- measured slower on the mixed batch: the ticket's
 // atomic sits between items, and the loop kept ~20 more registers live.)
-template <typename Tag, int D>
-__global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_kernel(
+template <typename Tag, int D, int W>
+__global__ __launch_bounds__(item_threads(W), 4) void decode_items_kernel(
     DecodeArgs a, const int4* __restrict__ items) {
   extern __shared__ float comb[];
   const int heads = a.hkv * a.head_blocks;
   const int4 it = items[blockIdx.x / heads];
   if (it.x < 0) return;
-  decode_item<Tag, D, false>(a, it, blockIdx.x % heads, comb);
+  decode_item<Tag, D, false, W>(a, it, blockIdx.x % heads, comb);
 }
 
 // decode_items_kernel over an INT8 cache (same items, partitions and
 // partials); the V scale multiplies each merged result before it is stored.
-template <typename Tag, int D>
-__global__ __launch_bounds__(kItemThreads, 16 / kItemWaves) void decode_items_i8_kernel(
+template <typename Tag, int D, int W>
+__global__ __launch_bounds__(item_threads(W), 4) void decode_items_i8_kernel(
     DecodeArgs a, const int4* __restrict__ items) {
   extern __shared__ float comb[];
   const int heads = a.hkv * a.head_blocks;
   const int4 it = items[blockIdx.x / heads];
   if (it.x < 0) return;
-  decode_item<Tag, D, true>(a, it, blockIdx.x % heads, comb);
+  decode_item<Tag, D, true, W>(a, it, blockIdx.x % heads, comb);
 }
 
 // ---- generic VALU path ----
@@ -674,17 +676,33 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
       a.k_scale = k_scale;
       a.v_scale = v_scale;
       a.arrivals = arrivals;
-      const size_t lds = comb_floats(kItemWaves, a.nh_max, head_dim) * sizeof(float);
-      const dim3 g3(static_cast<uint32_t>(grid)), b3(kItemThreads);
+      // 8 waves per item for the partitions chosen for long contexts (>= 2048
+      // positions, INT8 >= 4096): each wave then still streams many blocks, and
+      // the 32K context decodes ~4 % faster; 4 otherwise (mixed batches of
+      // short items lose 8 % at 8 waves on the INT8 cache)
+      const int waves = sp.part >= (k_scale ? 4096 : 2048) ? 8 : 4;
+      const size_t lds = comb_floats(waves, a.nh_max, head_dim) * sizeof(float);
+      const dim3 g3(static_cast<uint32_t>(grid)), b3(item_threads(waves));
       if (k_scale) {  // INT8 cache
-        if (head_dim == 128)
-          decode_items_i8_kernel<Tag, 128><<<g3, b3, lds, st>>>(a, items);
-        else
-          decode_items_i8_kernel<Tag, 64><<<g3, b3, lds, st>>>(a, items);
+        if (head_dim == 128) {
+          if (waves == 8)
+            decode_items_i8_kernel<Tag, 128, 8><<<g3, b3, lds, st>>>(a, items);
+          else
+            decode_items_i8_kernel<Tag, 128, 4><<<g3, b3, lds, st>>>(a, items);
+        } else if (waves == 8) {
+          decode_items_i8_kernel<Tag, 64, 8><<<g3, b3, lds, st>>>(a, items);
+        } else {
+          decode_items_i8_kernel<Tag, 64, 4><<<g3, b3, lds, st>>>(a, items);
+        }
       } else if (head_dim == 128) {
-        decode_items_kernel<Tag, 128><<<g3, b3, lds, st>>>(a, items);
+        if (waves == 8)
+          decode_items_kernel<Tag, 128, 8><<<g3, b3, lds, st>>>(a, items);
+        else
+          decode_items_kernel<Tag, 128, 4><<<g3, b3, lds, st>>>(a, items);
+      } else if (waves == 8) {
+        decode_items_kernel<Tag, 64, 8><<<g3, b3, lds, st>>>(a, items);
       } else {
-        decode_items_kernel<Tag, 64><<<g3, b3, lds, st>>>(a, items);
+        decode_items_kernel<Tag, 64, 4><<<g3, b3, lds, st>>>(a, items);
       }
       status = launch_status();
     }

@@ -61,6 +61,17 @@ def test_small_cases_against_oracle(lens, hq, hkv, d, dtype, partition_size):
     assert_close(db.out_bits(), ref, dtype, f"{lens} {hq}/{hkv} d={d} {dtype}")
 
 
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f16")])
+@pytest.mark.parametrize("partition_size", [2048, 4096])
+def test_eight_wave_items_against_oracle(d, dtype, partition_size):
+    # partitions of >= 2048 positions run the items kernel with 8 waves per work-group
+    print(f"[gpu] 8-wave items d={d} {dtype} P={partition_size}", flush=True)
+    lens = [17, 100, 2100, 4500, 9000]
+    w = workloads.make_custom(lens, hq=16, hkv=2, d=d, dtype=dtype, seed=partition_size + d)
+    db, ref = _run_small(w, partition_size)
+    assert_close(db.out_bits(), ref, dtype, f"8 waves {d} {dtype} P={partition_size}")
+
+
 @pytest.mark.parametrize("mode", [pa.PARTITION_BALANCED])
 @pytest.mark.parametrize("groups", [1, 2, 3, 7, 64, 0])
 @pytest.mark.parametrize("hq,hkv,d,dtype", [(16, 2, 128, "bf16"), (8, 8, 64, "f16"),

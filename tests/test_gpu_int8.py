@@ -89,6 +89,19 @@ def test_small_cases_against_oracle(lens, hq, hkv, d, dtype, partition_size):
     assert_close(db.out_bits(), ref, dtype, f"int8 {lens} P={partition_size}")
 
 
+@pytest.mark.parametrize("partition_size", [4096, 8192])
+def test_eight_wave_items_against_oracle(partition_size):
+    # INT8 partitions of >= 4096 positions run with 8 waves per work-group
+    print(f"[gpu] int8 8-wave items P={partition_size}", flush=True)
+    lens = [17, 100, 4200, 9000]
+    w = workloads.make_custom(lens, hq=16, hkv=2, d=128, dtype="bf16", seed=partition_size)
+    _, _, _, ref = step.run_int8(w)
+    db = runner.DeviceBatch(w, int8=True)
+    db.prefill()
+    db.step(partition_size=partition_size)
+    assert_close(db.out_bits(), ref, "bf16", f"int8 8 waves P={partition_size}")
+
+
 def test_shared_prefix_and_zero_length_rows():
     import torch
     print("[gpu] int8 shared prefix, zero-length rows", flush=True)
