@@ -59,18 +59,25 @@ namespace {
 
 // ---- fixed partitions: work items from a plan ----
 
-// Size class of a last partition: 0 (the largest) .. kClasses - 1 (an empty
-// sequence).  Classes 0..5 are sixths of a partition, largest first; class 6
-// holds slivers below 1/64 of a partition.
-constexpr int kClasses = 8;
+// Size class of a last partition of `tokens` positions: 0 (the longest) ..
+// kClasses - 1 (an empty sequence).  An item's duration is set by its rounds,
+// the blocks each wave of its work-group streams (ceil(blocks / waves)), so
+// the classes follow rounds: with at most 16 rounds per partition each round
+// count has its own class, with more (long partitions on few waves) two or
+// more adjacent round counts share one.  Ordering by rounds keeps every item
+// that streams more behind none that streams less, which is what keeps the
+// end of the list short.
+constexpr int kRoundClasses = 16;
+constexpr int kClasses = kRoundClasses + 1;
 #ifndef PA_FUSED_MERGE
 #define PA_FUSED_MERGE 1
 #endif
 constexpr bool kFusedMerge = PA_FUSED_MERGE != 0;
-__device__ __forceinline__ int size_class(int tokens, int part_size) {
+__device__ __forceinline__ int size_class(int tokens, int part_size, int waves) {
   if (tokens <= 0) return kClasses - 1;
-  if (tokens * 64 < part_size) return kClasses - 2;
-  return 6 - (tokens * 6 + part_size - 1) / part_size;
+  const int max_rounds = ((part_size + kBlock - 1) / kBlock + waves - 1) / waves;
+  const int rounds = ((tokens + kBlock - 1) / kBlock + waves - 1) / waves;
+  return (max_rounds - min(rounds, max_rounds)) * kRoundClasses / max_rounds;
 }
 
 // Entries of the item list: every (sequence, partition), rounded up to a
@@ -90,6 +97,7 @@ struct PlanArgs {
   int* arrivals;     // per (sequence, head group): partials stored so far (zeroed here)
   int num_arrivals;
   int max_items;     // items the decode grid serves (see plan_partition)
+  int waves;         // waves per decode work-group (size classes count rounds of these)
 };
 
 __device__ __forceinline__ int plan_len(const PlanArgs& a, int i) {
@@ -151,7 +159,7 @@ __device__ __forceinline__ void plan_count(const PlanArgs& a, int part, int i0, 
   for (int i = i0; i < i1; ++i) {
     const int len = plan_len(a, i);
     const int np = plan_parts(a, len, part);
-    const int cls = size_class(np > 0 ? len - (np - 1) * part : 0, part);
+    const int cls = size_class(np > 0 ? len - (np - 1) * part : 0, part, a.waves);
 #pragma unroll
     for (int c = 0; c < kClasses; ++c) cnt[c] += cls == c;
     cnt[kClasses] += max(np - 1, 0);
@@ -190,7 +198,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
     const int len = plan_len(a, i);
     const int np = plan_parts(a, len, part);
     for (int p = 0; p + 1 < np; ++p) a.items[full_pos++] = make_int4(i, p, len, part);
-    const int cls = size_class(np > 0 ? len - (np - 1) * part : 0, part);
+    const int cls = size_class(np > 0 ? len - (np - 1) * part : 0, part, a.waves);
     int at = 0;
 #pragma unroll
     for (int c = 0; c < kClasses; ++c)
@@ -571,11 +579,13 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(
 // and every item count halves (measured on MI355X: the mixed 70B-layer batch
 // decodes in 62.7 us at 2048 against 63.6 us at 1024, the 32K batch in 99 us
 // at 4096 against 103 us at 2048).
+constexpr int kLongContext = 16384;
+
 int auto_partition(int num_seqs, int hkv, int max_len, int kv_bytes = 2) {
   const int k = kv_bytes == 1 ? 2 : 1;
   if (max_len <= 1024 * k) return PA_PARTITION_NONE;
   const int long_part = 2048 * k;
-  if (max_len >= 16384 &&
+  if (max_len >= kLongContext &&
       static_cast<int64_t>(num_seqs) * ((max_len + long_part - 1) / long_part) * hkv >= 1024 / k)
     return long_part;
   int ps = 1024 * k;
@@ -593,7 +603,20 @@ bool resolve_split(int partition_size, int num_seqs, int hkv, int max_len, Split
   if (ps == PA_PARTITION_NONE) ps = max(kBlock, (max_len + kBlock - 1) / kBlock * kBlock);
   out->part = ps;
   out->np = max(1, (max_len + ps - 1) / ps);
+  out->long_context = max_len >= kLongContext;
   return true;
+}
+
+// Waves per work-group of the items kernels: 8 for the long partitions of a
+// long-context batch (>= 16K positions; partitions >= 2048 positions, INT8 >=
+// 4096), where each wave still streams many blocks and the 32K context
+// decodes ~4 % faster; 4 otherwise (mixed batches of short items lose up to
+// 8 % at 8 waves), and 4 whenever 8 waves' partials would not fit the 64 KiB
+// of LDS a work-group gets by default (query-head groups of 16 at D = 128).
+int item_waves(const Split& sp, bool int8, int group, int head_dim) {
+  const bool long_part = sp.part >= (int8 ? 4096 : 2048);
+  const size_t lds = comb_floats(8, std::min(16, group), head_dim) * sizeof(float);
+  return sp.long_context && long_part && lds <= 65536 ? 8 : kItemWaves;
 }
 
 // Workspace of the fixed-partition path: [plan: meta (256 B), items, split
@@ -648,10 +671,11 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   float* ws_acc = reinterpret_cast<float*>(ws + lay.acc);
   // the matrix-core kernels merge split sequences themselves (merge_if_last)
   int* arrivals = fused_merge ? reinterpret_cast<int*>(ws + lay.arrivals) : nullptr;
+  const int waves = use_mfma ? item_waves(sp, k_scale != nullptr, group, head_dim) : kWaves;
   if (use_mfma || sp.np > 1) {
     PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np, arrivals,
                 fused_merge ? num_seqs * hkv * head_blocks : 0,  // one per (sequence, head group)
-                item_grid};
+                item_grid, waves};
     if (write) {  // the step's cache writes ride along with the plan
       const int64_t wgs = 1 + (write->threads() + kThreads - 1) / kThreads;
       const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);
@@ -676,11 +700,6 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
       a.k_scale = k_scale;
       a.v_scale = v_scale;
       a.arrivals = arrivals;
-      // 8 waves per item for the partitions chosen for long contexts (>= 2048
-      // positions, INT8 >= 4096): each wave then still streams many blocks, and
-      // the 32K context decodes ~4 % faster; 4 otherwise (mixed batches of
-      // short items lose 8 % at 8 waves on the INT8 cache)
-      const int waves = sp.part >= (k_scale ? 4096 : 2048) ? 8 : 4;
       const size_t lds = comb_floats(waves, a.nh_max, head_dim) * sizeof(float);
       const dim3 g3(static_cast<uint32_t>(grid)), b3(item_threads(waves));
       if (k_scale) {  // INT8 cache

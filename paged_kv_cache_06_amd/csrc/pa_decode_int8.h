@@ -57,9 +57,9 @@ __device__ __forceinline__ void load_block_i8(const DecodeArgs& a, int g, int ph
   const auto rk = buffer_of(reinterpret_cast<const char*>(a.k_cache) + off, range);
   const auto rv = buffer_of(reinterpret_cast<const char*>(a.v_cache) + off, range);
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) r.k[i] = buffer_load16(rk, lane * 16 + i * 1024);
+  for (int i = 0; i < D / 64; ++i) r.k[i] = stream_load16(rk, lane * 16 + i * 1024);
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) r.v[i] = buffer_load16(rv, lane * 16 + i * 1024);
+  for (int i = 0; i < D / 64; ++i) r.v[i] = stream_load16(rv, lane * 16 + i * 1024);
 }
 
 // Matrix-core operands of the block: kf[m] is the A operand of QK step m
