@@ -30,10 +30,9 @@ METRIC = "paged-attn decode achieved HBM GB/s (% of peak); attended KV tokens/s"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 CSRC = os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc")
-# main-pass kernels of a decode call (balanced split, fixed partitions, VALU
-# path) and the sources each is built from
+# main-pass kernels of a decode call (matrix-core items kernels, VALU path) and
+# the sources each is built from
 DECODE_KERNELS = {
-    "decode_stream_kernel": ("pa_decode_balanced.hip", "pa_decode_common.h"),
     "decode_items_kernel": ("pa_decode.hip", "pa_decode_common.h"),
     "decode_generic_kernel": ("pa_decode.hip", "pa_decode_common.h"),
     "decode_items_i8_kernel": ("pa_decode.hip", "pa_decode_int8.h", "pa_decode_common.h"),
@@ -413,7 +412,7 @@ def main():
     ap.add_argument("--config", default="3", help="workload 1..5 or 4b (default 3)")
     ap.add_argument("--copies", type=int, default=0,
                     help="KV pool copies used round-robin (default: enough for >= 1.5 GB)")
-    ap.add_argument("--partition", type=int, default=-1, help="-1 auto, -2 balanced split, 0 none, else tokens")
+    ap.add_argument("--partition", type=int, default=-1, help="-1 auto, 0 none, else tokens")
     ap.add_argument("--kv", choices=("native", "int8"), default="native",
                     help="KV cache storage: the workload's dtype, or INT8 codes with "
                          "per-channel scales")
@@ -520,8 +519,6 @@ def main():
         3 if int8 else {"f32": 0, "f16": 1, "bf16": 2}[w.dtype])
     if int8:
         main_kernel = "decode_items_i8_kernel"
-    elif ps == pa.PARTITION_BALANCED:
-        main_kernel = "decode_stream_kernel"
     elif w.dtype != "f32" and w.head_dim in (64, 128):
         main_kernel = "decode_items_kernel"
     else:

@@ -75,7 +75,6 @@ typedef int32_t pa_dtype;
  * multiple of 16 */
 #define PA_PARTITION_NONE 0    /* one pass over each whole sequence, no partials */
 #define PA_PARTITION_AUTO (-1) /* the library picks */
-#define PA_PARTITION_BALANCED (-2) /* equal K/V work per wave (matrix-core path) */
 
 /* Short English text of a status code (static storage). */
 const char* pa_status_string(pa_status status);
@@ -254,12 +253,7 @@ pa_status pa_transfer_blocks(const void* src_k, const void* src_v, int32_t src_n
  * sequence) plus, when some sequence is split, the partial results
  * (4 * (2 + head_dim) bytes per sequence, query head and partition) and
  * 4 bytes per sequence and query head (arrival counts of the in-kernel merge).
- * PA_PARTITION_BALANCED: 16 bytes per range start (one more than ranges) and
- * two partial slots per range of min(16, num_q_heads) rows, rounded up to a
- * power of two, of 4 * (2 + head_dim) bytes each; ranges = 2048, or
- * ceil(num_seqs * num_q_heads * (2 + ceil(max_context_len / 16)) / 512) when
- * that is larger.  PA_PARTITION_AUTO: as for the partition size it resolves
- * to.  Each area is 256-byte aligned after a 256-byte header.  0 on invalid
+ * PA_PARTITION_AUTO: as for the partition size it resolves to.  Each area is 256-byte aligned after a 256-byte header.  0 on invalid
  * sizes. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size);
@@ -269,13 +263,6 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * choice of pa_paged_attention_decode_int8. */
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
-
-/* Caps the work-groups of the balanced split at max_groups, four waves (four
- * ranges) each (0: no cap; the default is the number the device holds
- * resident at once).  For sharing the GPU with concurrent work, and for
- * tests.  Library-wide, not thread-safe against concurrent decode calls.
- * PA_ERR_INVALID_ARG if negative. */
-pa_status pa_decode_set_max_groups(int32_t max_groups);
 
 /* Decode attention over the paged cache:
  *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_s[t]) V_s[t],
@@ -292,14 +279,10 @@ pa_status pa_decode_set_max_groups(int32_t max_groups);
  *                 (its K/V must already be in the cache); 0 gives out = 0;
  *                 each must be <= max_context_len and <= 16 * max_blocks_per_seq
  *   partition_size  how the work is split:
- *                 PA_PARTITION_BALANCED (matrix-core path only): the blocks
- *                 of all (sequence, KV head) pairs are cut into ranges of
- *                 equal cost, one per resident wave (at most 512 blocks
- *                 each); a pair cut by range boundaries is merged by a
- *                 second pass (running max / log-sum-exp rule);
  *                 a positive multiple of 16: sequences longer than it are
- *                 split into partitions of that many positions, merged the
- *                 same way (on the matrix-core path, when that would make
+ *                 split into partitions of that many positions whose partial
+ *                 results are merged by the running-max (log-sum-exp) rule
+ *                 (on the matrix-core path, when that would make
  *                 more than max(2 * num_seqs, ceil(2048 / (num_kv_heads *
  *                 ceil(group / 16)))) partitions in all, the size is doubled
  *                 until it does not, at most 6 times, else one partition per
@@ -370,8 +353,7 @@ pa_status pa_reshape_and_cache_int8(const void* key, const void* value, void* k_
 /* pa_paged_attention_decode over an INT8 cache: out[s, h] = attention of
  * q[s, h] over the values code_K * k_scale, code_V * v_scale of the
  * sequence's positions.  q and out have dtype F16 or BF16; head_dim 64 or
- * 128; partition_size NONE, AUTO or a positive multiple of 16 (the balanced
- * split serves 16-bit caches only); the workspace is sized by
+ * 128; partition_size NONE, AUTO or a positive multiple of 16; the workspace is sized by
  * pa_decode_workspace_bytes as for a 16-bit cache.  Other arguments and
  * errors as pa_paged_attention_decode. */
 pa_status pa_paged_attention_decode_int8(const void* q, const void* k_cache, const void* v_cache,
@@ -418,10 +400,11 @@ pa_status pa_decode_step_int8(const void* key, const void* value, const int64_t*
 
 /* ---------------------------------------------------------------------------
  * Kernel timing.  Between pa_timing_begin and pa_timing_end every kernel the
- * library launches is bracketed by HIP events on its own stream.
- * pa_timing_end waits for those events and returns, per kernel kind, the
- * summed milliseconds and the launch count.  At most `capacity` launches are
- * recorded; later ones run untimed.
+ * library launches carries two HIP events attached to its dispatch on its own
+ * stream, which record the start and the end of the kernel's execution (the
+ * interval a kernel-trace profiler reports).  pa_timing_end waits for those
+ * events and returns, per kernel kind, the summed milliseconds and the launch
+ * count.  At most `capacity` launches are recorded; later ones run untimed.
  * ------------------------------------------------------------------------- */
 #define PA_KERNEL_DECODE 0          /* main pass of pa_paged_attention_decode */
 #define PA_KERNEL_DECODE_REDUCE 1   /* merge pass of split sequences */

@@ -22,10 +22,10 @@ import os
 import numpy as np
 
 __all__ = [
-    "BLOCK_SIZE", "PARTITION_NONE", "PARTITION_AUTO", "PARTITION_BALANCED", "PAError", "load", "lib_path",
+    "BLOCK_SIZE", "PARTITION_NONE", "PARTITION_AUTO", "PAError", "load", "lib_path",
     "Pool", "BlockManager", "blocks_for_bytes", "reshape_and_cache", "copy_blocks",
     "paged_attention_decode", "decode_workspace_bytes", "decode_auto_partition",
-    "decode_set_max_groups", "reshape_and_cache_int8", "paged_attention_decode_int8",
+    "reshape_and_cache_int8", "paged_attention_decode_int8",
     "swap_blocks", "transfer_blocks", "new_host_kv_cache", "paged_attention_prefill",
     "decode_step", "decode_step_int8",
     "new_kv_cache", "new_kv_cache_int8", "logical_view", "timing_begin", "timing_end", "timing_launches", "status_string",
@@ -34,7 +34,6 @@ __all__ = [
 BLOCK_SIZE = 16
 PARTITION_NONE = 0
 PARTITION_AUTO = -1
-PARTITION_BALANCED = -2
 KERNEL_KINDS = ("decode", "decode_reduce", "reshape_and_cache", "copy_blocks", "decode_plan",
                 "transfer_blocks", "prefill")
 
@@ -79,7 +78,6 @@ _SIGNATURES = {
     "pa_copy_blocks": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "pa_decode_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode_auto_partition": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
-    "pa_decode_set_max_groups": (_c_i32, [_c_i32]),
     "pa_paged_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_p, _c_i32,
                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                            _c_p, _c_sz, _c_i32, _c_p]),
@@ -531,11 +529,6 @@ def decode_auto_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, max_con
     return int(load().pa_decode_auto_partition(int(num_seqs), int(num_q_heads),
                                                int(num_kv_heads), int(head_dim),
                                                int(max_context_len), int(dtype_code)))
-
-
-def decode_set_max_groups(max_groups: int) -> None:
-    """Cap the work-groups of the balanced split (0: the device's resident count)."""
-    _check(load().pa_decode_set_max_groups(int(max_groups)), "pa_decode_set_max_groups")
 
 
 _workspaces = {}

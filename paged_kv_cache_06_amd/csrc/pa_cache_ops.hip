@@ -132,14 +132,12 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
                                               num_tokens, num_slots, num_kv_heads, head_dim);
   const int64_t grid = ((dtype == PA_F32 ? w32.threads() : w16.threads()) + 255) / 256;
   if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
-  const int slot = timing_start(PA_KERNEL_RESHAPE_AND_CACHE, st);
+  const dim3 g(static_cast<uint32_t>(grid)), b(256);
   if (dtype == PA_F32)
-    reshape_and_cache_kernel<float><<<dim3(grid), dim3(256), 0, st>>>(w32);
-  else
-    reshape_and_cache_kernel<uint16_t><<<dim3(grid), dim3(256), 0, st>>>(w16);
-  const pa_status s = launch_status();
-  timing_stop(slot, st);
-  return s;
+    return launch_kernel(PA_KERNEL_RESHAPE_AND_CACHE, reshape_and_cache_kernel<float>, g, b, 0,
+                         st, w32);
+  return launch_kernel(PA_KERNEL_RESHAPE_AND_CACHE, reshape_and_cache_kernel<uint16_t>, g, b, 0,
+                       st, w16);
 }
 
 pa_status pa_reshape_and_cache_int8(const void* key, const void* value, void* k_cache,
@@ -166,23 +164,25 @@ pa_status pa_reshape_and_cache_int8(const void* key, const void* value, void* k_
   if (grid > 0x7fffffff) return PA_ERR_INVALID_ARG;
   int8_t* kc = static_cast<int8_t*>(k_cache);
   int8_t* vc = static_cast<int8_t*>(v_cache);
-  const int slot = timing_start(PA_KERNEL_RESHAPE_AND_CACHE, st);
   const dim3 g(static_cast<uint32_t>(grid)), b(256);
+  constexpr int kKind = PA_KERNEL_RESHAPE_AND_CACHE;
   if (dtype == PA_F32)
-    reshape_and_cache_i8_kernel<F32T><<<g, b, 0, st>>>(CacheWriteI8Args<F32T>{
-        static_cast<const float*>(key), static_cast<const float*>(value), kc, vc, slot_mapping,
-        k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim});
-  else if (dtype == PA_BF16)
-    reshape_and_cache_i8_kernel<BF16T><<<g, b, 0, st>>>(CacheWriteI8Args<BF16T>{
-        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), kc, vc,
-        slot_mapping, k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim});
-  else
-    reshape_and_cache_i8_kernel<F16T><<<g, b, 0, st>>>(CacheWriteI8Args<F16T>{
-        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), kc, vc,
-        slot_mapping, k_scale, v_scale, num_tokens, num_slots, num_kv_heads, head_dim});
-  const pa_status s = launch_status();
-  timing_stop(slot, st);
-  return s;
+    return launch_kernel(kKind, reshape_and_cache_i8_kernel<F32T>, g, b, 0, st,
+                         CacheWriteI8Args<F32T>{static_cast<const float*>(key),
+                                                static_cast<const float*>(value), kc, vc,
+                                                slot_mapping, k_scale, v_scale, num_tokens,
+                                                num_slots, num_kv_heads, head_dim});
+  if (dtype == PA_BF16)
+    return launch_kernel(kKind, reshape_and_cache_i8_kernel<BF16T>, g, b, 0, st,
+                         CacheWriteI8Args<BF16T>{static_cast<const uint16_t*>(key),
+                                                 static_cast<const uint16_t*>(value), kc, vc,
+                                                 slot_mapping, k_scale, v_scale, num_tokens,
+                                                 num_slots, num_kv_heads, head_dim});
+  return launch_kernel(kKind, reshape_and_cache_i8_kernel<F16T>, g, b, 0, st,
+                       CacheWriteI8Args<F16T>{static_cast<const uint16_t*>(key),
+                                              static_cast<const uint16_t*>(value), kc, vc,
+                                              slot_mapping, k_scale, v_scale, num_tokens,
+                                              num_slots, num_kv_heads, head_dim});
 }
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
@@ -198,12 +198,10 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
   const int64_t bytes = static_cast<int64_t>(num_kv_heads) * kBlock * head_dim * elem_bytes(dtype);
   const int64_t vec = bytes / 16;
   const int64_t gy = (vec + 1023) / 1024;
-  const int slot = timing_start(PA_KERNEL_COPY_BLOCKS, st);
-  copy_blocks_kernel<<<dim3(2 * num_pairs, static_cast<uint32_t>(gy)), dim3(256), 0, st>>>(
-      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), block_pairs, num_blocks, vec);
-  const pa_status s = launch_status();
-  timing_stop(slot, st);
-  return s;
+  return launch_kernel(PA_KERNEL_COPY_BLOCKS, copy_blocks_kernel,
+                       dim3(2 * num_pairs, static_cast<uint32_t>(gy)), dim3(256), 0, st,
+                       static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), block_pairs,
+                       num_blocks, vec);
 }
 
 pa_status pa_transfer_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks,
@@ -226,14 +224,11 @@ pa_status pa_transfer_blocks(const void* src_k, const void* src_v, int32_t src_n
   const int64_t bytes = static_cast<int64_t>(num_kv_heads) * kBlock * head_dim * elem_bytes(dtype);
   const int64_t vec = bytes / 16;
   const int64_t gy = (vec + 1023) / 1024;
-  const int slot = timing_start(PA_KERNEL_TRANSFER_BLOCKS, st);
-  transfer_blocks_kernel<<<dim3(2 * num_pairs, static_cast<uint32_t>(gy)), dim3(256), 0, st>>>(
-      static_cast<const uint4*>(sk), static_cast<const uint4*>(sv), static_cast<uint4*>(dk),
-      static_cast<uint4*>(dv), static_cast<const int64_t*>(pr), src_num_blocks, dst_num_blocks,
-      vec);
-  const pa_status s = launch_status();
-  timing_stop(slot, st);
-  return s;
+  return launch_kernel(PA_KERNEL_TRANSFER_BLOCKS, transfer_blocks_kernel,
+                       dim3(2 * num_pairs, static_cast<uint32_t>(gy)), dim3(256), 0, st,
+                       static_cast<const uint4*>(sk), static_cast<const uint4*>(sv),
+                       static_cast<uint4*>(dk), static_cast<uint4*>(dv),
+                       static_cast<const int64_t*>(pr), src_num_blocks, dst_num_blocks, vec);
 }
 
 }  // extern "C"

@@ -1,10 +1,12 @@
 // Shared helpers of the HIP kernels and their launchers (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
+#include <utility>
 
 #include "pa.h"
 
@@ -52,13 +54,30 @@ struct F16T {
 };
 
 // ---- kernel timing hooks (pa_timing.hip) ----
-// Returns a slot index when timing is on and capacity remains, else -1.
-int timing_start(int kind, hipStream_t stream);
-void timing_stop(int slot, hipStream_t stream);
+// The events of the next launch of kernel kind `kind` while timing is on and
+// capacity remains, else two null events (an untimed launch).
+struct TimedLaunch {
+  hipEvent_t start, stop;
+};
+TimedLaunch timing_events(int kind);
 
 // Launch check: converts the last launch error to a status.
 inline pa_status launch_status() {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_DEVICE;
+}
+
+// Launches kernel<<<grid, block, lds, stream>>>(args...).  While timing is on
+// the launch carries two HIP events attached to its dispatch, which record
+// the start and the end of the kernel's own execution on its stream (no
+// separate marker packets around it).
+template <typename... Params, typename... Args>
+pa_status launch_kernel(int kind, void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds,
+                        hipStream_t stream, Args&&... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  const TimedLaunch t = timing_events(kind);
+  hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), stream, t.start, t.stop,
+                        0, static_cast<Params>(std::forward<Args>(args))...);
+  return launch_status();
 }
 
 }  // namespace pa

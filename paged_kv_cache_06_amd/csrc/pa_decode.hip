@@ -50,7 +50,6 @@
 // Generic path (any supported dtype/head_dim, fp32 in particular): one
 // work-group per query head, VALU dot products, 256-position chunks with the
 // same online softmax and the same partial-result format.
-#include "pa_decode_balanced.h"
 #include "pa_decode_int8.h"
 #include "pa_cache_write.h"
 #include "pa_decode_common.h"
@@ -676,22 +675,15 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
     PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np, arrivals,
                 fused_merge ? num_seqs * hkv * head_blocks : 0,  // one per (sequence, head group)
                 item_grid, waves};
-    if (write) {  // the step's cache writes ride along with the plan
-      const int64_t wgs = 1 + (write->threads() + kThreads - 1) / kThreads;
-      const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);
-      decode_prep_kernel<W><<<dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), 0, st>>>(pa, *write);
-      const pa_status ps = launch_status();
-      timing_stop(pslot, st);
-      if (ps != PA_OK) return ps;
-    } else {
-      const int pslot = timing_start(PA_KERNEL_DECODE_PLAN, st);
-      decode_plan_kernel<<<dim3(1), dim3(kThreads), 0, st>>>(pa);
-      const pa_status ps = launch_status();
-      timing_stop(pslot, st);
-      if (ps != PA_OK) return ps;
-    }
+    const pa_status ps =
+        write ?  // the step's cache writes ride along with the plan
+            launch_kernel(PA_KERNEL_DECODE_PLAN, decode_prep_kernel<W>,
+                          dim3(static_cast<uint32_t>(1 + (write->threads() + kThreads - 1) / kThreads)),
+                          dim3(kThreads), 0, st, pa, *write)
+              : launch_kernel(PA_KERNEL_DECODE_PLAN, decode_plan_kernel, dim3(1), dim3(kThreads),
+                              0, st, pa);
+    if (ps != PA_OK) return ps;
   }
-  int slot = timing_start(PA_KERNEL_DECODE, st);
   pa_status status = PA_OK;
   if (use_mfma) {
     if constexpr (sizeof(E) == 2) {
@@ -702,46 +694,35 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
       a.arrivals = arrivals;
       const size_t lds = comb_floats(waves, a.nh_max, head_dim) * sizeof(float);
       const dim3 g3(static_cast<uint32_t>(grid)), b3(item_threads(waves));
+      const int4* it = items;
+      constexpr int kK = PA_KERNEL_DECODE;
       if (k_scale) {  // INT8 cache
-        if (head_dim == 128) {
-          if (waves == 8)
-            decode_items_i8_kernel<Tag, 128, 8><<<g3, b3, lds, st>>>(a, items);
-          else
-            decode_items_i8_kernel<Tag, 128, 4><<<g3, b3, lds, st>>>(a, items);
-        } else if (waves == 8) {
-          decode_items_i8_kernel<Tag, 64, 8><<<g3, b3, lds, st>>>(a, items);
-        } else {
-          decode_items_i8_kernel<Tag, 64, 4><<<g3, b3, lds, st>>>(a, items);
-        }
-      } else if (head_dim == 128) {
-        if (waves == 8)
-          decode_items_kernel<Tag, 128, 8><<<g3, b3, lds, st>>>(a, items);
+        if (head_dim == 128)
+          status = waves == 8 ? launch_kernel(kK, decode_items_i8_kernel<Tag, 128, 8>, g3, b3, lds, st, a, it)
+                              : launch_kernel(kK, decode_items_i8_kernel<Tag, 128, 4>, g3, b3, lds, st, a, it);
         else
-          decode_items_kernel<Tag, 128, 4><<<g3, b3, lds, st>>>(a, items);
-      } else if (waves == 8) {
-        decode_items_kernel<Tag, 64, 8><<<g3, b3, lds, st>>>(a, items);
+          status = waves == 8 ? launch_kernel(kK, decode_items_i8_kernel<Tag, 64, 8>, g3, b3, lds, st, a, it)
+                              : launch_kernel(kK, decode_items_i8_kernel<Tag, 64, 4>, g3, b3, lds, st, a, it);
+      } else if (head_dim == 128) {
+        status = waves == 8 ? launch_kernel(kK, decode_items_kernel<Tag, 128, 8>, g3, b3, lds, st, a, it)
+                            : launch_kernel(kK, decode_items_kernel<Tag, 128, 4>, g3, b3, lds, st, a, it);
       } else {
-        decode_items_kernel<Tag, 64, 4><<<g3, b3, lds, st>>>(a, items);
+        status = waves == 8 ? launch_kernel(kK, decode_items_kernel<Tag, 64, 8>, g3, b3, lds, st, a, it)
+                            : launch_kernel(kK, decode_items_kernel<Tag, 64, 4>, g3, b3, lds, st, a, it);
       }
-      status = launch_status();
     }
   } else {
-    decode_generic_kernel<Tag><<<dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, st>>>(
-        static_cast<const E*>(q), static_cast<const E*>(k_cache), static_cast<const E*>(v_cache),
-        tables, lens, scale_log2, static_cast<E*>(out), ws_ml, ws_acc, num_seqs, hq, hkv, group,
-        head_dim, max_blocks, sp.part, sp.np);
-    status = launch_status();
+    status = launch_kernel(
+        PA_KERNEL_DECODE, decode_generic_kernel<Tag>, dim3(static_cast<uint32_t>(grid)),
+        dim3(kThreads), 0, st, static_cast<const E*>(q), static_cast<const E*>(k_cache),
+        static_cast<const E*>(v_cache), tables, lens, scale_log2, static_cast<E*>(out), ws_ml,
+        ws_acc, num_seqs, hq, hkv, group, head_dim, max_blocks, sp.part, sp.np);
   }
-  timing_stop(slot, st);
   if (status != PA_OK || sp.np <= 1 || fused_merge) return status;
-  slot = timing_start(PA_KERNEL_DECODE_REDUCE, st);
   const int rows = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(num_seqs) * hq, 2048));
-  decode_reduce_kernel<Tag><<<dim3(rows), dim3(kThreads), 0, st>>>(
-      ws_ml, ws_acc, split, meta, lens, static_cast<E*>(out), hq, head_dim, max_blocks, sp.part,
-      sp.np);
-  status = launch_status();
-  timing_stop(slot, st);
-  return status;
+  return launch_kernel(PA_KERNEL_DECODE_REDUCE, decode_reduce_kernel<Tag>, dim3(rows),
+                       dim3(kThreads), 0, st, ws_ml, ws_acc, split, meta, lens,
+                       static_cast<E*>(out), hq, head_dim, max_blocks, sp.part, sp.np);
 }
 }  // namespace
 }  // namespace pa
@@ -760,9 +741,6 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t max_context_len, int32_t partition_size) {
   pa::Split sp;
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-  if (partition_size == PA_PARTITION_BALANCED)
-    return pa::balanced_split_workspace_bytes(
-        num_q_heads, head_dim, pa::balanced_split_ranges(num_seqs, num_q_heads, max_context_len));
   // the automatic choice shrinks partitions for fewer KV heads, so sizing with
   // one KV head covers every head count
   if (!pa::resolve_split(partition_size, num_seqs, 1, max_context_len, &sp)) return 0;
@@ -807,32 +785,19 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   const bool use_mfma = mfma_path(dtype, head_dim);
-  if (partition_size == PA_PARTITION_BALANCED && !use_mfma) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return PA_ERR_INVALID_ARG;
-  const bool balanced = use_mfma && partition_size == PA_PARTITION_BALANCED;
   Split sp{kBlock, 1};
-  size_t need;
-  int64_t ranges = 0;
-  if (balanced) {
-    // block indices of the balanced split stay below 2^30
-    const int64_t units = static_cast<int64_t>(num_kv_heads) * ((num_q_heads / num_kv_heads + 15) / 16);
-    if (static_cast<int64_t>(num_seqs) * units * max_blocks_per_seq >= (int64_t{1} << 30))
-      return PA_ERR_INVALID_ARG;
-    ranges = balanced_split_ranges(num_seqs, num_q_heads, max_context_len);
-    need = balanced_split_workspace_bytes(num_q_heads, head_dim, ranges);
-  } else {
-    if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp))
-      return PA_ERR_INVALID_ARG;
-    need = workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
-  }
+  if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp))
+    return PA_ERR_INVALID_ARG;
+  const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
     return PA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   const float scale_log2 = scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool fused = wr.key != nullptr && wr.num_tokens > 0 && use_mfma && !balanced;
+  const bool fused = wr.key != nullptr && wr.num_tokens > 0 && use_mfma;
   if (wr.key != nullptr && wr.num_tokens > 0 && !fused) {  // write first, then decode
     const pa_status ws_st =
         pa_reshape_and_cache(wr.key, wr.value, const_cast<void*>(k_cache),
@@ -840,10 +805,6 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                              num_kv_heads, head_dim, dtype, stream);
     if (ws_st != PA_OK) return ws_st;
   }
-  if (balanced)
-    return launch_balanced_split(dtype, q, k_cache, v_cache, block_tables, context_lens,
-                                 scale_log2, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                 max_blocks_per_seq, ranges, ws, st);
   const int64_t num_slots = static_cast<int64_t>(wr.num_blocks) * kBlock;
   switch (dtype) {
     case PA_BF16: {
@@ -880,7 +841,6 @@ pa_status decode_int8_impl(const void* q, const void* k_cache, const void* v_cac
                            pa_dtype dtype, void* stream, const StepWrite& wr) {
   if (dtype != PA_BF16 && dtype != PA_F16) return PA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (partition_size == PA_PARTITION_BALANCED) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0)
     return PA_ERR_INVALID_ARG;

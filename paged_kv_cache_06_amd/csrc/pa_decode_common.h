@@ -1,8 +1,7 @@
-// Device pieces shared by the decode kernels (matrix-core operands, block
-// loads, the online softmax of one block, the merge of waves) and the host
-// helpers both decode paths use.  Included by pa_decode.hip (fixed
-// partitions, generic path, the decode entry points) and
-// pa_decode_balanced.hip (balanced split).
+// Device pieces shared by the decode and prefill kernels (matrix-core
+// operands, block loads, the online softmax of one block, the merge of waves)
+// and the host helpers of the decode path.  Included by pa_decode.hip (items
+// kernels, generic path, the decode entry points) and pa_prefill.hip.
 #pragma once
 
 #include <algorithm>

@@ -500,10 +500,8 @@ template <typename Tag>
 pa_status launch_prefill(const PrefillArgs& a, int head_dim, int64_t units, hipStream_t st) {
   const dim3 g3(static_cast<uint32_t>(units)), b3(kPrefillWaves * kWave);
   if (head_dim == 128)  // the ring is static LDS
-    prefill_kernel<Tag, 128><<<g3, b3, 0, st>>>(a);
-  else
-    prefill_kernel<Tag, 64><<<g3, b3, 0, st>>>(a);
-  return launch_status();
+    return launch_kernel(PA_KERNEL_PREFILL, prefill_kernel<Tag, 128>, g3, b3, 0, st, a);
+  return launch_kernel(PA_KERNEL_PREFILL, prefill_kernel<Tag, 64>, g3, b3, 0, st, a);
 }
 
 }  // namespace
@@ -551,11 +549,8 @@ pa_status pa_paged_attention_prefill(const void* q, const void* k_cache, const v
                         num_seqs * num_kv_heads * a.head_blocks;
   if (units > 0x7fffffff) return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int slot = timing_start(PA_KERNEL_PREFILL, st);
-  const pa_status s = dtype == PA_BF16 ? launch_prefill<BF16T>(a, head_dim, units, st)
-                                       : launch_prefill<F16T>(a, head_dim, units, st);
-  timing_stop(slot, st);
-  return s;
+  return dtype == PA_BF16 ? launch_prefill<BF16T>(a, head_dim, units, st)
+                          : launch_prefill<F16T>(a, head_dim, units, st);
 }
 
 }  // extern "C"

@@ -1,8 +1,9 @@
-// Kernel timing: HIP events around each library launch while timing is on.
+// Kernel timing: HIP events attached to each library launch while timing is on.
 //
-// Events are recorded on the launch's own stream, so the measured interval is
-// the kernel's run time on that stream (plus the event overhead, a few
-// microseconds at most).  Single-threaded use, like the rest of the library.
+// The two events of a launch travel with its dispatch (hipExtLaunchKernel), so
+// they record when the kernel itself starts and ends on its stream -- the
+// interval a kernel-trace profiler reports -- without marker packets of their
+// own between kernels.  Single-threaded use, like the rest of the library.
 #include <utility>
 #include <vector>
 
@@ -31,19 +32,12 @@ Timing& state() {
 
 namespace pa {
 
-int timing_start(int kind, hipStream_t stream) {
+TimedLaunch timing_events(int kind) {
   Timing& t = state();
-  if (!t.active || t.used >= static_cast<int>(t.recs.size())) return -1;
-  Record& r = t.recs[t.used];
-  if (hipEventRecord(r.start, stream) != hipSuccess) return -1;
+  if (!t.active || t.used >= static_cast<int>(t.recs.size())) return TimedLaunch{nullptr, nullptr};
+  Record& r = t.recs[t.used++];
   r.kind = kind;
-  return t.used++;
-}
-
-void timing_stop(int slot, hipStream_t stream) {
-  if (slot < 0) return;
-  Timing& t = state();
-  if (hipEventRecord(t.recs[slot].stop, stream) != hipSuccess) t.recs[slot].kind = -1;
+  return TimedLaunch{r.start, r.stop};
 }
 
 }  // namespace pa

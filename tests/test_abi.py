@@ -65,14 +65,14 @@ def test_host_only_calls_and_argument_errors_without_a_gpu():
                                        ctypes.c_void_p(16), 1.0, ctypes.c_void_p(16), 4, 8, 4,
                                        128, 64, 1024, 256, ctypes.c_void_p(256), 1024, 2, None)
     assert st == -6  # workspace without room for the partials
-    # the balanced split exists only on the matrix-core path (bf16/fp16, D 64/128)
-    st = lib.pa_paged_attention_decode(None, None, None, None, None, 1.0, None, 1, 8, 4, 128, 1,
-                                       16, pa.PARTITION_BALANCED, None, 0, 0, None)
-    assert st == -4
+    # a negative partition size other than AUTO is refused
+    st = lib.pa_paged_attention_decode(ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                       ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                       ctypes.c_void_p(16), 1.0, ctypes.c_void_p(16), 4, 8, 4,
+                                       128, 64, 1024, -2, None, 0, 2, None)
+    assert st == -1
     assert pa.decode_auto_partition(4, 8, 4, 128, 4096, 2) > 0
     assert pa.decode_auto_partition(4, 8, 4, 96, 512, 2) == pa.PARTITION_NONE
-    assert lib.pa_decode_set_max_groups(-1) == -1
-    assert lib.pa_decode_set_max_groups(0) == 0
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 4, 2, 64, 0, None) == 0
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 1, 4, 2, 64, 0, None) == -1
     assert lib.pa_copy_blocks(None, None, None, 0, 4, 2, 60, 2, None) == -1
@@ -102,7 +102,7 @@ def test_host_only_calls_and_argument_errors_without_a_gpu():
                                                   dtype, None)
     assert dec8(dtype=0) == -4  # fp32 queries
     assert dec8(d=256) == -4
-    assert dec8(part=pa.PARTITION_BALANCED) == -4
+    assert dec8(part=-2) == -1
     assert dec8(scales=None) == -1
     assert dec8(part=256) == -6  # no workspace
 
@@ -111,12 +111,11 @@ def test_empty_batches_are_no_ops_without_a_gpu():
     # zero sequences / tokens / pairs: argument checks, then PA_OK before any
     # pointer is read or anything is launched (NULL pointers are fine)
     lib = pa.load()
-    for part in (pa.PARTITION_AUTO, pa.PARTITION_NONE, 256, pa.PARTITION_BALANCED):
+    for part in (pa.PARTITION_AUTO, pa.PARTITION_NONE, 256):
         assert lib.pa_paged_attention_decode(None, None, None, None, None, 1.0, None, 0, 8, 4,
                                              128, 1, 16, part, None, 0, 2, None) == 0
         assert lib.pa_paged_attention_decode_int8(None, None, None, None, None, None, None, 1.0,
-                                                  None, 0, 8, 4, 128, 1, 16,
-                                                  part if part != pa.PARTITION_BALANCED else 0,
+                                                  None, 0, 8, 4, 128, 1, 16, part,
                                                   None, 0, 2, None) == 0
     assert lib.pa_paged_attention_prefill(None, None, None, None, None, None, 1.0, None, 0, 8,
                                           4, 128, 1, 16, 2, None) == 0
@@ -166,16 +165,6 @@ def test_workspace_size_closed_form():
     fixed_none = 256 + up(16 * entries(s)) + up(4 * s)
     assert pa.decode_workspace_bytes(s, hq, d, 1024, pa.PARTITION_NONE) == fixed_none
     assert pa.decode_workspace_bytes(s, hq, d, 256, 256) == fixed_none
-    # balanced split: meta, one range start more than ranges (16 B each), two
-    # partial slots of min(16, hq) rows (rounded up to a power of two) per
-    # range; ranges = 2048, or more when ranges of at most 512 blocks plus 2
-    # per unit are needed to cover num_seqs x hq units of the longest length
-    for hq_, d_, r in ((8, 128, 8), (64, 64, 16), (2, 128, 2), (3, 128, 4), (12, 64, 16)):
-        for max_len in (0, 100, 100000):
-            ranges = max(2048, -(-(s * hq_ * (2 + max(1, -(-max_len // 16)))) // 512))
-            rows = ranges * 2 * r
-            bal = 256 + up(16 * (ranges + 1)) + up(8 * rows) + up(4 * d_ * rows)
-            assert pa.decode_workspace_bytes(s, hq_, d_, max_len, pa.PARTITION_BALANCED) == bal
     # automatic: the fixed partition it resolves to
     auto_p = pa.decode_auto_partition(s, hq, 1, 64, 4096, 2)
     assert auto_p > 0

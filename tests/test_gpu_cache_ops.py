@@ -98,31 +98,41 @@ def test_slot_minus_one_and_out_of_range_are_skipped():
     assert k.sum().item() == 2 * 64 and v.sum().item() == 2 * 2 * 64
 
 
-@pytest.mark.parametrize("config", [2, 4])
-def test_full_size_step_writes(config):
-    """At full size: the step's tokens land in their slots, and (shared prefix) every
-    copy holds the source block's pre-step contents outside the written slots."""
+@pytest.mark.parametrize("config", [2, 3, 4, 5])
+def test_full_size_cache_after_the_step_matches_oracle_bits(config):
+    """At full size, in the benchmark's step: every block of both caches after
+    the prefill and the step (copy-on-write copies, then the step's token
+    writes) equals the oracle's cache bit for bit -- written slots, copied
+    blocks and never-written (NaN) slots alike -- and every copy-on-write copy
+    holds its source's pre-step contents outside the slots the step wrote."""
     import torch
-    print(f"[gpu] full-size step writes config={config}", flush=True)
+    print(f"[gpu] full-size cache after the step, workload {config}", flush=True)
     w = workloads.make(config)
+    ref = step.plan(w)
+    kc_ref, vc_ref = step.empty_cache(w, NAN_BITS[w.dtype])
+    for ph in ref.phases:
+        step.apply_phase(ph, kc_ref, vc_ref)
     db = runner.DeviceBatch(w)
     db.prefill()
     torch.cuda.synchronize()
     B = db.phases[2]
+    assert np.array_equal(B.pairs, ref.phases[2].pairs)
     kc, vc = db.caches[0]
     before = {}
-    for src, dst in B.pairs[:16].tolist():
+    for src, dst in B.pairs.tolist():
         kb, vb = pa.logical_view(kc[src:src + 1], vc[src:src + 1])
         before[dst] = (bits_of(kb)[0], bits_of(vb)[0])
     db.step()
     torch.cuda.synchronize()
-    k, v = (bits_of(x) for x in pa.logical_view(kc, vc))
-    sl = B.slots
-    assert np.array_equal(k[sl // 16, :, sl % 16, :], B.key)
-    assert np.array_equal(v[sl // 16, :, sl % 16, :], B.value)
-    written = set(sl.tolist())
+    (k, v), = _device_logical(db)
+    nb = w.num_blocks
+    assert _same_bits(k[:nb], kc_ref) and _same_bits(v[:nb], vc_ref)
+    assert _same_bits(k[nb:], np.full_like(k[nb:], NAN_BITS[w.dtype]))  # poison block
+    written = set(B.slots.tolist())
     for dst, (kb, vb) in before.items():
-        for r in range(16):
-            if dst * 16 + r not in written:
-                assert np.array_equal(k[dst, :, r], kb[:, r])
-                assert np.array_equal(v[dst, :, r], vb[:, r])
+        keep = [r for r in range(16) if dst * 16 + r not in written]
+        assert np.array_equal(k[dst][:, keep], kb[:, keep])
+        assert np.array_equal(v[dst][:, keep], vb[:, keep])
+    print(f"  {nb} blocks, {len(B.slots)} step tokens, {len(B.pairs)} copies", flush=True)
+    if config == 4:
+        assert len(B.pairs) == 192  # 64 prompts x (4 - 1) writers of the shared partial block

@@ -1,11 +1,11 @@
 """paged_attention_decode on the GPU against the oracle.
 
-Small cases compare every output with the oracle's paged decode (tables and
-cache built by the oracle itself).  The five workloads run at full size in the
-launch configuration the benchmark times; there the oracle computes sampled
-sequences one by one from their contiguous K/V, and properties that hold at any
-size (split == unsplit, run-to-run and block-relabelling invariance) cover the
-rest.
+Every case compares every output with the oracle's paged decode (tables and
+cache built by the oracle itself from the same seeded inputs): small shape
+cases, and the five workloads at full size in the launch configuration the
+benchmark times (the long-context workload also at its stated split of 512
+positions).  Properties that hold at any size (split == unsplit, run-to-run
+and block-relabelling invariance) are checked beside them.
 """
 import numpy as np
 import pytest
@@ -13,7 +13,7 @@ import torch
 
 import paged_kv_cache_06_amd as pa
 import workloads
-from oracle import attention, step
+from oracle import step
 from oracle.numerics import to_f64
 from paged_kv_cache_06_amd import runner
 from tests.helpers import NAN_BITS, assert_close, bits_of
@@ -61,48 +61,32 @@ def test_small_cases_against_oracle(lens, hq, hkv, d, dtype, partition_size):
     assert_close(db.out_bits(), ref, dtype, f"{lens} {hq}/{hkv} d={d} {dtype}")
 
 
-@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f16")])
-@pytest.mark.parametrize("partition_size", [2048, 4096])
-def test_eight_wave_items_against_oracle(d, dtype, partition_size):
-    # partitions of >= 2048 positions run the items kernel with 8 waves per work-group
-    print(f"[gpu] 8-wave items d={d} {dtype} P={partition_size}", flush=True)
-    lens = [17, 100, 2100, 4500, 9000]
-    w = workloads.make_custom(lens, hq=16, hkv=2, d=d, dtype=dtype, seed=partition_size + d)
-    db, ref = _run_small(w, partition_size)
-    assert_close(db.out_bits(), ref, dtype, f"8 waves {d} {dtype} P={partition_size}")
+EIGHT_WAVE_CASES = [
+    # (hq, hkv, d, dtype): 8 waves per item at D 64, and at D 128 up to 15
+    # query heads per KV head; 16 or more at D 128 fall back to 4 waves
+    (16, 2, 128, "bf16"),   # G = 8: 8 waves
+    (16, 2, 64, "f16"),     # G = 8: 8 waves
+    (32, 2, 64, "bf16"),    # G = 16, D 64: 8 waves, a full 16-head block
+    (32, 2, 128, "bf16"),   # G = 16, D 128: 4 waves (8 waves' partials exceed 64 KiB)
+    (64, 2, 128, "f16"),    # G = 32: 4 waves, 2 head blocks
+    (64, 1, 128, "bf16"),   # G = 64: 4 waves, 4 head blocks
+]
 
 
-@pytest.mark.parametrize("mode", [pa.PARTITION_BALANCED])
-@pytest.mark.parametrize("groups", [1, 2, 3, 7, 64, 0])
-@pytest.mark.parametrize("hq,hkv,d,dtype", [(16, 2, 128, "bf16"), (8, 8, 64, "f16"),
-                                            (64, 2, 128, "f16"), (32, 1, 128, "bf16")])
-def test_balanced_split_on_any_grid(mode, groups, hq, hkv, d, dtype):
-    # the range cuts move with the grid: one range (no cut) up to units cut
-    # into many pieces; then two sequences emptied, whose single empty block
-    # still goes through the schedule and must give zeros
-    import torch
-    lens = [1, 15, 16, 17, 33, 100, 257, 600, 3, 2000, 5]
-    print(f"[gpu] balanced split mode={mode} groups={groups} hq={hq} hkv={hkv} d={d} {dtype}",
+@pytest.mark.parametrize("hq,hkv,d,dtype", EIGHT_WAVE_CASES)
+@pytest.mark.parametrize("partition_size", [pa.PARTITION_AUTO, 2048, 4096])
+def test_long_context_items_against_oracle(hq, hkv, d, dtype, partition_size):
+    # a batch whose longest context passes 16K positions: partitions of >= 2048
+    # positions run the items kernel with 8 waves per work-group where the
+    # partials fit the LDS, 4 otherwise
+    print(f"[gpu] long-context items hq={hq} hkv={hkv} d={d} {dtype} P={partition_size}",
           flush=True)
-    w = workloads.make_custom(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=groups + hq)
-    pa.decode_set_max_groups(groups)
-    try:
-        db, ref = _run_small(w, mode)
-        assert_close(db.out_bits(), ref, dtype, f"balanced groups={groups}")
-        cut = db.context_lens.clone()
-        cut[0] = 0
-        cut[8] = 0
-        out = torch.full_like(db.out, float("nan"))
-        kc, vc = db.caches[0]
-        pa.paged_attention_decode(db.q, kc, vc, db.tables, cut, w.scale, out,
-                                  max_context_len=db.max_context_len, partition_size=mode)
-        torch.cuda.synchronize()
-    finally:
-        pa.decode_set_max_groups(0)
-    got = bits_of(out)
-    assert not got[[0, 8]].any()
-    keep = [i for i in range(len(lens)) if i not in (0, 8)]
-    assert_close(got[keep], ref[keep], dtype, f"balanced groups={groups}, two rows emptied")
+    lens = [17, 100, 2100, 4500, 16500]
+    w = workloads.make_custom(lens, hq=hq, hkv=hkv, d=d, dtype=dtype,
+                              seed=hq + d + max(partition_size, 0))
+    db, ref = _run_small(w, partition_size)
+    assert_close(db.out_bits(), ref, dtype,
+                 f"long context {hq}/{hkv} {d} {dtype} P={partition_size}")
 
 
 def test_tiny_config_every_output():
@@ -209,9 +193,12 @@ def test_nan_in_table_padding_and_block_tails_does_not_leak():
 # ---- full-size workloads, in the benchmark's launch configuration ----
 
 _FULL = {}
+_ORACLE = {}
 
 
 def _full(config):
+    """The workload on the device after the benchmark's step (copies, token
+    writes, decode with the automatic partition); one workload kept at a time."""
     if config not in _FULL:
         _FULL.clear()
         import torch
@@ -224,29 +211,36 @@ def _full(config):
     return _FULL[config]
 
 
-def _sample(w, k=6):
-    lens = np.asarray(w.context_lens)
-    order = np.argsort(lens, kind="stable")
-    picks = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
-    rng = np.random.default_rng(0)
-    picks |= set(int(x) for x in rng.choice(len(lens), size=min(k, len(lens)), replace=False))
-    return sorted(picks)
+def _oracle_full(config):
+    """The oracle's run of the same workload: (plan, k_cache, v_cache, out)."""
+    if config not in _ORACLE:
+        _ORACLE.clear()
+        w, _ = _full(config)
+        _ORACLE[config] = step.run(w, NAN_BITS[w.dtype])
+    return _ORACLE[config]
 
 
 @pytest.mark.parametrize("config", [2, 3, 4, 5])
-def test_full_size_sampled_sequences_against_oracle(config):
-    print(f"[gpu] full-size workload {config}: sampled oracle check", flush=True)
+def test_full_size_every_output_against_oracle(config):
+    print(f"[gpu] full-size workload {config}: every output against the oracle", flush=True)
     w, db = _full(config)
-    got = db.out_bits()
-    q = to_f64(w.q, w.dtype)
-    group = w.num_q_heads // w.num_kv_heads
-    for s in _sample(w, 4 if config == 5 else 6):
-        kb, vb = w.sequence_kv(s)
-        K, V = to_f64(kb, w.dtype), to_f64(vb, w.dtype)
-        ref = np.stack([attention.attend(q[s, h], K[:, h // group], V[:, h // group], w.scale)
-                        for h in range(w.num_q_heads)])
-        info = assert_close(got[s], ref, w.dtype, f"workload {config} seq {s}")
-        print(f"  seq {s} len {int(w.context_lens[s])}: {info}", flush=True)
+    _, _, _, ref = _oracle_full(config)
+    info = assert_close(db.out_bits(), ref, w.dtype, f"workload {config}")
+    print(f"  {w.num_seqs} sequences x {w.num_q_heads} heads: {info}", flush=True)
+
+
+def test_full_size_long_context_at_its_stated_split():
+    # the long-context workload names split-K partitions of 512 positions
+    # plus a reduce: every output of that launch against the oracle
+    import torch
+    print("[gpu] full-size workload 5 at partitions of 512: every output", flush=True)
+    w, db = _full(5)
+    _, _, _, ref = _oracle_full(5)
+    out = torch.full_like(db.out, float("nan"))
+    db.decode(partition_size=512, out=out)
+    torch.cuda.synchronize()
+    info = assert_close(bits_of(out), ref, w.dtype, "workload 5, P = 512")
+    print(f"  {info}", flush=True)
 
 
 @pytest.mark.parametrize("config", [3, 5])
@@ -266,7 +260,7 @@ def test_full_size_split_equals_unsplit_and_is_deterministic(config):
     # to the storage dtype the results are at most one unit in its last place
     # apart, or 1e-5 where the output is that small.
     ulp = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -10
-    for ps in (pa.PARTITION_NONE, 256, 1024, pa.PARTITION_BALANCED):
+    for ps in (pa.PARTITION_NONE, 256, 512, 1024):
         db.decode(partition_size=ps, out=out2)
         c = to_f64(bits_of(out2), w.dtype)
         ratio = np.abs(c - b) / (ulp * np.abs(b) + 1e-5)
@@ -301,7 +295,6 @@ def test_full_size_shared_prefix_through_cache_is_bit_identical_to_forks():
 @pytest.mark.parametrize("dtype,d,partition_size", [("bf16", 128, pa.PARTITION_AUTO),
                                                     ("f16", 64, 64),
                                                     ("bf16", 128, pa.PARTITION_NONE),
-                                                    ("bf16", 128, pa.PARTITION_BALANCED),
                                                     ("f32", 64, pa.PARTITION_AUTO)])
 def test_fused_step_equals_write_then_decode(dtype, d, partition_size):
     """decode_step (token writes in the plan's launch where it can) against

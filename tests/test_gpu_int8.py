@@ -10,7 +10,7 @@ import pytest
 
 import paged_kv_cache_06_amd as pa
 import workloads
-from oracle import attention, quant, step
+from oracle import quant, step
 from oracle.numerics import to_f64
 from paged_kv_cache_06_amd import runner
 from tests.helpers import assert_close, bits_of
@@ -89,17 +89,22 @@ def test_small_cases_against_oracle(lens, hq, hkv, d, dtype, partition_size):
     assert_close(db.out_bits(), ref, dtype, f"int8 {lens} P={partition_size}")
 
 
-@pytest.mark.parametrize("partition_size", [4096, 8192])
-def test_eight_wave_items_against_oracle(partition_size):
-    # INT8 partitions of >= 4096 positions run with 8 waves per work-group
-    print(f"[gpu] int8 8-wave items P={partition_size}", flush=True)
-    lens = [17, 100, 4200, 9000]
-    w = workloads.make_custom(lens, hq=16, hkv=2, d=128, dtype="bf16", seed=partition_size)
+@pytest.mark.parametrize("hq,hkv,d", [(16, 2, 128), (32, 2, 64), (32, 2, 128), (64, 2, 128),
+                                      (64, 1, 128)])
+@pytest.mark.parametrize("partition_size", [pa.PARTITION_AUTO, 4096, 8192])
+def test_long_context_items_against_oracle(hq, hkv, d, partition_size):
+    # a batch whose longest context passes 16K positions: INT8 partitions of
+    # >= 4096 positions run with 8 waves per work-group where the partials fit
+    # the LDS (G <= 15 at D 128, G <= 16 at D 64), 4 otherwise
+    print(f"[gpu] int8 long-context items {hq}/{hkv} D={d} P={partition_size}", flush=True)
+    lens = [17, 100, 4200, 16500]
+    w = workloads.make_custom(lens, hq=hq, hkv=hkv, d=d, dtype="bf16",
+                              seed=hq + d + max(partition_size, 0))
     _, _, _, ref = step.run_int8(w)
     db = runner.DeviceBatch(w, int8=True)
     db.prefill()
     db.step(partition_size=partition_size)
-    assert_close(db.out_bits(), ref, "bf16", f"int8 8 waves P={partition_size}")
+    assert_close(db.out_bits(), ref, "bf16", f"int8 long context {hq}/{hkv} P={partition_size}")
 
 
 def test_shared_prefix_and_zero_length_rows():
@@ -138,31 +143,28 @@ def _full(config):
     return _FULL[config]
 
 
-def _oracle_sequence(w, s):
-    """Oracle output of one sequence: quantize its contiguous K/V token by
-    token with the workload's scales, then attend over code * scale."""
-    sk, sv = w.int8_scales()
-    kb, vb = w.sequence_kv(s)
-    K = quant.dequantize(quant.quantize(kb, w.dtype, sk), sk)
-    V = quant.dequantize(quant.quantize(vb, w.dtype, sv), sv)
-    q = to_f64(w.q[s], w.dtype)
-    group = w.num_q_heads // w.num_kv_heads
-    return np.stack([attention.attend(q[h], K[:, h // group], V[:, h // group], w.scale)
-                     for h in range(w.num_q_heads)])
+_ORACLE = {}
+
+
+def _oracle_full(config):
+    """The oracle's INT8 run of the same workload: (plan, k_codes, v_codes, out)."""
+    if config not in _ORACLE:
+        _ORACLE.clear()
+        w, _ = _full(config)
+        _ORACLE[config] = step.run_int8(w)
+    return _ORACLE[config]
 
 
 @pytest.mark.parametrize("config", [3, 5])
-def test_full_size_sampled_sequences_against_oracle(config):
-    print(f"[gpu] int8 full-size workload {config}: sampled oracle check", flush=True)
+def test_full_size_every_output_and_code_against_oracle(config):
+    print(f"[gpu] int8 full-size workload {config}: every output and every code", flush=True)
     w, db = _full(config)
-    got = db.out_bits()
-    lens = np.asarray(w.context_lens)
-    order = np.argsort(lens, kind="stable")
-    picks = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]),
-                    *np.random.default_rng(0).choice(len(lens), 3, replace=False).tolist()})
-    for s in picks:
-        info = assert_close(got[s], _oracle_sequence(w, s), w.dtype, f"int8 workload {config} seq {s}")
-        print(f"  seq {s} len {int(lens[s])}: {info}", flush=True)
+    _, k_ref, v_ref, ref = _oracle_full(config)
+    info = assert_close(db.out_bits(), ref, w.dtype, f"int8 workload {config}")
+    print(f"  {w.num_seqs} sequences x {w.num_q_heads} heads: {info}", flush=True)
+    k, v = _codes(db)
+    nb = w.num_blocks
+    assert np.array_equal(k[:nb], k_ref) and np.array_equal(v[:nb], v_ref)
 
 
 def test_full_size_split_equals_unsplit_and_is_deterministic():
@@ -175,7 +177,7 @@ def test_full_size_split_equals_unsplit_and_is_deterministic():
     assert np.array_equal(bits_of(out2), base)
     b = to_f64(base, w.dtype)
     ulp = 2.0 ** -7
-    for ps in (pa.PARTITION_NONE, 256):
+    for ps in (pa.PARTITION_NONE, 256, 1024):
         db.decode(partition_size=ps, out=out2)
         c = to_f64(bits_of(out2), w.dtype)
         ratio = np.abs(c - b) / (ulp * np.abs(b) + 1e-5)

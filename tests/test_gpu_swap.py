@@ -103,29 +103,3 @@ def test_batch_swapped_out_and_back_in_decodes_identically(int8):
     db.decode()
     torch.cuda.synchronize()
     assert np.array_equal(db.out_bits(), base)
-
-
-def test_transfer_bandwidth_over_the_host_link():
-    """Not a correctness check: prints the device <-> pinned host block rate."""
-    import torch
-    print("[gpu] transfer bandwidth", flush=True)
-    nb, hkv, d = 2048, 8, 128  # 64 KiB per block (K + V), the 70B layer shape in bf16
-    kd, vd = pa.new_kv_cache(nb, hkv, d, torch.bfloat16, "cuda", 1.0)
-    kh, vh = pa.new_host_kv_cache(nb, hkv, d, torch.bfloat16)
-    perm = torch.randperm(nb)
-    pairs = torch.stack([perm, torch.arange(nb)], 1).to(torch.int64).cuda()
-    for direction in ("out", "in"):
-        args = (kd, vd, kh, vh) if direction == "out" else (kh, vh, kd, vd)
-        pa.transfer_blocks(*args, pairs)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(5):
-            pa.transfer_blocks(*args, pairs)
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / 5
-        gbs = nb * 2 * hkv * 16 * d * 2 / (ms * 1e-3) / 1e9
-        print(f"  swap {direction}: {nb} blocks of 64 KiB in {ms:.3f} ms = {gbs:.1f} GB/s", flush=True)
-        assert gbs > 0
