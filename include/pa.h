@@ -306,6 +306,28 @@ pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const vo
                                     int32_t partition_size, void* workspace,
                                     size_t workspace_bytes, pa_dtype dtype, void* stream);
 
+/* pa_paged_attention_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace in a scratch
+ * array of PA_DECODE_SCRATCH_BYTES that the library holds in device memory,
+ * one per device, until the process ends.  The call allocates nothing.
+ * Arguments as pa_paged_attention_decode without workspace and
+ * workspace_bytes; PA_ERR_WORKSPACE when the call would need more than
+ * PA_DECODE_SCRATCH_BYTES (pa_decode_workspace_bytes gives the need; a
+ * larger partition size needs less), PA_ERR_DEVICE when no device is
+ * current.  Every call on one device shares that device's array and
+ * rewrites what it reads, so calls that overlap on one device (different
+ * streams without ordering, or different host threads) race; calls ordered
+ * on one stream do not. */
+#define PA_DECODE_SCRATCH_BYTES ((size_t)128 << 20)
+pa_status pa_paged_attention_decode_noalloc(const void* q, const void* k_cache,
+                                            const void* v_cache, const int32_t* block_tables,
+                                            const int32_t* context_lens, float scale, void* out,
+                                            int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                                            int32_t partition_size, pa_dtype dtype, void* stream);
+
 /* Chunked prefill: sequence s appends a chunk of n_s new tokens whose K/V are
  * already in the cache (pa_reshape_and_cache first, as for decode); query i
  * of the chunk sits at position p = len_s - n_s + i and attends to positions

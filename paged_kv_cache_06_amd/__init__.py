@@ -24,7 +24,8 @@ import numpy as np
 __all__ = [
     "BLOCK_SIZE", "PARTITION_NONE", "PARTITION_AUTO", "PAError", "load", "lib_path",
     "Pool", "BlockManager", "blocks_for_bytes", "reshape_and_cache", "copy_blocks",
-    "paged_attention_decode", "decode_workspace_bytes", "decode_auto_partition",
+    "paged_attention_decode", "paged_attention_decode_noalloc", "DECODE_SCRATCH_BYTES",
+    "decode_workspace_bytes", "decode_auto_partition",
     "reshape_and_cache_int8", "paged_attention_decode_int8",
     "swap_blocks", "transfer_blocks", "new_host_kv_cache", "paged_attention_prefill",
     "decode_step", "decode_step_int8",
@@ -32,6 +33,7 @@ __all__ = [
 ]
 
 BLOCK_SIZE = 16
+DECODE_SCRATCH_BYTES = 128 << 20  # PA_DECODE_SCRATCH_BYTES
 PARTITION_NONE = 0
 PARTITION_AUTO = -1
 KERNEL_KINDS = ("decode", "decode_reduce", "reshape_and_cache", "copy_blocks", "decode_plan",
@@ -81,6 +83,9 @@ _SIGNATURES = {
     "pa_paged_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_p, _c_i32,
                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                            _c_p, _c_sz, _c_i32, _c_p]),
+    "pa_paged_attention_decode_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_p,
+                                                   _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                   _c_i32, _c_i32, _c_i32, _c_p]),
     "pa_reshape_and_cache_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "pa_paged_attention_decode_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f,
@@ -562,6 +567,31 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens.contiguous()),
         float(scale), _ptr(out), s, hq, hkv, d, mb, mcl, int(partition_size), ws_ptr, ws_bytes,
         _dtype_code(q), _stream(q)), "pa_paged_attention_decode")
+
+
+def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                   *, max_context_len: int | None = None,
+                                   partition_size: int = PARTITION_AUTO) -> None:
+    """paged_attention_decode with its workspace in the library's per-device
+    scratch array (``pa_paged_attention_decode_noalloc``): no device memory is
+    allocated by the call.  Calls that overlap on one device race."""
+    torch = _torch()
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    s, hq, dq = q.shape
+    _need(dq == d and tuple(out.shape) == (s, hq, d), "q/out must be [S, Hq, D]")
+    _need(q.is_contiguous() and out.is_contiguous(), "q/out must be contiguous")
+    _need(q.dtype == out.dtype == k_cache.dtype, "dtypes differ")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == s and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == s and
+          context_lens.is_contiguous(), "context_lens must be contiguous int32 [S]")
+    mb = block_tables.shape[1]
+    mcl = mb * BLOCK_SIZE if max_context_len is None else int(max_context_len)
+    _check(load().pa_paged_attention_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), _ptr(out), s, hq, hkv, d, mb, mcl, int(partition_size), _dtype_code(q),
+        _stream(q)), "pa_paged_attention_decode_noalloc")
 
 
 def decode_step(key, value, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, scale,

@@ -50,6 +50,8 @@
 // Generic path (any supported dtype/head_dim, fp32 in particular): one
 // work-group per query head, VALU dot products, 256-position chunks with the
 // same online softmax and the same partial-result format.
+#include <mutex>
+
 #include "pa_decode_int8.h"
 #include "pa_cache_write.h"
 #include "pa_decode_common.h"
@@ -886,6 +888,41 @@ pa_status decode_int8_impl(const void* q, const void* k_cache, const void* v_cac
 }  // namespace
 }  // namespace pa
 
+// ---- the decode entry point that allocates nothing ----
+//
+// pa_paged_attention_decode_noalloc runs the same kernels with its workspace
+// in `scratch`, a file-scope array of PA_DECODE_SCRATCH_BYTES in device
+// memory: each device the library runs on holds its own copy, at its own
+// address, until the process ends.  Host code never names the array in a
+// launch or a copy: on the host its name is only a stand-in, so the device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept.
+static __device__ __align__(256) char scratch[PA_DECODE_SCRATCH_BYTES];
+
+namespace pa {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's `scratch`, or null (no device, or
+// the symbol cannot be resolved).
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+}  // namespace pa
+
 extern "C" {
 
 pa_status pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -967,6 +1004,23 @@ pa_status pa_decode_step_int8(const void* key, const void* value, const int64_t*
                           max_blocks_per_seq, max_context_len, partition_size, workspace,
                           workspace_bytes, dtype, stream,
                           StepWrite{key, value, slot_mapping, num_new_tokens, num_blocks});
+}
+
+pa_status pa_paged_attention_decode_noalloc(const void* q, const void* k_cache,
+                                            const void* v_cache, const int32_t* block_tables,
+                                            const int32_t* context_lens, float scale, void* out,
+                                            int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                                            int32_t partition_size, pa_dtype dtype, void* stream) {
+  // an empty batch (or an argument error) needs no device and no workspace
+  void* ws = num_seqs > 0 ? pa::scratch_address() : nullptr;
+  if (num_seqs > 0 && ws == nullptr) return PA_ERR_DEVICE;
+  return pa::decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                         num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                         max_context_len, partition_size, ws,
+                         ws ? static_cast<size_t>(PA_DECODE_SCRATCH_BYTES) : 0, dtype, stream,
+                         pa::StepWrite{nullptr, nullptr, nullptr, 0, 0});
 }
 
 }  // extern "C"
