@@ -173,6 +173,21 @@ def test_planted_swap_without_release_is_caught(monkeypatch):
         tsw.test_random_swaps_conserve_references_in_both_tiers()
 
 
+def test_planted_per_listing_check_is_caught(monkeypatch):
+    def per_listing(src, dst, blocks):
+        if dst.num_free() < len(blocks):
+            raise pool.OutOfBlocks("short")
+        pairs = []
+        for b in blocks:  # checks each listing as it comes, after earlier frees
+            src._check(b)
+            pairs.append((int(b), dst.alloc()))
+            src.free(b)
+        return pairs
+    monkeypatch.setattr(tsw, "swap_blocks", per_listing)
+    with pytest.raises(AssertionError):
+        tsw.test_a_block_listed_more_often_than_held_changes_nothing()
+
+
 def test_planted_backwards_transfer_is_caught(monkeypatch):
     def backwards(src_k, src_v, dst_k, dst_v, pairs):
         for s, d in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():

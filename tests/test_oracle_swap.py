@@ -83,6 +83,44 @@ def test_swap_is_all_or_nothing():
             list(cpu.free_stack)) == before
 
 
+def _snapshot(*pools):
+    return [(list(p.refcount), list(p.free_stack)) for p in pools]
+
+
+def test_a_block_listed_more_often_than_held_changes_nothing():
+    """Each listing of a block moves one reference the caller holds, and a
+    swap is all or nothing ("KV Cache and PagedAttention: why your LLM server
+    slows down", section "How PagedAttention fixes this": single pages move to
+    the CPU; reading R18): a block held once and listed twice is refused with
+    both pools' counts and free stacks exactly as they were."""
+    gpu = BlockPool(8, free_order=range(8))
+    cpu = BlockPool(8, free_order=range(8))
+    t = []
+    gpu.append(t, 0, 32)  # blocks 0 and 1, one reference each
+    before = _snapshot(gpu, cpu)
+    with pytest.raises(BadBlock):
+        swap_blocks(gpu, cpu, [t[0], t[1], t[0]])
+    assert _snapshot(gpu, cpu) == before
+    with pytest.raises(BadBlock):
+        swap_blocks(gpu, cpu, [t[1], t[1]])
+    assert _snapshot(gpu, cpu) == before
+
+
+def test_a_block_held_twice_and_listed_twice_moves_both_references():
+    """Two holders of one block (a fork) swapping it together: each listing
+    gets its own destination block and drops one source reference, so the
+    source block is free afterwards and each copy is held once."""
+    gpu = BlockPool(8, free_order=range(8))
+    cpu = BlockPool(8, free_order=range(8))
+    a = []
+    gpu.append(a, 0, 16)  # block 0
+    gpu.fork(a)           # a second holder: count 2
+    pairs = swap_blocks(gpu, cpu, [a[0], a[0]])
+    assert pairs == [(0, 0), (0, 1)]
+    assert gpu.refcount[0] == 0 and gpu.num_free() == 8
+    assert cpu.refcount[0] == cpu.refcount[1] == 1 and cpu.num_free() == 6
+
+
 def test_fine_grained_eviction_moves_only_what_is_needed():
     """The page's contrast: freeing k device blocks by moving single blocks
     moves k of them; moving whole sequences moves every block of each
