@@ -183,52 +183,105 @@ def host_cpu():
     return {"cpu_model": model, "usable_cpus": usable}
 
 
-def cpu_baseline(w, budget_s, int8=False):
-    """The oracle (fp64 NumPy) on the first sequences of the batch, ~budget_s of work
-    (INT8 cache: the oracle's quantization of each sequence's K/V, then attention
-    over code * scale)."""
+# Oracle state the CPU baseline's worker processes share: set in the parent
+# before the pool forks, read (never written) by the children.
+_ORACLE_STATE = {}
+
+
+def _oracle_cache(w, int8):
+    """The oracle's own pool, tables and paged cache of the batch after its
+    step (not timed)."""
     import numpy as np
+    from oracle import cache_ops, quant, step
+    pl = step.plan(w)
+    if int8:
+        sk, sv = w.int8_scales()
+        shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        kc = np.full(shape, 127, np.int8)
+        vc = kc.copy()
+        for ph in pl.phases:
+            cache_ops.copy_blocks(kc, vc, ph.pairs)
+            quant.reshape_and_cache(ph.key, ph.value, w.dtype, kc, vc, ph.slots, sk, sv)
+        return pl.tables, kc, vc, sk, sv
+    kc, vc = step.empty_cache(w, 0)
+    for ph in pl.phases:
+        step.apply_phase(ph, kc, vc)
+    return pl.tables, kc, vc, None, None
+
+
+def _oracle_decode(seqs):
+    """The oracle's paged decode (gather through its table, fp64 attention) of
+    the given sequences, BLAS on one thread; returns (tokens, bytes)."""
     from oracle import attention, quant
-    from oracle.numerics import to_f64
     from threadpoolctl import threadpool_limits
-    limiter = threadpool_limits(1)  # the oracle is a single-threaded loop; keep BLAS at 1
-    threads = 1
-    q = to_f64(w.q, w.dtype)
-    group = w.num_q_heads // w.num_kv_heads
-    e = w.elem_bytes
-    ec = 1 if int8 else e
-    sk, sv = w.int8_scales() if int8 else (None, None)
-    done_tokens, done_bytes, seqs, passes = 0, 0, 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:  # whole passes over the batch, or a prefix
-        for s in range(w.num_seqs):
-            kb, vb = w.sequence_kv(s)
+    w, int8 = _ORACLE_STATE["w"], _ORACLE_STATE["int8"]
+    tables, kc, vc, sk, sv = _ORACLE_STATE["cache"]
+    lens = w.context_lens
+    ec = 1 if int8 else w.elem_bytes
+    tokens = nbytes = 0
+    with threadpool_limits(1):
+        for s in seqs:
             if int8:
-                K = quant.dequantize(quant.quantize(kb, w.dtype, sk), sk)
-                V = quant.dequantize(quant.quantize(vb, w.dtype, sv), sv)
+                quant.paged_decode(w.q[s:s + 1], kc, vc, sk, sv, [tables[s]], lens[s:s + 1],
+                                   w.scale, w.dtype)
             else:
-                K, V = to_f64(kb, w.dtype), to_f64(vb, w.dtype)
-            for g in range(w.num_kv_heads):
-                for h in range(g * group, (g + 1) * group):
-                    attention.attend(q[s, h], K[:, g], V[:, g], w.scale)
-            n = int(w.context_lens[s])
-            done_tokens += n
-            done_bytes += (n * 2 * w.num_kv_heads * w.head_dim * ec
-                           + 2 * w.num_q_heads * w.head_dim * e)
-            seqs += 1
+                attention.paged_decode(w.q[s:s + 1], kc, vc, [tables[s]], lens[s:s + 1],
+                                       w.scale, w.dtype)
+            n = int(lens[s])
+            tokens += n
+            nbytes += n * 2 * w.num_kv_heads * w.head_dim * ec + 2 * w.num_q_heads * w.head_dim * w.elem_bytes
+    return tokens, nbytes
+
+
+def cpu_baseline(w, budget_s, int8=False):
+    """The oracle's decode of the batch on the host cores, ~budget_s of work per
+    run: once on one core (sequences in order, whole passes or a prefix), then
+    on all usable cores (a pool of forked worker processes, one BLAS thread
+    each, over about as many whole passes as fit the budget at the one-core
+    rate times the workers).  Runs before the GPU is touched, so no worker
+    inherits device state.  INT8 cache: attention over the oracle's code *
+    scale values."""
+    import multiprocessing
+
+    _ORACLE_STATE.update(w=w, int8=int8, cache=_oracle_cache(w, int8))
+    order = list(range(w.num_seqs))
+    # one core
+    tok1 = by1 = seqs1 = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for s in order:
+            t, b = _oracle_decode([s])
+            tok1, by1, seqs1 = tok1 + t, by1 + b, seqs1 + 1
             if time.perf_counter() - t0 > budget_s:
                 break
-        passes += 1
-    dt = time.perf_counter() - t0
-    limiter.restore_original_limits()
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    dt1 = time.perf_counter() - t0
+    # all usable cores (at most 16 processes)
+    workers = max(1, min(16, host_cpu()["usable_cpus"] or 1))
+    passes = max(1, int(round(seqs1 / dt1 * workers * budget_s / w.num_seqs)))
+    work = [[s] for _ in range(passes) for s in order]
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_decode, [[0]] * workers)  # workers started and warm
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_decode, work, chunksize=4)
+        dtn = time.perf_counter() - t0
+    _ORACLE_STATE.clear()
+    tokn = sum(t for t, _ in res)
+    byn = sum(b for _, b in res)
+    what = ("fp64 NumPy attention over the oracle's INT8 codes x scales, gathered through its "
+            "tables" if int8 else "fp64 NumPy attention, K/V gathered through the oracle's own "
+            "block tables from its paged cache")
+    return {"value": round(byn / dtn / 1e9, 4), "unit": "GB/s", "cores": workers,
             "kind": "oracle",
-            "tokens_per_s": round(done_tokens / dt, 1),
+            "tokens_per_s": round(tokn / dtn, 1),
+            "single_core": {"value": round(by1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                            "tokens_per_s": round(tok1 / dt1, 1)},
             "host": host_cpu(),
-            "sample": f"{seqs} sequence decodes in {passes} pass(es) over the {w.num_seqs}-sequence "
-                      f"batch ({done_tokens} attended tokens), oracle decode (fp64 NumPy "
-                      f"gather{' + INT8 quantize/dequantize' if int8 else ''} + softmax "
-                      f"attention), {dt:.1f} s"}
+            "sample": f"oracle paged decode ({what}) of the {w.num_seqs}-sequence batch: on 1 "
+                      f"core {seqs1} sequence decodes ({tok1} attended tokens) in {dt1:.1f} s; "
+                      f"on {workers} worker processes (1 BLAS thread each) {passes} whole "
+                      f"pass(es) ({len(work)} sequence decodes, {tokn} attended tokens) in "
+                      f"{dtn:.1f} s"}
 
 
 HOST_LINK_PEAK_GBS = 63.0  # PCIe 5.0 x16 per direction: 32 GT/s x 16 lanes x 128/130
@@ -422,7 +475,8 @@ def main():
     ap.add_argument("--prefill", action="store_true",
                     help="instead of decode steps: the chunked-prefill workload (16 sequences, "
                          "512-token chunks after U{0..3584} cached tokens, 32/8 heads, D 128)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="seconds of oracle work per CPU-baseline run (one core, all cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 plain device copies of MIB MiB (a known-size "
@@ -452,6 +506,16 @@ def main():
         sys.exit(2)
 
     import numpy as np
+
+    cpu = None
+    if not (args.swap or args.prefill or args.no_cpu_baseline):
+        # the oracle on the host cores first, before anything touches the GPU
+        import workloads
+        cpu = cpu_baseline(workloads.make(args.config), args.cpu_seconds, args.kv == "int8")
+        print(f"# cpu baseline: {cpu['tokens_per_s']:.0f} tokens/s on {cpu['cores']} "
+              f"processes, {cpu['single_core']['tokens_per_s']:.0f} on one", file=sys.stderr,
+              flush=True)
+
     import torch
 
     if not torch.cuda.is_available():
@@ -564,8 +628,8 @@ def main():
     if args.calibrate_copy > 0:
         calibration_copies(args.calibrate_copy)
         result["calibration_copy_bytes"] = args.calibrate_copy << 20
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, int8)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
