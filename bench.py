@@ -94,6 +94,38 @@ def step_bytes(w, db, int8=False):
     return decode_bytes(w, int8, db.bm.rows) + writes + copies
 
 
+def kv_memory(w, db):
+    """The pages' memory figures for this batch, from the library's block pool:
+    slots the paged cache holds against the tokens it stores, against a
+    contiguous reservation of the batch's longest context per sequence, and
+    (shared prompts) blocks held against the same prompts with one sample each
+    and against every sample holding its own copy."""
+    import numpy as np
+    import paged_kv_cache_06_amd as pa
+    lens = np.asarray(w.context_lens, dtype=np.int64)
+    used = db.bm.pool.stats()["used"]
+    tokens = unique_kv_tokens(lens, db.bm.rows)  # distinct cached positions
+    paged_slots = used * 16
+    reserved = int(lens.max()) * w.num_seqs
+    out = {"tokens": int(tokens), "blocks_held": int(used), "paged_slots": int(paged_slots),
+           "paged_waste_pct": round(100.0 * (paged_slots - tokens) / paged_slots, 3),
+           "contiguous_reserved_slots": int(reserved),
+           "contiguous_waste_pct": round(100.0 * (reserved - lens.sum()) / reserved, 3)}
+    prompts = np.asarray(w.prompt_of)
+    if (prompts >= 0).any():
+        first = [int(np.flatnonzero(prompts == p)[0]) for p in range(len(w.prompt_lens))]
+        pool = pa.Pool(w.num_blocks)
+        bm = pa.BlockManager(pool, len(first), db.bm.rows.shape[1])
+        for i, s in enumerate(first):
+            bm.append(i, int(w.prompt_lens[prompts[s]]))
+            bm.append(i, int(w.private_lens[s]))
+        out.update(samples_per_prompt=round(w.num_seqs / len(first), 3),
+                   blocks_one_sample_per_prompt=int(pool.stats()["used"]),
+                   blocks_every_sample_unshared=int((-(-lens // 16)).sum()))
+        out["shared_vs_one_sample"] = round(used / out["blocks_one_sample_per_prompt"], 4)
+    return out
+
+
 def source_hash(kernel):
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
@@ -622,6 +654,7 @@ def main():
     copy_gbs = measured_copy_gbs()
     result["roofline"]["measured_copy_gbs"] = copy_gbs
     result["roofline"]["frac_of_measured_copy"] = round(achieved / copy_gbs, 4)
+    result["kv_memory"] = kv_memory(w, db)
     if logical != dbytes:  # shared prefixes: also the per-sequence (logical) figure
         result["logical_bytes_per_launch"] = logical
         result["logical_gb_per_s"] = round(logical / (dec_ms * 1e-3) / 1e9, 2)
