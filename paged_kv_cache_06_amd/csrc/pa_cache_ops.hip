@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int64_t j = base + i * 256;
-    if (j < vec_per_block) d[j] = tmp[i];
+    if (j < vec_per_block) stream_store16(d + j, tmp[i]);
   }
 }
 

@@ -95,8 +95,7 @@ __device__ __forceinline__ void write_token_chunk(const CacheWriteArgs<E>& w, in
   const int64_t head_base = (b * w.hkv + h) * static_cast<int64_t>(w.head_dim) * kBlock;
 
   const uint4 kv = *reinterpret_cast<const uint4*>(w.key + src);
-  *reinterpret_cast<uint4*>(w.k_cache + head_base + (static_cast<int64_t>(c) * kBlock + r) * X) =
-      kv;
+  stream_store16(w.k_cache + head_base + (static_cast<int64_t>(c) * kBlock + r) * X, kv);
 
   union {
     uint4 v;
@@ -105,7 +104,7 @@ __device__ __forceinline__ void write_token_chunk(const CacheWriteArgs<E>& w, in
   vv.v = *reinterpret_cast<const uint4*>(w.value + src);
   E* vdst = w.v_cache + head_base + static_cast<int64_t>(c) * X * kBlock + r;
 #pragma unroll
-  for (int i = 0; i < X; ++i) vdst[i * kBlock] = vv.e[i];
+  for (int i = 0; i < X; ++i) stream_store(vdst + i * kBlock, vv.e[i]);
 }
 
 template <typename E>
@@ -166,12 +165,11 @@ __device__ __forceinline__ void CacheWriteI8Args<Tag>::write(int64_t gid) const 
   uint32_t kw[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < 16; ++e) kw[e / 4] |= code(Tag::to_f32(key[src + e]), ks[e]) << (8 * (e % 4));
-  *reinterpret_cast<uint4*>(k_cache + slab + ((c % 4) * 16 + r) * 16) =
-      make_uint4(kw[0], kw[1], kw[2], kw[3]);
+  stream_store16(k_cache + slab + ((c % 4) * 16 + r) * 16, make_uint4(kw[0], kw[1], kw[2], kw[3]));
   int8_t* vdst = v_cache + slab + ((r / 4) * 16) * 16 + (c % 4) * 4 + r % 4;
 #pragma unroll
   for (int e = 0; e < 16; ++e)
-    vdst[e * 16] = static_cast<int8_t>(code(Tag::to_f32(value[src + e]), vs[e]));
+    stream_store(vdst + e * 16, static_cast<int8_t>(code(Tag::to_f32(value[src + e]), vs[e])));
 }
 
 }  // namespace

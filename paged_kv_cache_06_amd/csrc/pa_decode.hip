@@ -243,11 +243,16 @@ __global__ __launch_bounds__(kThreads) void decode_prep_kernel(PlanArgs a, W w) 
 // the one that completes the count reads every partial back and writes the
 // output rows, so no second launch is needed.
 //
-// Partials are written and read with device-scope (relaxed) atomic stores
-// and loads, which go to and come from the device-coherent level instead of
-// the XCD's L2, and every store has completed (s_waitcnt) before the
-// arrival count moves; so no L2-wide write-back or invalidation is needed
-// (device-scope fences, which do both, made the kernel twice as slow).
+// Partials are written with device-scope (relaxed) atomic stores, which
+// write through to the device-coherent level instead of staying in the XCD's
+// L2, and every store has completed (s_waitcnt: the hardware acknowledges a
+// device-scope store once it has reached that level) before the arrival
+// count moves.  The publishing side therefore needs no release fence, whose
+// L2 write-back made the kernel twice as slow when every work-group paid it.
+// The work-group that completes the count takes an agent-scope acquire
+// fence before it reads the partials back (with device-scope loads), so its
+// reads cannot be served from lines cached before the count was observed;
+// that is one fence per split (sequence, head group), not per work-group.
 __device__ __forceinline__ void publish(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -268,6 +273,7 @@ __device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int s, int gh
   }
   __syncthreads();
   if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   for (int e = threadIdx.x; e < nh * D; e += W * kWave) {
     const int h = e / D, d = e % D;
     const size_t row = row0 + h;
