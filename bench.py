@@ -32,13 +32,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 CSRC = os.path.join(ROOT, "paged_kv_cache_06_amd", "csrc")
 # main-pass kernels of a decode call (matrix-core items kernels, VALU path) and
 # the sources each is built from
+_DECODE_SOURCES = ("pa_decode.hip", "pa_decode_common.h", "pa_decode_int8.h", "pa_cache_write.h",
+                   "pa_common.h")
 DECODE_KERNELS = {
-    "decode_items_kernel": ("pa_decode.hip", "pa_decode_common.h"),
-    "decode_generic_kernel": ("pa_decode.hip", "pa_decode_common.h"),
-    "decode_items_i8_kernel": ("pa_decode.hip", "pa_decode_int8.h", "pa_decode_common.h"),
+    "decode_items_kernel": _DECODE_SOURCES,
+    "decode_generic_kernel": _DECODE_SOURCES,
+    "decode_items_i8_kernel": _DECODE_SOURCES,
 }
-# kernels with counter-measured traffic files and the sources each is built from
-KERNEL_SOURCES = dict(DECODE_KERNELS, prefill_kernel=("pa_prefill.hip", "pa_decode_common.h"))
+# kernels with counter-measured traffic files and every source each is built from
+KERNEL_SOURCES = dict(DECODE_KERNELS,
+                      prefill_kernel=("pa_prefill.hip", "pa_decode_common.h", "pa_common.h"))
 
 
 def traffic_file(kernel):
