@@ -61,6 +61,7 @@ struct CacheWriteArgs {
     return padded_tokens(num_tokens, window) * hkv *
            (head_dim * static_cast<int>(sizeof(E)) / 16);
   }
+  template <bool kNT>
   __device__ void write(int64_t gid) const;
 };
 
@@ -77,7 +78,7 @@ CacheWriteArgs<E> cache_write_args(const void* key, const void* value, void* k_c
 // store (token rows of a chunk are contiguous) and X element stores of V
 // (transposed within the block), in the token-fastest order above.  Threads
 // past the end and skipped slots do nothing.
-template <typename E>
+template <typename E, bool kNT>
 __device__ __forceinline__ void write_token_chunk(const CacheWriteArgs<E>& w, int64_t gid) {
   constexpr int X = 16 / sizeof(E);
   const int chunks = w.head_dim / X;
@@ -94,8 +95,18 @@ __device__ __forceinline__ void write_token_chunk(const CacheWriteArgs<E>& w, in
   const int64_t src = th * w.head_dim + static_cast<int64_t>(c) * X;
   const int64_t head_base = (b * w.hkv + h) * static_cast<int64_t>(w.head_dim) * kBlock;
 
+  // kNT: a decode step's tokens (one per sequence) are stored past the
+  // caches; runs of tokens (prefill, chunks) keep the default policy, under
+  // which the L2 merges their 2-byte V stores (non-temporal, a 133K-token
+  // prefill write took 1.9x as long).  The policy is a template parameter,
+  // not a branch: the compiler merges the two sides' stores and drops the
+  // hint.
   const uint4 kv = *reinterpret_cast<const uint4*>(w.key + src);
-  stream_store16(w.k_cache + head_base + (static_cast<int64_t>(c) * kBlock + r) * X, kv);
+  E* kdst = w.k_cache + head_base + (static_cast<int64_t>(c) * kBlock + r) * X;
+  if constexpr (kNT)
+    stream_store16(kdst, kv);
+  else
+    *reinterpret_cast<uint4*>(kdst) = kv;
 
   union {
     uint4 v;
@@ -104,12 +115,18 @@ __device__ __forceinline__ void write_token_chunk(const CacheWriteArgs<E>& w, in
   vv.v = *reinterpret_cast<const uint4*>(w.value + src);
   E* vdst = w.v_cache + head_base + static_cast<int64_t>(c) * X * kBlock + r;
 #pragma unroll
-  for (int i = 0; i < X; ++i) stream_store(vdst + i * kBlock, vv.e[i]);
+  for (int i = 0; i < X; ++i) {
+    if constexpr (kNT)
+      stream_store(vdst + i * kBlock, vv.e[i]);
+    else
+      vdst[i * kBlock] = vv.e[i];
+  }
 }
 
 template <typename E>
+template <bool kNT>
 __device__ __forceinline__ void CacheWriteArgs<E>::write(int64_t gid) const {
-  write_token_chunk<E>(*this, gid);
+  write_token_chunk<E, kNT>(*this, gid);
 }
 
 // ---- INT8 cache ("KV Cache for the intermediate", section "KV Cache
@@ -131,6 +148,7 @@ struct CacheWriteI8Args {
   __host__ __device__ int64_t threads() const {
     return padded_tokens(num_tokens, window) * hkv * (head_dim / 16);
   }
+  template <bool kNT>
   __device__ void write(int64_t gid) const;
 };
 
@@ -140,6 +158,7 @@ struct CacheWriteI8Args {
 // bytes apart (the V layout groups 4 tokens of 4 dimension slices per lane
 // of the decode).
 template <typename Tag>
+template <bool kNT>
 __device__ __forceinline__ void CacheWriteI8Args<Tag>::write(int64_t gid) const {
   const int chunks = head_dim / 16;
   if (gid >= threads()) return;
@@ -165,11 +184,21 @@ __device__ __forceinline__ void CacheWriteI8Args<Tag>::write(int64_t gid) const 
   uint32_t kw[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < 16; ++e) kw[e / 4] |= code(Tag::to_f32(key[src + e]), ks[e]) << (8 * (e % 4));
-  stream_store16(k_cache + slab + ((c % 4) * 16 + r) * 16, make_uint4(kw[0], kw[1], kw[2], kw[3]));
+  const uint4 kcodes = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+  int8_t* kdst = k_cache + slab + ((c % 4) * 16 + r) * 16;
+  if constexpr (kNT)  // as for the 16-bit cache
+    stream_store16(kdst, kcodes);
+  else
+    *reinterpret_cast<uint4*>(kdst) = kcodes;
   int8_t* vdst = v_cache + slab + ((r / 4) * 16) * 16 + (c % 4) * 4 + r % 4;
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
-    stream_store(vdst + e * 16, static_cast<int8_t>(code(Tag::to_f32(value[src + e]), vs[e])));
+  for (int e = 0; e < 16; ++e) {
+    const int8_t v = static_cast<int8_t>(code(Tag::to_f32(value[src + e]), vs[e]));
+    if constexpr (kNT)
+      stream_store(vdst + e * 16, v);
+    else
+      vdst[e * 16] = v;
+  }
 }
 
 }  // namespace

@@ -54,10 +54,10 @@ struct F16T {
 };
 
 // ---- cache stores ----
-// Stores into the caches carry the non-temporal hint: the data is read back
-// by later kernels, through HBM, not by this one.  Left dirty in the XCDs'
-// L2 caches, a decode step's few new tokens slowed the decode kernel that
-// followed by ~4 us on MI355X (100.9 against 96.7 us on the 70B-layer batch).
+// Stores with the non-temporal hint, for cache data that later kernels read
+// back through HBM, not this one: left dirty in the XCDs' L2 caches, a decode
+// step's few new tokens slowed the decode kernel that followed by ~4 us on
+// MI355X (100.9 against 96.7 us on the 70B-layer batch).
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void stream_store16(void* p, uint4 v) {
   __builtin_nontemporal_store(u32x4_nt{v.x, v.y, v.z, v.w}, static_cast<u32x4_nt*>(p));

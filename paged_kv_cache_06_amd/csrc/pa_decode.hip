@@ -227,14 +227,14 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
 // others write the step's new tokens into the cache (both only read their
 // inputs, so they can run side by side); the decode kernels follow on the
 // stream.
-template <typename W>
+template <typename W, bool kNT>
 __global__ __launch_bounds__(kThreads) void decode_prep_kernel(PlanArgs a, W w) {
   __shared__ int wave_tot[kWaves * kPlanVals];
   if (blockIdx.x == 0) {
     plan_body(a, wave_tot);
     return;
   }
-  w.write(static_cast<int64_t>(blockIdx.x - 1) * kThreads + threadIdx.x);
+  w.template write<kNT>(static_cast<int64_t>(blockIdx.x - 1) * kThreads + threadIdx.x);
 }
 
 // Merge of a split sequence's partials by the last of its work-groups to
@@ -683,13 +683,19 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
     PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np, arrivals,
                 fused_merge ? num_seqs * hkv * head_blocks : 0,  // one per (sequence, head group)
                 item_grid, waves};
-    const pa_status ps =
-        write ?  // the step's cache writes ride along with the plan
-            launch_kernel(PA_KERNEL_DECODE_PLAN, decode_prep_kernel<W>,
-                          dim3(static_cast<uint32_t>(1 + (write->threads() + kThreads - 1) / kThreads)),
-                          dim3(kThreads), 0, st, pa, *write)
-              : launch_kernel(PA_KERNEL_DECODE_PLAN, decode_plan_kernel, dim3(1), dim3(kThreads),
-                              0, st, pa);
+    pa_status ps;
+    if (write) {  // the step's cache writes ride along with the plan
+      const dim3 g(static_cast<uint32_t>(1 + (write->threads() + kThreads - 1) / kThreads));
+      // one token per sequence: stored past the caches (see write_token_chunk)
+      ps = write->window == 1
+               ? launch_kernel(PA_KERNEL_DECODE_PLAN, decode_prep_kernel<W, true>, g,
+                               dim3(kThreads), 0, st, pa, *write)
+               : launch_kernel(PA_KERNEL_DECODE_PLAN, decode_prep_kernel<W, false>, g,
+                               dim3(kThreads), 0, st, pa, *write);
+    } else {
+      ps = launch_kernel(PA_KERNEL_DECODE_PLAN, decode_plan_kernel, dim3(1), dim3(kThreads), 0, st,
+                         pa);
+    }
     if (ps != PA_OK) return ps;
   }
   pa_status status = PA_OK;
