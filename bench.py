@@ -504,6 +504,9 @@ def main():
     ap.add_argument("--kv", choices=("native", "int8"), default="native",
                     help="KV cache storage: the workload's dtype, or INT8 codes with "
                          "per-channel scales")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="workloads with shared prompts: decode every sequence's blocks through "
+                         "its own table instead of reading each shared prefix once")
     ap.add_argument("--swap", action="store_true",
                     help="instead of decode steps: move every block of the batch to a pinned "
                          "host pool and back (host-tier swap bandwidth)")
@@ -578,7 +581,8 @@ def main():
     ec = 1 if int8 else w.elem_bytes
     pool_bytes = 2 * (w.num_blocks + 1) * w.num_kv_heads * 16 * w.head_dim * ec
     copies = args.copies or max(1, int(np.ceil(1.5e9 / pool_bytes)))
-    db = runner.DeviceBatch(w, copies=copies, int8=int8)
+    shared = (not args.no_shared and not int8 and bool(np.any(np.asarray(w.prompt_of) >= 0)))
+    db = runner.DeviceBatch(w, copies=copies, int8=int8, shared_prefix=shared)
     db.prefill()
     torch.cuda.synchronize()
     print(f"# setup {time.perf_counter() - t_setup:.1f} s: workload {w.name}, "
@@ -641,7 +645,8 @@ def main():
                    "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
                    "attended_tokens": tokens, "max_context_len": db.max_context_len,
-                   "partition_size": ps, "kv_pool_copies": copies, "parallelism": "none"},
+                   "partition_size": ps, "kv_pool_copies": copies, "parallelism": "none",
+                   "shared_prefix_groups": int(db.shared[2].numel()) if db.shared else 0},
         "pct_of_hbm_peak": round(100 * sbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "kernels_ms_per_step": {k: round(v["ms"] / max(1, v["launches"]), 5)

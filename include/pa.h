@@ -195,6 +195,23 @@ int32_t pa_refcount(const pa_pool* pool, int32_t block);
 int32_t pa_num_free(const pa_pool* pool);
 pa_status pa_pool_stats(const pa_pool* pool, pa_pool_stats_t* out);
 
+/* Groups of sequences that share leading blocks, for
+ * pa_paged_attention_decode_shared (host arrays).  Sequences whose tables
+ * (host, [num_seqs][max_blocks], nblocks[s] entries in use) begin with the
+ * same block form a candidate group, in the order of their first sequence;
+ * its shared length is the longest run of leading entries equal in all its
+ * rows.  Groups of two or more sequences sharing at least min_blocks (>= 1)
+ * entries are written: group g is prefix_seqs[prefix_start[g] ..
+ * prefix_start[g + 1]) in sequence order and shares prefix_blocks[g]
+ * entries.  Capacities: prefix_seqs num_seqs, prefix_start num_seqs / 2 + 1,
+ * prefix_blocks num_seqs / 2.  *num_groups / *num_members receive the
+ * counts.  PA_ERR_INVALID_ARG on NULL pointers or bad sizes,
+ * PA_ERR_HOST_MEMORY if scratch cannot be allocated. */
+pa_status pa_shared_prefix_groups(const int32_t* tables, const int32_t* nblocks, int32_t num_seqs,
+                                  int32_t max_blocks, int32_t min_blocks, int32_t* prefix_seqs,
+                                  int32_t* prefix_start, int32_t* prefix_blocks,
+                                  int32_t* num_groups, int32_t* num_members);
+
 /* Whole blocks whose K and V for all layers fit in `bytes`:
  * bytes / (2 * layers * 16 * num_kv_heads * head_dim * elem_bytes), the KV_size
  * closed form of "KV Cache for the intermediate", section "Precise scientific
@@ -328,6 +345,49 @@ pa_status pa_paged_attention_decode_noalloc(const void* q, const void* k_cache,
                                             int32_t max_blocks_per_seq, int32_t max_context_len,
                                             int32_t partition_size, pa_dtype dtype, void* stream);
 
+/* pa_paged_attention_decode for a batch whose sequences share leading blocks
+ * (the samples of one prompt hold its blocks by reference count: "KV Cache
+ * and PagedAttention: why your LLM server slows down", section "How
+ * PagedAttention fixes this"; "PagedAttention for the professional", results
+ * list: n = 4 samples in about the memory of one).  The same outputs, with
+ * each group's shared positions read from the cache once for all its
+ * sequences (up to floor(16 / (num_q_heads / num_kv_heads)) sequences per
+ * pass) instead of once per sequence.
+ *   prefix_seqs    device int32 [num_members]: the sequences of every group,
+ *                  group by group (pa_shared_prefix_groups computes them)
+ *   prefix_start   device int32 [num_groups + 1]: group g is
+ *                  prefix_seqs[prefix_start[g] .. prefix_start[g + 1])
+ *   prefix_blocks  device int32 [num_groups]: leading table entries every
+ *                  sequence of group g holds in common (the same block ids)
+ *   num_groups, num_members  host counts (num_members <= 2^24)
+ * A sequence belongs to at most one group, and a group lists at most
+ * 32767 * floor(16 / (num_q_heads / num_kv_heads)) sequences.  Of a group,
+ * only whole blocks below every member's length are read as shared; the rest
+ * of each sequence is read through its own table.  Sequence ids out of range
+ * are ignored; tables whose listed entries differ, or group ranges that
+ * overlap, give other outputs than pa_paged_attention_decode, never an
+ * out-of-range access.  The workspace
+ * is sized by pa_decode_shared_workspace_bytes.  Groups are used on the
+ * matrix-core path (bf16/fp16, head_dim 64/128) with at most 16 query heads
+ * per KV head; otherwise the call decodes as pa_paged_attention_decode.
+ * Other arguments and errors as pa_paged_attention_decode. */
+pa_status pa_paged_attention_decode_shared(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* prefix_seqs, const int32_t* prefix_start,
+    const int32_t* prefix_blocks, int32_t num_groups, int32_t num_members, float scale, void* out,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/* Workspace bytes of pa_paged_attention_decode_shared: as
+ * pa_decode_workspace_bytes with one more partial slot per (sequence, query
+ * head), (num_seqs + num_members) * (partitions) more work-list entries, and
+ * 8 bytes per sequence and per group; equal to pa_decode_workspace_bytes when
+ * num_groups is 0.  0 on invalid sizes. */
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t partition_size,
+                                        int32_t num_groups, int32_t num_members);
+
 /* Chunked prefill: sequence s appends a chunk of n_s new tokens whose K/V are
  * already in the cache (pa_reshape_and_cache first, as for decode); query i
  * of the chunk sits at position p = len_s - n_s + i and attends to positions
@@ -404,6 +464,19 @@ pa_status pa_decode_step(const void* key, const void* value, const int64_t* slot
                          int32_t max_blocks_per_seq, int32_t max_context_len,
                          int32_t partition_size, void* workspace, size_t workspace_bytes,
                          pa_dtype dtype, void* stream);
+
+/* pa_decode_step with shared prefixes: the step's token writes, then
+ * pa_paged_attention_decode_shared (arguments as there and as
+ * pa_decode_step), the writes riding in the launch that builds the work list
+ * as in pa_decode_step. */
+pa_status pa_decode_step_shared(
+    const void* key, const void* value, const int64_t* slot_mapping, int32_t num_new_tokens,
+    int32_t num_blocks, const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* prefix_seqs, const int32_t* prefix_start,
+    const int32_t* prefix_blocks, int32_t num_groups, int32_t num_members, float scale, void* out,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, pa_dtype dtype, void* stream);
 
 /* One decode step over an INT8 cache: pa_reshape_and_cache_int8 of the new
  * tokens followed by pa_paged_attention_decode_int8 (arguments as there),

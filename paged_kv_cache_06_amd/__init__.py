@@ -25,6 +25,8 @@ __all__ = [
     "BLOCK_SIZE", "PARTITION_NONE", "PARTITION_AUTO", "PAError", "load", "lib_path",
     "Pool", "BlockManager", "blocks_for_bytes", "reshape_and_cache", "copy_blocks",
     "paged_attention_decode", "paged_attention_decode_noalloc", "DECODE_SCRATCH_BYTES",
+    "shared_prefix_groups", "paged_attention_decode_shared", "decode_step_shared",
+    "decode_shared_workspace_bytes",
     "decode_workspace_bytes", "decode_auto_partition",
     "reshape_and_cache_int8", "paged_attention_decode_int8",
     "swap_blocks", "transfer_blocks", "new_host_kv_cache", "paged_attention_prefill",
@@ -86,6 +88,14 @@ _SIGNATURES = {
     "pa_paged_attention_decode_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_p,
                                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                                    _c_i32, _c_i32, _c_i32, _c_p]),
+    "pa_shared_prefix_groups": (_c_i32, [_P_I32, _P_I32, _c_i32, _c_i32, _c_i32, _P_I32, _P_I32,
+                                         _P_I32, _P_I32, _P_I32]),
+    "pa_decode_shared_workspace_bytes": (_c_sz, [_c_i32] * 7),
+    "pa_paged_attention_decode_shared": (_c_i32, [_c_p] * 8 + [_c_i32, _c_i32, _c_f, _c_p] +
+                                         [_c_i32] * 7 + [_c_p, _c_sz, _c_i32, _c_p]),
+    "pa_decode_step_shared": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32] + [_c_p] * 8 +
+                              [_c_i32, _c_i32, _c_f, _c_p] + [_c_i32] * 7 +
+                              [_c_p, _c_sz, _c_i32, _c_p]),
     "pa_reshape_and_cache_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "pa_paged_attention_decode_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f,
@@ -627,9 +637,115 @@ def decode_step(key, value, slot_mapping, q, k_cache, v_cache, block_tables, con
         _dtype_code(q), _stream(q)), "pa_decode_step")
 
 
-def _workspace(q, s, hq, d, mcl, partition_size, workspace):
+def shared_prefix_groups(rows, nblocks, min_blocks: int = 1):
+    """Groups of sequences whose tables begin with the same blocks
+    (``pa_shared_prefix_groups``): rows int32 [S, MB] and nblocks [S] on the
+    host.  Returns (prefix_seqs, prefix_start, prefix_blocks) int32 arrays."""
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    nb = np.ascontiguousarray(nblocks, dtype=np.int32)
+    s, mb = rows.shape
+    _need(nb.shape == (s,), "nblocks must have one entry per row")
+    seqs = np.zeros(max(s, 1), np.int32)
+    start = np.zeros(s // 2 + 1, np.int32)
+    blocks = np.zeros(max(s // 2, 1), np.int32)
+    ng, nm = _c_i32(), _c_i32()
+    _check(load().pa_shared_prefix_groups(_i32p(rows), _i32p(nb), s, max(mb, 1), int(min_blocks),
+                                          _i32p(seqs), _i32p(start), _i32p(blocks),
+                                          ctypes.byref(ng), ctypes.byref(nm)),
+           "pa_shared_prefix_groups")
+    return seqs[:nm.value].copy(), start[:ng.value + 1].copy(), blocks[:ng.value].copy()
+
+
+def decode_shared_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                  partition_size, num_groups, num_members) -> int:
+    return int(load().pa_decode_shared_workspace_bytes(
+        int(num_seqs), int(num_q_heads), int(head_dim), int(max_context_len),
+        int(partition_size), int(num_groups), int(num_members)))
+
+
+def _shared_args(prefix_seqs, prefix_start, prefix_blocks):
     torch = _torch()
-    need = decode_workspace_bytes(s, hq, d, mcl, partition_size)
+    for t, name in ((prefix_seqs, "prefix_seqs"), (prefix_start, "prefix_start"),
+                    (prefix_blocks, "prefix_blocks")):
+        _need(t.dtype == torch.int32 and t.dim() == 1 and t.is_contiguous(),
+              f"{name} must be a contiguous int32 vector")
+    ng = prefix_blocks.numel()
+    _need(prefix_start.numel() == ng + 1, "prefix_start must have num_groups + 1 entries")
+    return ng, prefix_seqs.numel()
+
+
+def paged_attention_decode_shared(q, k_cache, v_cache, block_tables, context_lens, prefix_seqs,
+                                  prefix_start, prefix_blocks, scale, out, *,
+                                  max_context_len: int | None = None,
+                                  partition_size: int = PARTITION_AUTO, workspace=None) -> None:
+    """paged_attention_decode reading each group's shared leading blocks once
+    (``pa_paged_attention_decode_shared``); prefix_* are device int32 vectors
+    as ``shared_prefix_groups`` gives them."""
+    torch = _torch()
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    s, hq, dq = q.shape
+    _need(dq == d and tuple(out.shape) == (s, hq, d), "q/out must be [S, Hq, D]")
+    _need(q.is_contiguous() and out.is_contiguous(), "q/out must be contiguous")
+    _need(q.dtype == out.dtype == k_cache.dtype, "dtypes differ")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == s and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == s and
+          context_lens.is_contiguous(), "context_lens must be contiguous int32 [S]")
+    ng, nm = _shared_args(prefix_seqs, prefix_start, prefix_blocks)
+    mb = block_tables.shape[1]
+    mcl = mb * BLOCK_SIZE if max_context_len is None else int(max_context_len)
+    ws_ptr, ws_bytes = _workspace(q, s, hq, d, mcl, partition_size, workspace,
+                                  decode_shared_workspace_bytes(s, hq, d, mcl, partition_size, ng,
+                                                                nm))
+    _check(load().pa_paged_attention_decode_shared(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(prefix_seqs), _ptr(prefix_start), _ptr(prefix_blocks), ng, nm, float(scale),
+        _ptr(out), s, hq, hkv, d, mb, mcl, int(partition_size), ws_ptr, ws_bytes, _dtype_code(q),
+        _stream(q)), "pa_paged_attention_decode_shared")
+
+
+def decode_step_shared(key, value, slot_mapping, q, k_cache, v_cache, block_tables, context_lens,
+                       prefix_seqs, prefix_start, prefix_blocks, scale, out, *,
+                       max_context_len: int | None = None, partition_size: int = PARTITION_AUTO,
+                       workspace=None) -> None:
+    """decode_step with shared prefixes (``pa_decode_step_shared``)."""
+    torch = _torch()
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    t = key.shape[0]
+    _need(tuple(key.shape) == (t, hkv, d) and tuple(value.shape) == (t, hkv, d),
+          "key/value must be [T, Hkv, D]")
+    _need(key.is_contiguous() and value.is_contiguous(), "key/value must be contiguous")
+    _need(key.dtype == k_cache.dtype == value.dtype, "dtypes differ")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == t and
+          slot_mapping.is_contiguous(), "slot_mapping must be contiguous int64 [T]")
+    s, hq, dq = q.shape
+    _need(dq == d and tuple(out.shape) == (s, hq, d), "q/out must be [S, Hq, D]")
+    _need(q.is_contiguous() and out.is_contiguous(), "q/out must be contiguous")
+    _need(q.dtype == out.dtype == k_cache.dtype, "dtypes differ")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == s and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == s and
+          context_lens.is_contiguous(), "context_lens must be contiguous int32 [S]")
+    ng, nm = _shared_args(prefix_seqs, prefix_start, prefix_blocks)
+    mb = block_tables.shape[1]
+    mcl = mb * BLOCK_SIZE if max_context_len is None else int(max_context_len)
+    ws_ptr, ws_bytes = _workspace(q, s, hq, d, mcl, partition_size, workspace,
+                                  decode_shared_workspace_bytes(s, hq, d, mcl, partition_size, ng,
+                                                                nm))
+    _check(load().pa_decode_step_shared(
+        _ptr(key), _ptr(value), _ptr(slot_mapping), t, nb, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), _ptr(context_lens), _ptr(prefix_seqs), _ptr(prefix_start),
+        _ptr(prefix_blocks), ng, nm, float(scale), _ptr(out), s, hq, hkv, d, mb, mcl,
+        int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q)),
+        "pa_decode_step_shared")
+
+
+def _workspace(q, s, hq, d, mcl, partition_size, workspace, need=None):
+    torch = _torch()
+    if need is None:
+        need = decode_workspace_bytes(s, hq, d, mcl, partition_size)
     if workspace is None and need > 0:
         key = (q.device, need)
         workspace = _workspaces.get(key)

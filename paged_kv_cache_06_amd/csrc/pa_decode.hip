@@ -81,31 +81,151 @@ __device__ __forceinline__ int size_class(int tokens, int part_size, int waves) 
   return (max_rounds - min(rounds, max_rounds)) * kRoundClasses / max_rounds;
 }
 
-// Entries of the item list: every (sequence, partition), rounded up to a
-// multiple of 32 and padded with end markers.
-__host__ __device__ inline int plan_capacity(int num_seqs, int np_max) {
-  return (num_seqs * np_max + 31) / 32 * 32;
+// Entries of the item list: a private item per (sequence, partition) and a
+// prefix item per (group tile, partition of the shared prefix), rounded up to
+// a multiple of 32 and padded with end markers.
+__host__ __device__ inline int plan_capacity(int num_seqs, int np_max, int num_members = 0) {
+  return ((num_seqs + num_members) * np_max + 31) / 32 * 32;
 }
+
+// Item records (int4):
+//   private item  (s, start, end, slot | nparts << 16): positions [start, end)
+//                 of sequence s; its partial goes to slot `slot` of s's rows,
+//                 and s has nparts partials in all (nparts <= 1: no merge, the
+//                 item writes the output);
+//   prefix item   (-2 - j, start, end, p | t << 16): positions [start, end) of
+//                 group j's shared prefix, for the members of its tile t (the
+//                 listed sequences t * members_per_tile ..), partial slot p
+//                 of each;
+//   end marker    (-1, 0, 0, 0).
+constexpr int kMaxPartitions = 1 << 15;  // slot, nparts and tile fit 15 bits each
+constexpr int kMaxMembers = 1 << 24;     // sequences listed in shared-prefix groups
 
 struct PlanArgs {
   const int32_t* lens;
-  // [num_seqs * np_max] (sequence, partition, length, partition size);
-  // sequence -1 past the end
-  int4* items;
+  int4* items;  // [capacity] records above
   int* split;   // [num_seqs] sequences with more than one partition, then -1
   int* meta;    // [0] items, [1] split sequences
   int num_seqs, max_blocks, part_size, np_max;
+  int max_len;       // positions a sequence may hold (the call's max_context_len)
   int* arrivals;     // per (sequence, head group): partials stored so far (zeroed here)
   int num_arrivals;
   int max_items;     // items the decode grid serves (see plan_partition)
   int waves;         // waves per decode work-group (size classes count rounds of these)
+  // shared prefixes (num_groups == 0: none)
+  const int32_t* pfx_seqs;    // [num_members] sequences of every group, group by group
+  const int32_t* pfx_start;   // [num_groups + 1]
+  const int32_t* pfx_blocks;  // [num_groups] leading table entries the group shares
+  int num_groups, num_members;
+  int members_per_tile;       // floor(16 / query heads per KV head)
+  int* grp_of;                // workspace [num_seqs]: group of each sequence, or -1
+  int* nparts_of;             // workspace [num_seqs]: partials of each sequence
+  int* grp_tokens;            // workspace [num_groups]: shared positions of each group
+  int* grp_leader;            // workspace [num_groups]: a member whose row holds them
+  int capacity;               // entries of the item list
 };
 
+// A length beyond the call's bound is cut to it, so that no sequence has more
+// partitions than its rows of the workspace hold.
 __device__ __forceinline__ int plan_len(const PlanArgs& a, int i) {
-  return min(max(a.lens[i], 0), a.max_blocks * kBlock);
+  return min(max(a.lens[i], 0), a.max_len);
 }
-__device__ __forceinline__ int plan_parts(const PlanArgs& a, int len, int part) {
-  return min((len + part - 1) / part, a.np_max);
+__device__ __forceinline__ int ceil_div(int x, int y) { return (x + y - 1) / y; }
+
+// Members of group j, clamped to the member list.
+__device__ __forceinline__ void group_range(const PlanArgs& a, int j, int* m0, int* m1) {
+  *m0 = min(max(a.pfx_start[j], 0), a.num_members);
+  *m1 = min(max(a.pfx_start[j + 1], *m0), a.num_members);
+}
+
+// Group membership and each group's shared positions: the listed blocks, cut
+// to whole blocks below every member's length, so that every shared position
+// is a written slot of every member (no column needs its own mask there).
+// Members out of range are ignored; a sequence listed twice keeps one group.
+__device__ __forceinline__ void plan_groups(const PlanArgs& a) {
+  for (int i = threadIdx.x; i < a.num_seqs; i += kThreads) a.grp_of[i] = -1;
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.num_groups; j += kThreads) {
+    int m0, m1;
+    group_range(a, j, &m0, &m1);
+    int shortest = a.max_len, valid = 0, leader = -1;
+    for (int m = m0; m < m1; ++m) {
+      const int s = a.pfx_seqs[m];
+      if (s < 0 || s >= a.num_seqs) continue;
+      a.grp_of[s] = j;
+      shortest = min(shortest, plan_len(a, s));
+      if (leader < 0) leader = s;
+      ++valid;
+    }
+    const int listed = min(max(a.pfx_blocks[j], 0), a.max_len / kBlock);
+    a.grp_tokens[j] = valid >= 2 ? min(listed, shortest / kBlock) * kBlock : 0;
+    a.grp_leader[j] = leader;
+  }
+  __syncthreads();
+}
+
+// Positions of sequence i before its private range (its group's shared ones).
+__device__ __forceinline__ int plan_shared(const PlanArgs& a, int i) {
+  if (a.num_groups == 0) return 0;
+  const int j = a.grp_of[i];
+  return j < 0 ? 0 : a.grp_tokens[j];
+}
+
+// Counts of one sequence / one group at partition size `part`: cnt[class] for
+// the last partition of each range, cnt[kFull] for the full ones, cnt[kSplit]
+// for a sequence with more than one partial.
+constexpr int kFull = kClasses, kSplit = kClasses + 1;
+constexpr int kPlanVals = kClasses + 2;
+
+struct SeqPlan {
+  int len, shared, np_pre, np_priv;  // np_priv: private partitions (0: none)
+  bool emits;                        // some private item (an empty sequence has one)
+};
+
+__device__ __forceinline__ SeqPlan seq_plan(const PlanArgs& a, int i, int part) {
+  SeqPlan p;
+  p.len = plan_len(a, i);
+  p.shared = plan_shared(a, i);
+  p.np_pre = ceil_div(p.shared, part);
+  p.np_priv = ceil_div(p.len - p.shared, part);
+  p.emits = p.np_priv > 0 || p.shared == 0;
+  return p;
+}
+
+// Tiles of group j: runs of members_per_tile listed members (at most
+// kMaxPartitions of them; members past those get no shared pass, so their
+// outputs stay unwritten -- the documented limit on a group's size).
+__device__ __forceinline__ int group_tiles(const PlanArgs& a, int j) {
+  int m0, m1;
+  group_range(a, j, &m0, &m1);
+  return a.grp_tokens[j] > 0 ? min(ceil_div(m1 - m0, a.members_per_tile), kMaxPartitions - 1)
+                             : 0;
+}
+
+__device__ __forceinline__ void plan_count(const PlanArgs& a, int part, int i0, int i1, int j0,
+                                           int j1, int* cnt) {
+#pragma unroll
+  for (int c = 0; c < kPlanVals; ++c) cnt[c] = 0;
+  for (int i = i0; i < i1; ++i) {
+    const SeqPlan p = seq_plan(a, i, part);
+    if (!p.emits) continue;
+    const int last = p.np_priv > 0 ? p.len - p.shared - (p.np_priv - 1) * part : 0;
+    const int cls = size_class(last, part, a.waves);
+#pragma unroll
+    for (int c = 0; c < kClasses; ++c) cnt[c] += cls == c;
+    cnt[kFull] += max(p.np_priv - 1, 0);
+    cnt[kSplit] += p.np_pre + p.np_priv > 1;
+  }
+  for (int j = j0; j < j1; ++j) {
+    const int tiles = group_tiles(a, j);
+    if (tiles == 0) continue;
+    const int tokens = a.grp_tokens[j];
+    const int np = ceil_div(tokens, part);
+    const int cls = size_class(tokens - (np - 1) * part, part, a.waves);
+#pragma unroll
+    for (int c = 0; c < kClasses; ++c) cnt[c] += cls == c ? tiles : 0;
+    cnt[kFull] += (np - 1) * tiles;
+  }
 }
 
 // The partition size of a list longer than max_items.  The decode grid is
@@ -113,79 +233,63 @@ __device__ __forceinline__ int plan_parts(const PlanArgs& a, int len, int part) 
 // longest length) would dispatch thousands of work-groups that find only an
 // end marker -- so such a list takes part_size doubled, up to kDoublings
 // times, until it fits, else one partition per sequence.  Larger partitions
-// are fewer, longer items over the same blocks.  Sequences hold at least one
-// item each (an empty one too), and max_items >= num_seqs.
+// are fewer, longer items over the same blocks.
 constexpr int kDoublings = 6;
 
-__device__ __forceinline__ int plan_partition(const PlanArgs& a, int* wave_tot) {
-  const int S = a.num_seqs;
-  const int whole = a.max_blocks * kBlock;
-  const int per = (S + kThreads - 1) / kThreads;
-  const int i0 = threadIdx.x * per;
-  const int i1 = min(S, i0 + per);
+__device__ __forceinline__ int doubled(const PlanArgs& a, int k) {
+  return static_cast<int>(min(static_cast<int64_t>(a.part_size) << k,
+                              static_cast<int64_t>(a.max_blocks) * kBlock));
+}
+
+__device__ __forceinline__ int plan_partition(const PlanArgs& a, int i0, int i1, int j0, int j1,
+                                              int* wave_tot) {
   int cnt[kDoublings + 1];
 #pragma unroll
-  for (int k = 0; k <= kDoublings; ++k) cnt[k] = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int len = plan_len(a, i);
+  for (int k = 0; k <= kDoublings; ++k) {
+    int c[kPlanVals];
+    plan_count(a, doubled(a, k), i0, i1, j0, j1, c);
+    int n = c[kFull];
 #pragma unroll
-    for (int k = 0; k <= kDoublings; ++k) {
-      const int part = static_cast<int>(min(static_cast<int64_t>(a.part_size) << k,
-                                            static_cast<int64_t>(whole)));
-      cnt[k] += max(plan_parts(a, len, part), 1);
-    }
+    for (int q = 0; q < kClasses; ++q) n += c[q];
+    cnt[k] = n;
   }
   int excl[kDoublings + 1], all[kDoublings + 1];
   block_scan<kDoublings + 1>(cnt, excl, all, wave_tot);
   __syncthreads();  // wave_tot is written again by the caller's scan
 #pragma unroll
   for (int k = 0; k <= kDoublings; ++k)
-    if (all[k] <= a.max_items)
-      return static_cast<int>(min(static_cast<int64_t>(a.part_size) << k,
-                                  static_cast<int64_t>(whole)));
-  return whole;
+    if (all[k] <= a.max_items) return doubled(a, k);
+  return a.max_blocks * kBlock;
 }
 
 // The item list, largest first (see the file header).  One work-group; each
-// thread takes a run of consecutive sequences, so one exclusive scan of its
-// per-class counts places every item, in sequence order within a class.
-constexpr int kPlanVals = kClasses + 2;  // classes, full partitions, split sequences
-
-// Per-class item counts of this thread's sequences i0 .. i1-1 at partition
-// size `part`, then full partitions, then split sequences.
-__device__ __forceinline__ void plan_count(const PlanArgs& a, int part, int i0, int i1,
-                                           int* cnt) {
-#pragma unroll
-  for (int c = 0; c < kPlanVals; ++c) cnt[c] = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int len = plan_len(a, i);
-    const int np = plan_parts(a, len, part);
-    const int cls = size_class(np > 0 ? len - (np - 1) * part : 0, part, a.waves);
-#pragma unroll
-    for (int c = 0; c < kClasses; ++c) cnt[c] += cls == c;
-    cnt[kClasses] += max(np - 1, 0);
-    cnt[kClasses + 1] += np > 1;
-  }
-}
-
+// thread takes a run of consecutive sequences and a run of consecutive
+// groups, so one exclusive scan of its per-class counts places every item
+// (sequences before groups within a thread's share of a class).
 __device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
   constexpr int kVals = kPlanVals;
   const int S = a.num_seqs;
-  const int per = (S + kThreads - 1) / kThreads;
-  const int i0 = threadIdx.x * per;
-  const int i1 = min(S, i0 + per);
+  const int per = ceil_div(S, kThreads);
+  const int i0 = min(S, threadIdx.x * per), i1 = min(S, i0 + per);
+  const int gper = ceil_div(a.num_groups, kThreads);
+  const int j0 = min(a.num_groups, static_cast<int>(threadIdx.x) * gper);
+  const int j1 = min(a.num_groups, j0 + gper);
+  if (a.num_groups > 0) plan_groups(a);
   int part = a.part_size;
   int cnt[kVals], excl[kVals], all[kVals];
-  plan_count(a, part, i0, i1, cnt);
+  plan_count(a, part, i0, i1, j0, j1, cnt);
   block_scan<kVals>(cnt, excl, all, wave_tot);
-  if (all[kClasses] + S > a.max_items) {  // the same on every thread
+  int listed = all[kFull];
+#pragma unroll
+  for (int c = 0; c < kClasses; ++c) listed += all[c];
+  if (listed > a.max_items) {  // the same on every thread
     __syncthreads();  // the scan's totals are read before they are rewritten
-    part = plan_partition(a, wave_tot);
-    plan_count(a, part, i0, i1, cnt);
+    part = plan_partition(a, i0, i1, j0, j1, wave_tot);
+    plan_count(a, part, i0, i1, j0, j1, cnt);
     block_scan<kVals>(cnt, excl, all, wave_tot);
   }
   // item positions: full partitions from 0, then classes in order
-  const int num_full = all[kClasses];
+  const int num_full = all[kFull];
   int pos[kClasses];
   int run = num_full;
 #pragma unroll
@@ -193,27 +297,56 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
     pos[c] = run + excl[c];
     run += all[c];
   }
-  int full_pos = excl[kClasses];
-  int split_pos = excl[kClasses + 1];
+  const int total = min(run, a.capacity);
+  // list positions are a permutation of [0, run); those past the capacity
+  // (a listing whose group ranges overlap) are dropped, never written
+  auto put = [&](int at, int4 item) {
+    if (at < a.capacity) a.items[at] = item;
+  };
+  int full_pos = excl[kFull];
+  int split_pos = excl[kSplit];
   for (int i = i0; i < i1; ++i) {
-    const int len = plan_len(a, i);
-    const int np = plan_parts(a, len, part);
-    for (int p = 0; p + 1 < np; ++p) a.items[full_pos++] = make_int4(i, p, len, part);
-    const int cls = size_class(np > 0 ? len - (np - 1) * part : 0, part, a.waves);
+    const SeqPlan p = seq_plan(a, i, part);
+    const int nparts = p.np_pre + p.np_priv;
+    if (a.num_groups > 0) a.nparts_of[i] = nparts;
+    if (!p.emits) continue;
+    for (int q = 0; q + 1 < p.np_priv; ++q) {
+      const int start = p.shared + q * part;
+      put(full_pos++, make_int4(i, start, start + part, (p.np_pre + q) | nparts << 16));
+    }
+    const int q = max(p.np_priv - 1, 0);
+    const int start = p.shared + q * part;
+    const int cls = size_class(p.np_priv > 0 ? p.len - start : 0, part, a.waves);
     int at = 0;
 #pragma unroll
     for (int c = 0; c < kClasses; ++c)
       if (cls == c) at = pos[c]++;
-    a.items[at] = make_int4(i, max(np - 1, 0), len, part);
-    if (np > 1) a.split[split_pos++] = i;
+    put(at, make_int4(i, start, p.len, (p.np_pre + q) | nparts << 16));
+    if (nparts > 1) a.split[split_pos++] = i;
   }
-  const int total = num_full + S;
-  const int cap = plan_capacity(S, a.np_max);
-  for (int u = total + threadIdx.x; u < cap; u += kThreads) a.items[u] = make_int4(-1, 0, 0, 0);
-  for (int i = all[kClasses + 1] + threadIdx.x; i < S; i += kThreads) a.split[i] = -1;
+  for (int j = j0; j < j1; ++j) {
+    const int tiles = group_tiles(a, j);
+    if (tiles == 0) continue;
+    const int tokens = a.grp_tokens[j];
+    const int np = ceil_div(tokens, part);
+    const int cls = size_class(tokens - (np - 1) * part, part, a.waves);
+    for (int t = 0; t < tiles; ++t) {
+      for (int q = 0; q + 1 < np; ++q)
+        put(full_pos++, make_int4(-2 - j, q * part, (q + 1) * part, q | t << 16));
+      int at = 0;
+#pragma unroll
+      for (int c = 0; c < kClasses; ++c)
+        if (cls == c) at = pos[c]++;
+      put(at, make_int4(-2 - j, (np - 1) * part, tokens, (np - 1) | t << 16));
+    }
+  }
+  for (int u = total + threadIdx.x; u < a.capacity; u += kThreads)
+    a.items[u] = make_int4(-1, 0, 0, 0);
+  for (int i = all[kSplit] + threadIdx.x; i < S; i += kThreads) a.split[i] = -1;
   if (threadIdx.x == 0) {
     a.meta[0] = total;
-    a.meta[1] = all[kClasses + 1];
+    a.meta[1] = all[kSplit];
+    a.meta[2] = part;
   }
   for (int i = threadIdx.x; i < a.num_arrivals; i += kThreads) a.arrivals[i] = 0;
 }
@@ -260,20 +393,19 @@ __device__ __forceinline__ float fetch(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Counts this work-group in on (sequence s, head group gh); true for the one
+// that completes the count of nparts.  Called by one thread after every
+// partial store of the work-group has completed.
+__device__ __forceinline__ bool arrive(const DecodeArgs& a, int s, int gh, int nparts) {
+  const int heads = a.hkv * a.head_blocks;
+  return __hip_atomic_fetch_add(a.arrivals + static_cast<size_t>(s) * heads + gh, 1,
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
+}
+
+// The merge itself: rows row0 .. row0 + nh - 1, nparts partials each, all
+// threads of the work-group.
 template <typename Tag, int D, int W>
-__device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int s, int gh, int nparts,
-                                              size_t row0, int nh) {
-  __shared__ int s_last;
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
-  __syncthreads();                 // ... and every thread's
-  if (threadIdx.x == 0) {
-    const int heads = a.hkv * a.head_blocks;
-    s_last = __hip_atomic_fetch_add(a.arrivals + static_cast<size_t>(s) * heads + gh, 1,
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+__device__ __forceinline__ void merge_rows(const DecodeArgs& a, int nparts, size_t row0, int nh) {
   for (int e = threadIdx.x; e < nh * D; e += W * kWave) {
     const int h = e / D, d = e % D;
     const size_t row = row0 + h;
@@ -291,41 +423,60 @@ __device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int s, int gh
   }
 }
 
-// The end of an item: the waves' partials are combined through LDS; a
-// sequence with one partition is normalised and stored, a split one leaves
-// its partial (m, l, acc) for the merge (in-kernel when a.arrivals is set,
-// else by the merge kernel).  vs: INT8 cache only, the V scales of head g,
-// applied to each combined accumulator.
 template <typename Tag, int D, int W>
-__device__ __forceinline__ void finish_item(const DecodeArgs& a, float* comb, int s, int p,
-                                            int len, int part, int g, int h0, int nh, int gh,
+__device__ __forceinline__ void merge_if_last(const DecodeArgs& a, int s, int gh, int nparts,
+                                              size_t row0, int nh) {
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+  __syncthreads();                 // ... and every thread's
+  if (threadIdx.x == 0) s_last = arrive(a, s, gh, nparts);
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  merge_rows<Tag, D, W>(a, nparts, row0, nh);
+}
+
+// Stores one combined (M, L, A) of row `row`, dimension d: the output when
+// the row has one partial, else partial `slot` of the row.
+template <typename Tag, int D>
+__device__ __forceinline__ void store_result(const DecodeArgs& a, size_t row, int d, int slot,
+                                             int nparts, float M, float L, float A) {
+  if (nparts <= 1) {
+    a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
+    return;
+  }
+  const size_t part = row * a.np_max + slot;
+  if (a.arrivals) {  // merged in-kernel: stored where every XCD sees them
+    publish(a.ws_acc + part * D + d, A);
+    if (d == 0) {
+      publish(a.ws_ml + 2 * part, M);
+      publish(a.ws_ml + 2 * part + 1, L);
+    }
+  } else {
+    a.ws_acc[part * D + d] = A;
+    if (d == 0) {
+      a.ws_ml[2 * part] = M;
+      a.ws_ml[2 * part + 1] = L;
+    }
+  }
+}
+
+// The end of an item: the waves' partials are combined through LDS; a
+// sequence with one partial is normalised and stored, a split one leaves
+// its partial (m, l, acc) in slot `slot` for the merge (in-kernel when
+// a.arrivals is set, else by the merge kernel).  vs: INT8 cache only, the V
+// scales of head g, applied to each combined accumulator.
+template <typename Tag, int D, int W>
+__device__ __forceinline__ void finish_item(const DecodeArgs& a, float* comb, int s, int slot,
+                                            int nparts, int g, int h0, int nh, int gh,
                                             const float* vs) {
-  const int nparts = min((len + part - 1) / part, a.np_max);
   const size_t row0 = static_cast<size_t>(s) * a.hq_total + g * a.group + h0;
   for (int e = threadIdx.x; e < nh * D; e += W * kWave) {
     const int h = e / D, d = e % D;
     float M, L, A;
     combine_waves<W>(comb, a.nh_max, D, h, d, M, L, A);
     if (vs) A *= vs[d];
-    const size_t row = row0 + h;
-    if (nparts <= 1) {
-      a.out[row * D + d] = Tag::from_f32(L > 0.f ? A / L : 0.f);
-    } else {
-      const size_t part = row * a.np_max + p;
-      if (a.arrivals) {  // merged in-kernel: stored where every XCD sees them
-        publish(a.ws_acc + part * D + d, A);
-        if (d == 0) {
-          publish(a.ws_ml + 2 * part, M);
-          publish(a.ws_ml + 2 * part + 1, L);
-        }
-      } else {
-        a.ws_acc[part * D + d] = A;
-        if (d == 0) {
-          a.ws_ml[2 * part] = M;
-          a.ws_ml[2 * part + 1] = L;
-        }
-      }
-    }
+    store_result<Tag, D>(a, row0 + h, d, slot, nparts, M, L, A);
   }
   if (nparts > 1 && a.arrivals) merge_if_last<Tag, D, W>(a, s, gh, nparts, row0, nh);
 }
@@ -333,18 +484,16 @@ __device__ __forceinline__ void finish_item(const DecodeArgs& a, float* comb, in
 // Waves of a decode work-group: 4, or 8 for long partitions (item_waves).
 __host__ __device__ constexpr int item_threads(int waves) { return waves * kWave; }
 
-// One work item (sequence it.x, partition it.y of it.w positions, length
-// it.z) for head group
-// gh (KV head x query head block): the waves take the item's blocks
-// round-robin, then finish_item.
+// One private item (sequence it.x, positions [it.y, it.z), partial slot and
+// count in it.w) for head group gh (KV head x query head block): the waves
+// take the item's blocks round-robin, then finish_item.
 template <typename Tag, int D, bool kInt8, int W>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int4 it, int gh, float* comb) {
-  const int s = it.x, p = it.y, len = it.z, part = it.w;
+  const int s = it.x, start = it.y, end = it.z;
+  const int slot = it.w & 0xFFFF, nparts = it.w >> 16;
   const int g = gh / a.head_blocks, h0 = (gh % a.head_blocks) * 16;
   const int nh = min(16, a.group - h0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int start = p * part;
-  const int end = min(len, start + part);
   const int nblk = max(end - start + kBlock - 1, 0) / kBlock;
   const int b_first = start / kBlock + wave;
   const int count = nblk > wave ? (nblk - wave + W - 1) / W : 0;
@@ -362,8 +511,91 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int4 it, int gh
   }
   stage_partials<D, W>(comb, a.nh_max, nh, st);
   __syncthreads();
-  finish_item<Tag, D, W>(a, comb, s, p, len, part, g, h0, nh, gh,
+  finish_item<Tag, D, W>(a, comb, s, slot, nparts, g, h0, nh, gh,
                          kInt8 ? a.v_scale + static_cast<size_t>(g) * D : nullptr);
+}
+
+// One prefix item: positions [it.y, it.z) of the blocks a group of sequences
+// shares ("KV Cache and PagedAttention: why your LLM server slows down",
+// section "How PagedAttention fixes this": one copy of a shared prompt's
+// blocks serves every sample), read once for up to 16 query heads of KV head
+// g drawn from several of the group's sequences -- column c of the 16-wide
+// products is member c / G, head c % G -- instead of once per sequence.
+// Each member's partial goes to slot it.w of its rows and is merged with its
+// private partials like any other.  Only for query-head groups G <= 16.
+template <typename Tag, int D, int W>
+__device__ __forceinline__ void decode_prefix_tile(const DecodeArgs& a, int4 it, int g,
+                                                   float* comb) {
+  __shared__ int s_mem[16], s_np[16], s_last[16];
+  const int j = -2 - it.x, start = it.y, end = it.z;
+  const int slot = it.w & 0xFFFF, tile = it.w >> 16;
+  const int G = a.group, mpt = a.members_per_tile;
+  const int leader = uniform_load(a.grp_leader, j);
+  const int m0 = min(max(uniform_load(a.pfx_start, j), 0), a.num_members);
+  const int m1 = min(max(uniform_load(a.pfx_start, j + 1), m0), a.num_members);
+  const int first = m0 + tile * mpt;
+  const int k = min(max(m1 - first, 0), mpt);
+  if (threadIdx.x < 16) {
+    // a listed sequence out of range, or kept by another group, is left out
+    const int t = threadIdx.x;
+    const int seq = t < k ? a.pfx_seqs[first + t] : -1;
+    const bool ok = seq >= 0 && seq < a.num_seqs && a.grp_of[seq] == j;
+    s_mem[t] = ok ? seq : -1;
+    s_np[t] = ok ? a.nparts_of[seq] : 0;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nblk = (end - start + kBlock - 1) / kBlock;
+  const int b_first = start / kBlock + wave;
+  const int count = nblk > wave ? (nblk - wave + W - 1) / W : 0;
+  const int32_t* trow = a.tables + static_cast<size_t>(leader) * a.max_blocks;
+  const int ids = load_ids<W>(trow, b_first, count);
+  __syncthreads();
+  // B operand of the QK products: lane l holds column l % 16 (member m, head
+  // hh), dims (j * 4 + l / 16) * 8 .. +7 of k-step j; empty columns read 0
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = lane & 15, kg = lane >> 4;
+  const int m = n / G, hh = n % G;
+  const int seq = m < k ? s_mem[m] : -1;
+  uint4 qf[D / 32];
+  if (seq >= 0) {
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        a.q + (static_cast<size_t>(seq) * a.hq_total + g * G + hh) * D + kg * 8);
+#pragma unroll
+    for (int step = 0; step < D / 32; ++step) qf[step] = qrow[step * 4];
+  } else {
+#pragma unroll
+    for (int step = 0; step < D / 32; ++step) qf[step] = make_uint4(0, 0, 0, 0);
+  }
+  WaveState<D> st;
+  st.reset();
+  attend_blocks<Tag, D, W>(a, trow, ids, b_first, count, end, g, qf, st);
+  stage_partials<D, W>(comb, 16, 16, st);
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * D; e += W * kWave) {
+    const int c = e / D, d = e % D;
+    const int mc = c / G;
+    if (mc >= k || s_mem[mc] < 0) continue;
+    float M, L, A;
+    combine_waves<W>(comb, 16, D, c, d, M, L, A);
+    const size_t row = static_cast<size_t>(s_mem[mc]) * a.hq_total + g * G + c % G;
+    store_result<Tag, D>(a, row, d, slot, s_np[mc], M, L, A);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+  __syncthreads();                 // ... and every thread's
+  if (threadIdx.x < 16) {
+    const int t = threadIdx.x;
+    s_last[t] = t < k && s_mem[t] >= 0 && s_np[t] > 1 && arrive(a, s_mem[t], g, s_np[t]);
+  }
+  __syncthreads();
+  bool fenced = false;
+  for (int t = 0; t < k; ++t) {
+    if (!s_last[t]) continue;
+    if (!fenced) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      fenced = true;
+    }
+    merge_rows<Tag, D, W>(a, s_np[t], static_cast<size_t>(s_mem[t]) * a.hq_total + g * G, G);
+  }
 }
 
 // Work-group b serves item b / heads of the plan for head group b % heads
@@ -377,7 +609,11 @@ __global__ __launch_bounds__(item_threads(W), 4) void decode_items_kernel(
   extern __shared__ float comb[];
   const int heads = a.hkv * a.head_blocks;
   const int4 it = items[blockIdx.x / heads];
-  if (it.x < 0) return;
+  if (it.x == -1) return;
+  if (it.x < -1) {
+    if (a.pfx_seqs) decode_prefix_tile<Tag, D, W>(a, it, blockIdx.x % heads, comb);
+    return;
+  }
   decode_item<Tag, D, false, W>(a, it, blockIdx.x % heads, comb);
 }
 
@@ -611,6 +847,7 @@ bool resolve_split(int partition_size, int num_seqs, int hkv, int max_len, Split
   out->part = ps;
   out->np = max(1, (max_len + ps - 1) / ps);
   out->long_context = max_len >= kLongContext;
+  out->max_len = max_len;
   return true;
 }
 
@@ -620,9 +857,9 @@ bool resolve_split(int partition_size, int num_seqs, int hkv, int max_len, Split
 // decodes ~4 % faster; 4 otherwise (mixed batches of short items lose up to
 // 8 % at 8 waves), and 4 whenever 8 waves' partials would not fit the 64 KiB
 // of LDS a work-group gets by default (query-head groups of 16 at D = 128).
-int item_waves(const Split& sp, bool int8, int group, int head_dim) {
+int item_waves(const Split& sp, bool int8, int nh_rows, int head_dim) {
   const bool long_part = sp.part >= (int8 ? 4096 : 2048);
-  const size_t lds = comb_floats(8, std::min(16, group), head_dim) * sizeof(float);
+  const size_t lds = comb_floats(8, nh_rows, head_dim) * sizeof(float);
   return sp.long_context && long_part && lds <= 65536 ? 8 : kItemWaves;
 }
 
@@ -630,18 +867,32 @@ int item_waves(const Split& sp, bool int8, int group, int head_dim) {
 // list] [m, l of every partial] [acc of every partial]; the partial areas
 // exist only when some sequence is split.
 
-Layout workspace_layout(int num_seqs, int hq, int head_dim, const Split& sp) {
+Layout workspace_layout(int num_seqs, int hq, int head_dim, const Split& sp,
+                        const SharedPrefix* sh = nullptr) {
   Layout l;
-  const size_t cap = static_cast<size_t>(plan_capacity(num_seqs, sp.np));
+  const int members = sh ? sh->num_members : 0;
+  // a member of a group has its shared prefix's partitions besides its own,
+  // at most one more than the longest context's
+  l.np_slots = sp.np + (sh ? 1 : 0);
+  const size_t cap = static_cast<size_t>(plan_capacity(num_seqs, l.np_slots, members));
   l.meta = 0;
   l.items = kAlign;
   l.split = l.items + align_up(cap * sizeof(int4));
-  l.ml = l.split + align_up(static_cast<size_t>(num_seqs) * sizeof(int));
+  l.grp_of = l.split + align_up(static_cast<size_t>(num_seqs) * sizeof(int));
+  l.nparts_of = l.grp_tokens = l.grp_leader = l.ml = l.grp_of;
+  if (sh) {
+    const size_t seqs = align_up(static_cast<size_t>(num_seqs) * sizeof(int));
+    const size_t groups = align_up(static_cast<size_t>(sh->num_groups) * sizeof(int));
+    l.nparts_of = l.grp_of + seqs;
+    l.grp_tokens = l.nparts_of + seqs;
+    l.grp_leader = l.grp_tokens + groups;
+    l.ml = l.grp_leader + groups;
+  }
   l.acc = l.ml;
   l.total = l.ml;
   l.arrivals = l.total;
-  if (sp.np > 1) {
-    const size_t parts = static_cast<size_t>(num_seqs) * sp.np * hq;
+  if (l.np_slots > 1) {
+    const size_t parts = static_cast<size_t>(num_seqs) * l.np_slots * hq;
     l.acc = l.ml + align_up(parts * 2 * sizeof(float));
     l.arrivals = l.acc + align_up(parts * head_dim * sizeof(float));
     l.total = l.arrivals + align_up(static_cast<size_t>(num_seqs) * hq * sizeof(int));
@@ -654,23 +905,26 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
                  const int32_t* lens, float scale_log2, void* out, int num_seqs, int hq, int hkv,
                  int head_dim, int max_blocks, const Split& sp, char* ws, bool use_mfma,
                  hipStream_t st, const float* k_scale = nullptr, const float* v_scale = nullptr,
-                 const W* write = nullptr) {
+                 const W* write = nullptr, const SharedPrefix* sh = nullptr) {
   using E = typename Tag::Bits;
   const int group = hq / hkv;
   const int head_blocks = use_mfma ? (group + 15) / 16 : 1;
-  if (static_cast<int64_t>(sp.np) * num_seqs * hq > 0x7fffffff / 2) return PA_ERR_INVALID_ARG;
+  const Layout lay = workspace_layout(num_seqs, hq, head_dim, sp, sh);
+  const int np_slots = lay.np_slots;
+  if (static_cast<int64_t>(np_slots) * num_seqs * hq > 0x7fffffff / 2 ||
+      np_slots >= kMaxPartitions)
+    return PA_ERR_INVALID_ARG;
   // the matrix-core path's grid: items for two per sequence and at least 2048
   // work-groups, or the list's whole capacity when that is smaller; a longer
   // list takes larger partitions (plan_partition).  The merge kernel of the
   // other paths reads partitions of sp.part, so their plan keeps it.
-  const bool fused_merge = use_mfma && sp.np > 1 && kFusedMerge;
-  const int cap = plan_capacity(num_seqs, sp.np);
+  const bool fused_merge = use_mfma && np_slots > 1 && kFusedMerge;
+  const int cap = plan_capacity(num_seqs, np_slots, sh ? sh->num_members : 0);
   const int heads = hkv * head_blocks;
   const int item_grid =
       fused_merge ? std::min(cap, std::max(2 * num_seqs, (2048 + heads - 1) / heads)) : cap;
   const int64_t grid = use_mfma ? static_cast<int64_t>(item_grid) * heads
                                 : static_cast<int64_t>(sp.np) * num_seqs * hq;
-  const Layout lay = workspace_layout(num_seqs, hq, head_dim, sp);
   int* meta = reinterpret_cast<int*>(ws + lay.meta);
   int4* items = reinterpret_cast<int4*>(ws + lay.items);
   int* split = reinterpret_cast<int*>(ws + lay.split);
@@ -678,11 +932,27 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
   float* ws_acc = reinterpret_cast<float*>(ws + lay.acc);
   // the matrix-core kernels merge split sequences themselves (merge_if_last)
   int* arrivals = fused_merge ? reinterpret_cast<int*>(ws + lay.arrivals) : nullptr;
-  const int waves = use_mfma ? item_waves(sp, k_scale != nullptr, group, head_dim) : kWaves;
+  // LDS rows per wave: the head group, or 16 columns of a prefix tile
+  const int nh_rows = sh ? 16 : std::min(16, group);
+  const int waves = use_mfma ? item_waves(sp, k_scale != nullptr, nh_rows, head_dim) : kWaves;
   if (use_mfma || sp.np > 1) {
-    PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, sp.np, arrivals,
+    PlanArgs pa{lens, items, split, meta, num_seqs, max_blocks, sp.part, np_slots,
+                std::min(sp.max_len, max_blocks * kBlock), arrivals,
                 fused_merge ? num_seqs * hkv * head_blocks : 0,  // one per (sequence, head group)
                 item_grid, waves};
+    pa.capacity = cap;
+    if (sh) {
+      pa.pfx_seqs = sh->seqs;
+      pa.pfx_start = sh->start;
+      pa.pfx_blocks = sh->blocks;
+      pa.num_groups = sh->num_groups;
+      pa.num_members = sh->num_members;
+      pa.members_per_tile = 16 / group;
+      pa.grp_of = reinterpret_cast<int*>(ws + lay.grp_of);
+      pa.nparts_of = reinterpret_cast<int*>(ws + lay.nparts_of);
+      pa.grp_tokens = reinterpret_cast<int*>(ws + lay.grp_tokens);
+      pa.grp_leader = reinterpret_cast<int*>(ws + lay.grp_leader);
+    }
     pa_status ps;
     if (write) {  // the step's cache writes ride along with the plan
       const dim3 g(static_cast<uint32_t>(1 + (write->threads() + kThreads - 1) / kThreads));
@@ -706,6 +976,17 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
       a.k_scale = k_scale;
       a.v_scale = v_scale;
       a.arrivals = arrivals;
+      if (sh) {
+        a.pfx_seqs = sh->seqs;
+        a.pfx_start = sh->start;
+        a.grp_of = reinterpret_cast<const int*>(ws + lay.grp_of);
+        a.nparts_of = reinterpret_cast<const int*>(ws + lay.nparts_of);
+        a.grp_leader = reinterpret_cast<const int*>(ws + lay.grp_leader);
+        a.num_members = sh->num_members;
+        a.members_per_tile = 16 / group;
+      }
+      a.np_max = np_slots;
+      a.nh_max = nh_rows;
       const size_t lds = comb_floats(waves, a.nh_max, head_dim) * sizeof(float);
       const dim3 g3(static_cast<uint32_t>(grid)), b3(item_threads(waves));
       const int4* it = items;
@@ -762,6 +1043,22 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return fixed;
 }
 
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t partition_size,
+                                        int32_t num_groups, int32_t num_members) {
+  if (num_groups < 0 || num_members < 0 || num_members > pa::kMaxMembers) return 0;
+  if (num_groups == 0)
+    return pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                     partition_size);
+  pa::Split sp;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  if (!pa::resolve_split(partition_size, num_seqs, 1, max_context_len, &sp)) return 0;
+  pa::SharedPrefix sh;
+  sh.num_groups = num_groups;
+  sh.num_members = num_members;
+  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, sp, &sh).total;
+}
+
 }  // extern "C"
 
 namespace pa {
@@ -788,7 +1085,8 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                       void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
                       int32_t partition_size, void* workspace, size_t workspace_bytes,
-                      pa_dtype dtype, void* stream, const StepWrite& wr) {
+                      pa_dtype dtype, void* stream, const StepWrite& wr,
+                      const SharedPrefix* shared = nullptr) {
   if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0)
@@ -805,7 +1103,13 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   Split sp{kBlock, 1};
   if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp))
     return PA_ERR_INVALID_ARG;
-  const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
+  // shared prefixes are read once on the matrix-core path with query-head
+  // groups of at most 16; elsewhere every sequence reads its own (same results)
+  const SharedPrefix* sh =
+      shared && shared->num_groups > 0 && use_mfma && num_q_heads / num_kv_heads <= 16
+          ? shared
+          : nullptr;
+  const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp, sh).total;
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
     return PA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -828,7 +1132,7 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
       w.window = step_window(wr.num_tokens, num_seqs);
       return launch<BF16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                            num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
-                           ws, use_mfma, st, nullptr, nullptr, fused ? &w : nullptr);
+                           ws, use_mfma, st, nullptr, nullptr, fused ? &w : nullptr, sh);
     }
     case PA_F16: {
       auto w = cache_write_args<uint16_t>(wr.key, wr.value, const_cast<void*>(k_cache),
@@ -837,7 +1141,7 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
       w.window = step_window(wr.num_tokens, num_seqs);
       return launch<F16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
-                          ws, use_mfma, st, nullptr, nullptr, fused ? &w : nullptr);
+                          ws, use_mfma, st, nullptr, nullptr, fused ? &w : nullptr, sh);
     }
     default:
       return launch<F32T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
@@ -1033,6 +1337,74 @@ pa_status pa_paged_attention_decode_noalloc(const void* q, const void* k_cache,
                          max_context_len, partition_size, ws,
                          ws ? static_cast<size_t>(PA_DECODE_SCRATCH_BYTES) : 0, dtype, stream,
                          pa::StepWrite{nullptr, nullptr, nullptr, 0, 0});
+}
+
+namespace {
+
+// Argument checks of the shared-prefix calls; the groups themselves are
+// device data that the plan bounds (members out of range are ignored).
+pa_status shared_args(const int32_t* prefix_seqs, const int32_t* prefix_start,
+                      const int32_t* prefix_blocks, int32_t num_groups, int32_t num_members,
+                      pa::SharedPrefix* out) {
+  if (num_groups < 0 || num_members < 0 || num_members > pa::kMaxMembers)
+    return PA_ERR_INVALID_ARG;
+  if (num_groups > 0 && (!prefix_seqs || !prefix_start || !prefix_blocks))
+    return PA_ERR_INVALID_ARG;
+  out->seqs = prefix_seqs;
+  out->start = prefix_start;
+  out->blocks = prefix_blocks;
+  out->num_groups = num_members > 0 ? num_groups : 0;
+  out->num_members = num_members;
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_paged_attention_decode_shared(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* prefix_seqs, const int32_t* prefix_start,
+    const int32_t* prefix_blocks, int32_t num_groups, int32_t num_members, float scale, void* out,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  pa::SharedPrefix sh;
+  const pa_status st =
+      shared_args(prefix_seqs, prefix_start, prefix_blocks, num_groups, num_members, &sh);
+  if (st != PA_OK) return st;
+  return pa::decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                         num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                         max_context_len, partition_size, workspace, workspace_bytes, dtype,
+                         stream, pa::StepWrite{nullptr, nullptr, nullptr, 0, 0}, &sh);
+}
+
+pa_status pa_decode_step_shared(
+    const void* key, const void* value, const int64_t* slot_mapping, int32_t num_new_tokens,
+    int32_t num_blocks, const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* prefix_seqs, const int32_t* prefix_start,
+    const int32_t* prefix_blocks, int32_t num_groups, int32_t num_members, float scale, void* out,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  using namespace pa;
+  pa::SharedPrefix sh;
+  const pa_status st =
+      shared_args(prefix_seqs, prefix_start, prefix_blocks, num_groups, num_members, &sh);
+  if (st != PA_OK) return st;
+  // the write's own checks, as pa_reshape_and_cache makes them
+  if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_new_tokens < 0 || num_blocks <= 0 || head_dim % (16 / elem_bytes(dtype)) != 0 ||
+      head_dim > 512)
+    return PA_ERR_INVALID_ARG;
+  if (num_new_tokens > 0 && (!key || !value || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  if ((static_cast<int64_t>(num_new_tokens) * num_kv_heads * head_dim + 255) / 256 > 0x7fffffff)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0)  // nothing to attend: only the write
+    return pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_new_tokens,
+                                num_blocks, num_kv_heads, head_dim, dtype, stream);
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, max_context_len,
+                     partition_size, workspace, workspace_bytes, dtype, stream,
+                     StepWrite{key, value, slot_mapping, num_new_tokens, num_blocks}, &sh);
 }
 
 }  // extern "C"

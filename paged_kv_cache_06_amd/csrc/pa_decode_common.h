@@ -117,6 +117,15 @@ struct DecodeArgs {
   const float* k_scale;  // INT8 cache only: [Hkv][D] per-channel scales
   const float* v_scale;
   int* arrivals;         // split sequences merged in-kernel: [S][heads] counters, else null
+  // shared prefixes (pfx_seqs null: none): the caller's member list and
+  // group starts, and the plan's group of each sequence, partial count of
+  // each sequence and a member of each group whose row holds its blocks
+  const int* pfx_seqs;
+  const int* pfx_start;
+  const int* grp_of;
+  const int* nparts_of;
+  const int* grp_leader;
+  int num_members, members_per_tile;
   float scale_log2;
   int num_seqs, hq_total, hkv, group, head_blocks, max_blocks, part_size, np_max;
   int nh_max;  // query heads of the largest head group (<= 16): LDS rows per wave
@@ -385,11 +394,22 @@ struct Split {
   int np;
   bool long_context = false;  // the longest context has >= 16K positions
   int waves = kItemWaves;     // waves per work-group of the matrix-core items kernels
+  int max_len = 0;            // the call's bound on every length
+};
+
+// Shared prefixes of a decode call: groups of sequences whose tables begin
+// with the same blocks (device arrays; none when num_groups is 0).
+struct SharedPrefix {
+  const int32_t* seqs = nullptr;    // [num_members] sequences, group by group
+  const int32_t* start = nullptr;   // [num_groups + 1]
+  const int32_t* blocks = nullptr;  // [num_groups] shared leading table entries
+  int num_groups = 0, num_members = 0;
 };
 
 // Byte offsets of a decode workspace's areas.
 struct Layout {
-  size_t meta, items, split, ml, acc, arrivals, total;
+  size_t meta, items, split, grp_of, nparts_of, grp_tokens, grp_leader, ml, acc, arrivals, total;
+  int np_slots;  // partial slots per (sequence, query head)
 };
 
 inline bool mfma_path(pa_dtype dt, int head_dim) {
@@ -414,6 +434,8 @@ DecodeArgs mfma_args(const void* q, const void* k_cache, const void* v_cache,
   a.k_scale = nullptr;
   a.v_scale = nullptr;
   a.arrivals = nullptr;
+  a.pfx_seqs = a.pfx_start = a.grp_of = a.nparts_of = a.grp_leader = nullptr;
+  a.num_members = a.members_per_tile = 0;
   a.scale_log2 = scale_log2;
   a.num_seqs = num_seqs;
   a.hq_total = hq;

@@ -402,4 +402,74 @@ int64_t pa_blocks_for_bytes(int64_t bytes, int32_t layers, int32_t kv_heads, int
   return bytes / per_block;
 }
 
+pa_status pa_shared_prefix_groups(const int32_t* tables, const int32_t* nblocks, int32_t num_seqs,
+                                  int32_t max_blocks, int32_t min_blocks, int32_t* prefix_seqs,
+                                  int32_t* prefix_start, int32_t* prefix_blocks,
+                                  int32_t* num_groups, int32_t* num_members) {
+  if (num_seqs < 0 || max_blocks <= 0 || min_blocks < 1 || !num_groups || !num_members)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!tables || !nblocks || !prefix_seqs || !prefix_start || !prefix_blocks))
+    return PA_ERR_INVALID_ARG;
+  *num_groups = 0;
+  *num_members = 0;
+  // sequences by their first block, in sequence order
+  std::unordered_map<int32_t, int32_t> leader_of;  // first block -> first sequence holding it
+  int32_t* next = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * (num_seqs > 0 ? num_seqs : 1)));
+  int32_t* last = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * (num_seqs > 0 ? num_seqs : 1)));
+  if (!next || !last) {
+    std::free(next);
+    std::free(last);
+    return PA_ERR_HOST_MEMORY;
+  }
+  try {
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      next[s] = -1;
+      last[s] = s;
+      const int32_t nb = nblocks[s];
+      if (nb < 1 || nb > max_blocks) continue;
+      const int32_t first = tables[static_cast<int64_t>(s) * max_blocks];
+      auto it = leader_of.find(first);
+      if (it == leader_of.end()) {
+        leader_of.emplace(first, s);
+      } else {
+        const int32_t l = it->second;
+        next[last[l]] = s;  // append to the leader's chain
+        last[l] = s;
+      }
+    }
+  } catch (...) {
+    std::free(next);
+    std::free(last);
+    return PA_ERR_HOST_MEMORY;
+  }
+  int32_t g = 0, m = 0;
+  for (int32_t l = 0; l < num_seqs; ++l) {
+    const int32_t nb = nblocks[l];
+    if (nb < 1 || nb > max_blocks || next[l] < 0) continue;
+    const int32_t* lead = tables + static_cast<int64_t>(l) * max_blocks;
+    // is l the head of its chain (the first sequence with its first block)?
+    auto it = leader_of.find(lead[0]);
+    if (it == leader_of.end() || it->second != l) continue;
+    int32_t shared = nb;
+    for (int32_t s = next[l]; s >= 0; s = next[s]) {
+      const int32_t* row = tables + static_cast<int64_t>(s) * max_blocks;
+      const int32_t lim = shared < nblocks[s] ? shared : nblocks[s];
+      int32_t k = 0;
+      while (k < lim && row[k] == lead[k]) ++k;
+      shared = k;
+    }
+    if (shared < min_blocks) continue;
+    prefix_start[g] = m;
+    prefix_blocks[g] = shared;
+    for (int32_t s = l; s >= 0; s = next[s]) prefix_seqs[m++] = s;
+    ++g;
+  }
+  prefix_start[g] = m;
+  std::free(next);
+  std::free(last);
+  *num_groups = g;
+  *num_members = m;
+  return PA_OK;
+}
+
 }  // extern "C"

@@ -20,9 +20,10 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import (BLOCK_SIZE, PARTITION_AUTO, BlockManager, Pool, copy_blocks, decode_step,
-               decode_step_int8, new_kv_cache,
+               decode_step_int8, decode_step_shared, new_kv_cache,
                new_kv_cache_int8, paged_attention_decode, paged_attention_decode_int8,
-               paged_attention_prefill, reshape_and_cache, reshape_and_cache_int8)
+               paged_attention_decode_shared, paged_attention_prefill, reshape_and_cache,
+               reshape_and_cache_int8, shared_prefix_groups)
 
 _TORCH_DTYPE = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
 NAN_FILL = float("nan")
@@ -131,11 +132,13 @@ class DeviceBatch:
     shows up in the output.  ``copies`` > 1 keeps that many independent caches
     (same tables) for benchmarks that must not hit in the last-level cache.
     ``int8`` keeps an INT8 cache with the workload's per-channel scales (its
-    poison block and unwritten slots hold code 127).
+    poison block and unwritten slots hold code 127).  ``shared_prefix``
+    decodes through the shared-prefix calls, with the groups of sequences
+    whose tables begin with the same blocks after the step.
     """
 
     def __init__(self, w, device="cuda", copies: int = 1, fill: float | None = NAN_FILL,
-                 prefix_cache: bool = False, int8: bool = False):
+                 prefix_cache: bool = False, int8: bool = False, shared_prefix: bool = False):
         import torch
 
         self.w = w
@@ -160,6 +163,10 @@ class DeviceBatch:
         self.q = self._dev(w.q)
         self.out = torch.empty(w.q.shape, dtype=self.torch_dtype, device=device)
         self.dev_phases = [self._dev_phase(ph) for ph in self.phases]
+        self.shared = None
+        if shared_prefix:
+            seqs, start, blocks = shared_prefix_groups(self.bm.rows, self.bm.nblocks)
+            self.shared = tuple(torch.from_numpy(x).to(device) for x in (seqs, start, blocks))
 
     def _dev(self, bits):
         return to_device(bits, self.w.dtype, self.device)
@@ -207,6 +214,12 @@ class DeviceBatch:
                              self.v_scale, self.tables, self.context_lens, self.w.scale, o,
                              max_context_len=self.max_context_len, partition_size=partition_size)
             return
+        if self.shared is not None:
+            decode_step_shared(ph["key"], ph["value"], ph["slots"], self.q, kc, vc, self.tables,
+                               self.context_lens, *self.shared, self.w.scale, o,
+                               max_context_len=self.max_context_len,
+                               partition_size=partition_size)
+            return
         decode_step(ph["key"], ph["value"], ph["slots"], self.q, kc, vc, self.tables,
                     self.context_lens, self.w.scale, o, max_context_len=self.max_context_len,
                     partition_size=partition_size)
@@ -219,6 +232,13 @@ class DeviceBatch:
                                         self.out if out is None else out,
                                         max_context_len=self.max_context_len,
                                         partition_size=partition_size)
+            return
+        if self.shared is not None:
+            paged_attention_decode_shared(self.q, kc, vc, self.tables, self.context_lens,
+                                          *self.shared, self.w.scale,
+                                          self.out if out is None else out,
+                                          max_context_len=self.max_context_len,
+                                          partition_size=partition_size)
             return
         paged_attention_decode(self.q, kc, vc, self.tables, self.context_lens, self.w.scale,
                                self.out if out is None else out,

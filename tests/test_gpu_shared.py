@@ -1,0 +1,153 @@
+"""pa_paged_attention_decode_shared / pa_decode_step_shared on the GPU.
+
+Reading a shared prefix once for all its sequences must not change any
+output: every output is compared with the oracle's decode (which knows
+nothing of sharing: each sequence attends through its own table), and with
+the decode that reads every sequence's blocks itself (the two differ only in
+summation order: within one unit in the last place, or 1e-5 near zero).
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_06_amd as pa
+import workloads
+from oracle import step
+from oracle.numerics import to_f64
+from paged_kv_cache_06_amd import runner
+from tests.helpers import NAN_BITS, assert_close, bits_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _close_to_plain(got_bits, plain_bits, dtype):
+    ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -10
+    a, b = to_f64(got_bits, dtype), to_f64(plain_bits, dtype)
+    ratio = np.abs(a - b) / (ulp * np.abs(b) + 1e-5)
+    assert ratio.max() <= 1.0, f"{ratio.max():.2f} ulp from the unshared decode"
+
+
+def _both(w, partition_size):
+    ref = step.run(w, NAN_BITS[w.dtype])[3]
+    shared = runner.DeviceBatch(w, shared_prefix=True)
+    plain = runner.DeviceBatch(w)
+    for db in (shared, plain):
+        db.prefill()
+        db.step(partition_size=partition_size)
+    torch.cuda.synchronize()
+    return shared, plain, ref
+
+
+SHAPES = [
+    # (hq, hkv, d, dtype): G = hq / hkv query heads per KV head
+    (8, 2, 128, "bf16"),    # G = 4: 4 samples per pass
+    (16, 2, 128, "f16"),    # G = 8: 2 per pass
+    (4, 4, 64, "bf16"),     # G = 1: 16 per pass
+    (4, 2, 64, "f16"),      # G = 2
+    (12, 4, 128, "bf16"),   # G = 3: 5 per pass, 15 columns
+    (32, 2, 64, "bf16"),    # G = 16: 1 per pass
+    (32, 1, 128, "f16"),    # G = 32: shared prefixes not used (plain decode)
+]
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", SHAPES)
+@pytest.mark.parametrize("partition_size", [pa.PARTITION_AUTO, pa.PARTITION_NONE, 16, 64, 512])
+def test_small_groups_against_oracle(hq, hkv, d, dtype, partition_size):
+    print(f"[gpu] shared decode {hq}/{hkv} d={d} {dtype} P={partition_size}", flush=True)
+    # prompts of 21 (partial block), 32 (block-aligned), 45 and 300 positions;
+    # 3, 5, 2 and 6 samples with 1..70 private positions; two unshared rows
+    prompt_of = [0, 0, 0, -1, 1, 1, 1, 1, 1, 2, 2, 3, 3, 3, 3, 3, 3, -1]
+    lens = [1, 5, 20, 2, 3, 40, 7, 9, 70, 1, 33, 2, 17, 16, 1, 64, 5, 100]
+    w = workloads.make_custom(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=hq + d,
+                              prompt_lens=[21, 32, 45, 300], prompt_of=prompt_of)
+    shared, plain, ref = _both(w, partition_size)
+    ng = shared.shared[2].numel()
+    assert ng == 4  # every prompt with two or more samples forms a group
+    assert_close(shared.out_bits(), ref, dtype, f"shared {hq}/{hkv} P={partition_size}")
+    _close_to_plain(shared.out_bits(), plain.out_bits(), dtype)
+
+
+def test_long_shared_prompt_splits_into_partitions():
+    # a 2050-position prompt (two 1024-position shared partitions and a partial
+    # block each sample copies), 4 samples, with a split private part as well
+    print("[gpu] shared decode, long prompt", flush=True)
+    w = workloads.make_custom([1, 300, 1500, 17], hq=32, hkv=8, d=128, dtype="bf16", seed=41,
+                              prompt_lens=[2050], prompt_of=[0, 0, 0, 0])
+    for part in (pa.PARTITION_AUTO, 256, 1024):
+        shared, plain, ref = _both(w, part)
+        assert_close(shared.out_bits(), ref, "bf16", f"long prompt P={part}")
+        _close_to_plain(shared.out_bits(), plain.out_bits(), "bf16")
+
+
+def _decode_with(db, seqs, start, blocks, out):
+    kc, vc = db.caches[0]
+    dev = [torch.tensor(x, dtype=torch.int32, device="cuda") for x in (seqs, start, blocks)]
+    pa.paged_attention_decode_shared(db.q, kc, vc, db.tables, db.context_lens, *dev, db.w.scale,
+                                     out, max_context_len=db.max_context_len)
+    torch.cuda.synchronize()
+
+
+def test_malformed_groups_are_bounded():
+    # ids out of range are left out; a group range that overlaps another only
+    # reaches the sequences it keeps; listed blocks beyond the members'
+    # lengths are cut to their whole blocks; a decreasing start leaves a group
+    # empty.  Where the listing stays true to the tables, every output
+    # matches the oracle.
+    print("[gpu] shared decode, malformed groups", flush=True)
+    w = workloads.make_custom([3, 5, 20, 9, 40, 7], hq=8, hkv=2, d=128, dtype="bf16", seed=7,
+                              prompt_lens=[64, 80], prompt_of=[0, 0, 0, 1, 1, 1])
+    db = runner.DeviceBatch(w)
+    db.prefill()
+    db.step()
+    ref = step.run(w, NAN_BITS["bf16"])[3]
+    cases = [
+        ([0, 1, 999, -5, 2, 3, 4, 5], [0, 5, 8], [4, 5]),       # bad ids in group 0
+        ([0, 1, 2, 3, 4, 5], [0, 3, 1, 3, 6], [4, 9, 4, 5]),     # group 2 = [1, 3) overlaps 0
+        ([0, 1, 2, 3, 4, 5], [0, 3, 6], [400, 9]),               # more blocks than the rows hold
+        ([3, 4, 5, 0, 1, 2], [3, 6, 0], [4, 5]),                 # decreasing start: group 1 empty
+    ]
+    for seqs, start, blocks in cases:
+        out = torch.full_like(db.out, float("nan"))
+        _decode_with(db, seqs, start, blocks, out)
+        assert_close(bits_of(out), ref, "bf16", f"groups {seqs} {start} {blocks}")
+    # a listing untrue to the tables (two prompts in one group) gives other
+    # outputs, but every access stays in range and the call completes
+    out = torch.full_like(db.out, float("nan"))
+    _decode_with(db, [0, 1, 2, 3, 4, 5], [0, 6], [5], out)
+
+
+def test_fused_shared_step_equals_write_then_decode():
+    print("[gpu] shared step fused vs unfused", flush=True)
+    w = workloads.make_custom([1, 5, 20, 2, 3, 40, 7, 9], hq=8, hkv=2, d=128, dtype="bf16",
+                              seed=31, prompt_lens=[21, 32, 45],
+                              prompt_of=[0, 0, 0, 1, 1, 1, 2, 2])
+    a = runner.DeviceBatch(w, shared_prefix=True)
+    b = runner.DeviceBatch(w, shared_prefix=True)
+    for db, fused in ((a, True), (b, False)):
+        db.prefill()
+        db.step(fused=fused)
+    torch.cuda.synchronize()
+    for x, y in zip(a.caches[0], b.caches[0]):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert np.array_equal(a.out_bits(), b.out_bits())
+
+
+@pytest.mark.parametrize("config", [4, "4b"])
+def test_full_size_shared_prefix_workloads_every_output(config):
+    print(f"[gpu] full-size workload {config} through the shared-prefix decode", flush=True)
+    w = workloads.make(config)
+    shared = runner.DeviceBatch(w, shared_prefix=True)
+    shared.prefill()
+    shared.step()
+    torch.cuda.synchronize()
+    assert shared.shared[2].numel() == (64 if config == 4 else 1)
+    ref = step.run(w, NAN_BITS["bf16"])[3]
+    info = assert_close(shared.out_bits(), ref, "bf16", f"workload {config}, shared")
+    print(f"  {info}", flush=True)
+    plain = runner.DeviceBatch(w)
+    plain.prefill()
+    plain.step()
+    _close_to_plain(shared.out_bits(), plain.out_bits(), "bf16")
+    again = torch.empty_like(shared.out)
+    shared.decode(out=again)
+    assert np.array_equal(bits_of(again), shared.out_bits())  # run to run
