@@ -620,6 +620,8 @@ def main():
     ps = args.partition if args.partition != -1 else pa.decode_auto_partition(
         w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, db.max_context_len,
         3 if int8 else {"f32": 0, "f16": 1, "bf16": 2}[w.dtype])
+    if db.shared is not None and args.partition == -1 and 0 < ps < db.max_context_len:
+        ps *= 2  # the shared-prefix decode doubles the automatic partition
     if int8:
         main_kernel = "decode_items_i8_kernel"
     elif w.dtype != "f32" and w.head_dim in (64, 128):

@@ -1052,6 +1052,7 @@ size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, i
                                      partition_size);
   pa::Split sp;
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  // the smallest automatic partition needs the most slots: size for it
   if (!pa::resolve_split(partition_size, num_seqs, 1, max_context_len, &sp)) return 0;
   pa::SharedPrefix sh;
   sh.num_groups = num_groups;
@@ -1109,6 +1110,13 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
       shared && shared->num_groups > 0 && use_mfma && num_q_heads / num_kv_heads <= 16
           ? shared
           : nullptr;
+  // with shared prefixes the automatic partition doubles: a prefix item
+  // serves several sequences, and fewer, longer ones (fewer partials to merge
+  // per sequence) measured faster -- 64 prompts x 4 samples of 2048 shared
+  // positions: 145 us at 2048 against 161 us at 1024 (MI355X)
+  if (sh && partition_size == PA_PARTITION_AUTO && sp.np > 1 &&
+      !resolve_split(2 * sp.part, num_seqs, num_kv_heads, max_context_len, &sp))
+    return PA_ERR_INVALID_ARG;
   const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp, sh).total;
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
     return PA_ERR_WORKSPACE;
