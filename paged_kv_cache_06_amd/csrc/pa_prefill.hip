@@ -16,8 +16,9 @@
 //   acc^T[D x 32 cols] += V^T . P^T             (MFMA 32x32x16, per block)
 // A work-group (4 waves, one tile each) walks the rounds its tiles need
 // through an LDS ring that each round enters once, software-pipelined so
-// that one round's QK products run beside the previous round's softmax; the
-// work-groups with the most rounds are handed out first.
+// that one round's QK products run beside the previous round's softmax.  The
+// longest sequences are handed out first, the work-groups of one sequence
+// together, so that those sharing its K/V share one XCD's L2.
 #include "pa_decode_common.h"
 
 namespace pa {
@@ -36,7 +37,7 @@ struct PrefillArgs {
   int cols_heads;           // query heads per tile: min(G, 32)
   int qpw;                  // queries per wave: 32 / cols_heads
   int groups_max;           // query runs of the longest chunk: ceil(max_chunk / qpw)
-  int largest_first;        // order work-groups by their work (num_seqs <= kOrderMaxSeqs)
+  int longest_first;        // longest sequence first (num_seqs <= kOrderMaxSeqs)
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
@@ -186,18 +187,23 @@ __device__ __forceinline__ uint4 pack8(const float* p) {
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-// ---- largest-first work-group order ----
+// ---- work-group order: longest sequence first, its groups together ----
 //
-// A work-group of the 32-column kernel covers query group rg (queries
-// rg*pw .. rg*pw + pw - 1 of its chunk, pw = 4 * qpw) of sequence s for one
-// KV head, and walks 32-position rounds up to its last query's position,
-// c_s + min(n_s, (rg + 1) * pw) - 1 (c_s = tokens before the chunk, n_s = its
-// length).  That count W(s, rg) grows with rg, so the groups of s with W >= V
-// are the top ones and their number has a closed form; summed over the
-// sequences and searched over V, it gives the pair of any rank in the order
-// of decreasing W (ties by sequence, then group).  Work-groups are
-// dispatched in index order, so handing out the longest first keeps the
-// long ones from starting last.
+// A work-group covers query group rg (queries rg*pw .. rg*pw + pw - 1 of its
+// chunk, pw = 4 * qpw) of sequence s for one KV head, and walks 32-position
+// rounds up to its last query's position.  Its K/V are a prefix of the
+// sequence's, shared by every group of (s, head).  Work-groups are dispatched
+// in index order, round-robin over the XCDs, and consecutive indices differ in
+// the KV head first; so an order that keeps the groups of one sequence
+// together keeps the work-groups of one (sequence, head) on one XCD at the
+// same time, where they walk the same blocks and all but the first read hit
+// that XCD's L2 (measured: HBM reads 1.55x -> 1.0x the bytes read once).
+// Sequences go by the rounds of their last group, W(s) = (c_s + n_s - 1)/32 + 1
+// (c_s = tokens before the chunk, n_s = its length), longest first, ties by
+// index; within a sequence the top (longest) group first.  The number of
+// groups in sequences with W >= V has a closed form per sequence; searched
+// over V it gives the pair of any rank.  Longest first keeps the long
+// work-groups from starting last.
 constexpr int kOrderMaxSeqs = 256;   // sequences one wave ranks (4 per lane)
 
 __device__ __forceinline__ int wave_sum(int x) {
@@ -212,43 +218,35 @@ __device__ __forceinline__ int wave_max(int x) {
   return x;
 }
 
-// groups rg < G of one sequence whose round count is at least V (V >= 1)
-__device__ __forceinline__ int groups_at_least(int c, int n, int G, int pw, int V) {
-  const int t = 32 * (V - 1) - c + 1;  // the group must reach min(n, (rg+1)pw) >= t
-  if (t <= 1) return G;
-  if (n < t) return 0;
-  return max(0, G - max(0, (t + pw - 1) / pw - 1));
-}
-
 // Pair (s, rg) of rank q, or false if q is past the last non-empty group.
 // Wave-uniform; every wave of the work-group computes the same answer.
-__device__ bool largest_first(const PrefillArgs& a, int q, int R, int pw, int& s_out,
+__device__ bool longest_first(const PrefillArgs& a, int q, int R, int pw, int& s_out,
                               int& rg_out) {
   const int lane = threadIdx.x & (kWave - 1);
   constexpr int kPer = kOrderMaxSeqs / kWave;
-  int c[kPer], n[kPer], G[kPer];
+  int G[kPer], W[kPer];
   int total = 0, vmax = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int s = lane + k * kWave;
-    c[k] = 0, n[k] = 0, G[k] = 0;
+    G[k] = 0, W[k] = 0;
     if (s < a.num_seqs) {
       const int q0 = a.qstart[s], q1 = a.qstart[s + 1];
       const int len = min(max(a.lens[s], q1 - q0), a.max_blocks * kBlock);
-      n[k] = max(0, min(q1 - q0, len));
-      c[k] = len - n[k];
-      G[k] = min((n[k] + pw - 1) / pw, R);
-      if (G[k] > 0) vmax = max(vmax, (c[k] + n[k] - 1) / 32 + 1);
+      const int n = max(0, min(q1 - q0, len));
+      G[k] = min((n + pw - 1) / pw, R);
+      if (G[k] > 0) W[k] = (len - 1) / 32 + 1;  // the last query sits at len - 1
+      vmax = max(vmax, W[k]);
     }
     total += G[k];
   }
   total = wave_sum(total);
   if (q >= total) return false;
   vmax = wave_max(vmax);
-  auto count = [&](int V) {
+  auto count = [&](int V) {  // groups in sequences with W >= V
     int x = 0;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) x += groups_at_least(c[k], n[k], G[k], pw, V);
+    for (int k = 0; k < kPer; ++k) x += W[k] >= V ? G[k] : 0;
     return wave_sum(x);
   };
   int lo = 1, hi = vmax + 1;  // count(lo) > q >= count(hi)
@@ -259,11 +257,10 @@ __device__ bool largest_first(const PrefillArgs& a, int q, int R, int pw, int& s
     else
       hi = mid;
   }
-  int r = q - count(lo + 1);  // rank among the pairs of exactly lo rounds
+  int r = q - count(lo + 1);  // rank among the groups of sequences with W == lo
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int at = groups_at_least(c[k], n[k], G[k], pw, lo);
-    const int e = at - groups_at_least(c[k], n[k], G[k], pw, lo + 1);
+    const int e = W[k] == lo ? G[k] : 0;
     int incl = e;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -274,7 +271,7 @@ __device__ bool largest_first(const PrefillArgs& a, int q, int R, int pw, int& s
     if (hit != 0) {
       const int f = static_cast<int>(__builtin_ctzll(hit));
       s_out = f + k * kWave;
-      rg_out = __builtin_amdgcn_readlane(G[k] - at + r - (incl - e), f);
+      rg_out = __builtin_amdgcn_readlane(G[k] - 1 - (r - (incl - e)), f);
       return true;
     }
     r -= __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -305,13 +302,13 @@ __global__ __launch_bounds__(kPrefillWaves * kWave, 2) void prefill_kernel(Prefi
   const int g = (u % inner) / a.head_blocks;
   const int hb = u % a.head_blocks;
   int s, rg;
-  if (a.largest_first) {
-    if (!largest_first(a, u / inner, run_groups, kPrefillWaves * a.qpw, s, rg)) return;
+  if (a.longest_first) {
+    if (!longest_first(a, u / inner, run_groups, kPrefillWaves * a.qpw, s, rg)) return;
     s = __builtin_amdgcn_readfirstlane(s);
     rg = __builtin_amdgcn_readfirstlane(rg);
-  } else {  // later query groups (more positions) first
-    rg = run_groups - 1 - u / (a.num_seqs * inner);
-    s = (u / inner) % a.num_seqs;
+  } else {  // sequences in index order, each one's groups together, top first
+    s = (u / inner) / run_groups;
+    rg = run_groups - 1 - (u / inner) % run_groups;
   }
   const int q0 = uniform_load(a.qstart, s), q1 = uniform_load(a.qstart, s + 1);
   const int len = min(max(uniform_load(a.lens, s), q1 - q0), a.max_blocks * kBlock);
@@ -544,7 +541,7 @@ pa_status pa_paged_attention_prefill(const void* q, const void* k_cache, const v
   a.cols_heads = std::min(a.group, 32);
   a.qpw = 32 / a.cols_heads;
   a.groups_max = (max_chunk_len + a.qpw - 1) / a.qpw;
-  a.largest_first = num_seqs <= kOrderMaxSeqs;
+  a.longest_first = num_seqs <= kOrderMaxSeqs;
   const int64_t units = static_cast<int64_t>((a.groups_max + kPrefillWaves - 1) / kPrefillWaves) *
                         num_seqs * num_kv_heads * a.head_blocks;
   if (units > 0x7fffffff) return PA_ERR_INVALID_ARG;

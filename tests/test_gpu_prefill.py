@@ -22,10 +22,12 @@ CASES = [
     ([70, 1], [0, 2000], 16, 8, 64, "f16"),                             # G = 2, whole prompt
     ([11, 3], [50, 400], 48, 1, 128, "bf16"),                           # G = 48: 2 head blocks, 2nd half full
     ([6, 17], [90, 3], 64, 1, 64, "f16"),                               # G = 64: 2 full head blocks
+    # equal lengths: ties in the longest-first order go by sequence index
+    ([1, 5, 5, 2, 64, 64, 3, 33], [10, 20, 20, 0, 0, 0, 61, 31], 8, 2, 128, "bf16"),
     # many sequences of mixed lengths: work-groups handed out longest first
     (np.random.default_rng(5).integers(1, 70, 40).tolist(),
      np.random.default_rng(6).integers(0, 600, 40).tolist(), 8, 2, 128, "bf16"),
-    # more sequences than the longest-first order ranks: plain order
+    # more sequences than the longest-first order ranks: index order
     (np.random.default_rng(7).integers(1, 5, 260).tolist(),
      np.random.default_rng(8).integers(0, 100, 260).tolist(), 8, 2, 64, "bf16"),
 ]
