@@ -16,11 +16,13 @@ def pytest_configure(config):
 def pytest_collection_modifyitems(config, items):
     # GPU tests run only where a GPU is visible; everywhere else they are skipped
     # with a reason instead of failing at import time.
-    try:
-        import torch
-        have_gpu = torch.cuda.is_available()
-    except Exception:  # pragma: no cover
-        have_gpu = False
+    have_gpu = False
+    if not os.environ.get("PA_SAN_POOL_LIB"):  # the sanitizer child runs host code only
+        try:
+            import torch
+            have_gpu = torch.cuda.is_available()
+        except Exception:  # pragma: no cover
+            have_gpu = False
     if have_gpu:
         return
     skip = pytest.mark.skip(reason="no GPU visible")
