@@ -29,7 +29,8 @@ __all__ = [
     "decode_shared_workspace_bytes",
     "decode_workspace_bytes", "decode_auto_partition",
     "reshape_and_cache_int8", "paged_attention_decode_int8",
-    "swap_blocks", "transfer_blocks", "new_host_kv_cache", "paged_attention_prefill",
+    "swap_blocks", "transfer_blocks", "release_finished_transfers", "new_host_kv_cache",
+    "paged_attention_prefill",
     "decode_step", "decode_step_int8",
     "new_kv_cache", "new_kv_cache_int8", "logical_view", "timing_begin", "timing_end", "timing_launches", "status_string",
 ]
@@ -498,9 +499,17 @@ def new_host_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype):
 _host_inflight: list = []
 
 
+def release_finished_transfers() -> int:
+    """Drop the references transfer_blocks keeps to host tensors whose copies
+    the device has finished (each call of transfer_blocks does this too);
+    returns how many copies still hold host tensors."""
+    _host_inflight[:] = [(e, ts) for e, ts in _host_inflight if not e.query()]
+    return len(_host_inflight)
+
+
 def _keep_host_alive(tensors, stream) -> None:
     torch = _torch()
-    _host_inflight[:] = [(e, ts) for e, ts in _host_inflight if not e.query()]
+    release_finished_transfers()
     host = [t for t in tensors if not t.is_cuda]
     if host:
         ev = torch.cuda.Event()

@@ -53,6 +53,7 @@ def test_transfer_round_trip_is_bit_exact(dtype):
     want_k, want_v = np.zeros_like(_np(kd)), np.zeros_like(_np(vd))
     cache_ops.transfer_blocks(ref_k, ref_v, want_k, want_v, back)
     assert np.array_equal(_np(kd2), want_k) and np.array_equal(_np(vd2), want_v)
+    assert pa.release_finished_transfers() == 0  # both copies done: no host tensor held
 
 
 def test_pageable_host_memory_is_refused():
