@@ -85,6 +85,49 @@ def test_copy_blocks_random_pairs_and_skips(dtype):
     assert _same_bits(k1, kr) and _same_bits(v1, vr)
 
 
+def _run(blocks, start_row, n):
+    """Slots of n consecutive positions from row start_row of blocks[0] on."""
+    return [int(blocks[(start_row + i) // 16]) * 16 + (start_row + i) % 16 for i in range(n)]
+
+
+@pytest.mark.parametrize("dtype,hkv,d", [("bf16", 8, 128), ("f16", 2, 64), ("bf16", 1, 256)])
+def test_token_runs_match_oracle_bits(dtype, hkv, d):
+    """Runs of new tokens through the windowed writer: aligned runs over whole
+    blocks, groups holding a skipped and an out-of-range slot, a run that
+    starts mid-block and crosses into another block, scattered slots and a
+    partial last window, bit for bit against the oracle."""
+    import torch
+    print(f"[gpu] token runs {dtype} hkv={hkv} d={d}", flush=True)
+    nb = 40
+    rng = np.random.default_rng(hkv * d)
+    perm = rng.permutation(nb)
+    group = _run(perm[5:6], 0, 16)
+    group[3], group[12] = -1, nb * 16 + 100   # skipped, out of range
+    scattered = rng.choice(np.arange(6 * 16, 16 * 16), 25, replace=False)
+    slots = (_run(perm[0:2], 0, 32) + group + _run(perm[4:5], 8, 8) + _run(perm[2:4], 5, 20)
+             + [int(perm[b // 16]) * 16 + b % 16 for b in scattered] + _run(perm[16:17], 0, 7))
+    slots = np.asarray(slots, np.int64)
+    T = len(slots)
+    valid = (slots >= 0) & (slots < nb * 16)
+    assert len(set(slots[valid].tolist())) == valid.sum()  # no slot written twice
+    pieces = [q for q in range(0, T - 7, 8)
+              if valid[q:q + 8].all() and slots[q] % 8 == 0
+              and (slots[q:q + 8] == slots[q] + np.arange(8)).all()]
+    assert pieces == [0, 8, 16, 24, 48]  # aligned groups of 8; the rest are not
+    bits = {"bf16": np.uint16, "f16": np.uint16}[dtype]
+    key = rng.integers(0, 0x7B00, (T, hkv, d)).astype(bits)   # finite values
+    value = rng.integers(0, 0x7B00, (T, hkv, d)).astype(bits)
+    kc_ref = np.full((nb, hkv, 16, d), NAN_BITS[dtype], bits)
+    vc_ref = kc_ref.copy()
+    cache_ops.reshape_and_cache(key, value, kc_ref, vc_ref, np.where(valid, slots, -1))
+    kc, vc = pa.new_kv_cache(nb, hkv, d, runner.torch_dtype(dtype), "cuda", float("nan"))
+    pa.reshape_and_cache(runner.to_device(key, dtype), runner.to_device(value, dtype), kc, vc,
+                         torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    k, v = pa.logical_view(kc, vc)
+    assert _same_bits(bits_of(k), kc_ref) and _same_bits(bits_of(v), vc_ref)
+
+
 def test_slot_minus_one_and_out_of_range_are_skipped():
     import torch
     print("[gpu] skipped slots", flush=True)

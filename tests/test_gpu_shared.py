@@ -116,6 +116,40 @@ def test_malformed_groups_are_bounded():
     _decode_with(db, [0, 1, 2, 3, 4, 5], [0, 6], [5], out)
 
 
+def test_large_groups_and_many_of_them():
+    # groups of more than 16 sequences are planned by the whole work-group, at
+    # most 64 of them; the rest, and every smaller group, by one thread each.
+    # 70 prompts x 17 samples: 70 large groups (64 + 6 past the list)
+    print("[gpu] shared decode, 70 groups of 17", flush=True)
+    prompts, samples = 70, 17
+    prompt_of = [p for p in range(prompts) for _ in range(samples)]
+    lens = [1 + (7 * i) % 9 for i in range(prompts * samples)]
+    w = workloads.make_custom(lens, hq=4, hkv=4, d=64, dtype="bf16", seed=12,
+                              prompt_lens=[32 + (p % 3) * 16 for p in range(prompts)],
+                              prompt_of=prompt_of)
+    shared, plain, ref = _both(w, pa.PARTITION_AUTO)
+    assert shared.shared[2].numel() == prompts
+    assert_close(shared.out_bits(), ref, "bf16", "70 groups of 17")
+    _close_to_plain(shared.out_bits(), plain.out_bits(), "bf16")
+
+
+def test_large_group_with_malformed_entries():
+    # one group of 39 listed entries: ids out of range among them are left
+    # out by the work-group's pass as by one thread's
+    print("[gpu] shared decode, a large group with bad entries", flush=True)
+    w = workloads.make_custom([3 + i % 5 for i in range(36)], hq=8, hkv=2, d=128, dtype="bf16",
+                              seed=5, prompt_lens=[80], prompt_of=[0] * 36)
+    db = runner.DeviceBatch(w)
+    db.prefill()
+    db.step()
+    ref = step.run(w, NAN_BITS["bf16"])[3]
+    seqs = list(range(36))
+    seqs[5:5] = [-3, 36, 1000]
+    out = torch.full_like(db.out, float("nan"))
+    _decode_with(db, seqs, [0, len(seqs)], [5], out)
+    assert_close(bits_of(out), ref, "bf16", "large group, bad entries")
+
+
 def test_fused_shared_step_equals_write_then_decode():
     print("[gpu] shared step fused vs unfused", flush=True)
     w = workloads.make_custom([1, 5, 20, 2, 3, 40, 7, 9], hq=8, hkv=2, d=128, dtype="bf16",
