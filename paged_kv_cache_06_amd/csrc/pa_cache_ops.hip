@@ -20,7 +20,7 @@ namespace {
 // One thread per (token, head, 16-byte chunk of D).
 template <typename E>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs<E> w) {
-  write_token_chunk<E, false>(w, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
+  w.template write<false>(static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
 }
 
 // INT8 cache: one thread per (token, head, 16-dimension chunk).

@@ -63,6 +63,8 @@ struct CacheWriteArgs {
   }
   template <bool kNT>
   __device__ void write(int64_t gid) const;
+  template <bool kNT, int N>
+  __device__ void write_many(int64_t gid0, int64_t stride) const;
 };
 
 template <typename E>
@@ -77,56 +79,84 @@ CacheWriteArgs<E> cache_write_args(const void* key, const void* value, void* k_c
 // Thread gid moves one 16-byte chunk of D of one (token, head): a 16-byte K
 // store (token rows of a chunk are contiguous) and X element stores of V
 // (transposed within the block), in the token-fastest order above.  Threads
-// past the end and skipped slots do nothing.
-template <typename E, bool kNT>
-__device__ __forceinline__ void write_token_chunk(const CacheWriteArgs<E>& w, int64_t gid) {
+// past the end and skipped slots do nothing.  The move is split into its
+// loads and its stores, so that a thread moving several chunks can have all
+// their loads in flight before it stores (write_many).
+template <typename E>
+struct ChunkMove {
+  uint4 k, v;
+  E* kdst;  // null: nothing to store
+  E* vdst;
+};
+
+template <typename E>
+__device__ __forceinline__ ChunkMove<E> load_token_chunk(const CacheWriteArgs<E>& w,
+                                                         int64_t gid) {
   constexpr int X = 16 / sizeof(E);
   const int chunks = w.head_dim / X;
-  if (gid >= w.threads()) return;
+  ChunkMove<E> m;
+  m.kdst = nullptr;
+  if (gid >= w.threads()) return m;
   const TokenChunk tc = token_chunk(gid, w.hkv, chunks, w.window);
   const int64_t t = tc.t;
   const int h = tc.h, c = tc.c;
-  if (t >= w.num_tokens) return;
+  if (t >= w.num_tokens) return m;
   const int64_t th = t * w.hkv + h;  // token * hkv + head
   const int64_t slot = w.slots[t];
-  if (slot < 0 || slot >= w.num_slots) return;
+  if (slot < 0 || slot >= w.num_slots) return m;
   const int64_t b = slot / kBlock;
   const int r = static_cast<int>(slot % kBlock);
   const int64_t src = th * w.head_dim + static_cast<int64_t>(c) * X;
   const int64_t head_base = (b * w.hkv + h) * static_cast<int64_t>(w.head_dim) * kBlock;
+  m.k = *reinterpret_cast<const uint4*>(w.key + src);
+  m.v = *reinterpret_cast<const uint4*>(w.value + src);
+  m.kdst = w.k_cache + head_base + (static_cast<int64_t>(c) * kBlock + r) * X;
+  m.vdst = w.v_cache + head_base + static_cast<int64_t>(c) * X * kBlock + r;
+  return m;
+}
 
-  // kNT: a decode step's tokens (one per sequence) are stored past the
-  // caches; runs of tokens (prefill, chunks) keep the default policy, under
-  // which the L2 merges their 2-byte V stores (non-temporal, a 133K-token
-  // prefill write took 1.9x as long).  The policy is a template parameter,
-  // not a branch: the compiler merges the two sides' stores and drops the
-  // hint.
-  const uint4 kv = *reinterpret_cast<const uint4*>(w.key + src);
-  E* kdst = w.k_cache + head_base + (static_cast<int64_t>(c) * kBlock + r) * X;
+// kNT: a decode step's tokens (one per sequence) are stored past the caches;
+// runs of tokens (prefill, chunks) keep the default policy, under which the
+// L2 merges their 2-byte V stores (non-temporal, a 133K-token prefill write
+// took 1.9x as long).  The policy is a template parameter, not a branch: the
+// compiler merges the two sides' stores and drops the hint.
+template <typename E, bool kNT>
+__device__ __forceinline__ void store_token_chunk(const ChunkMove<E>& m) {
+  constexpr int X = 16 / sizeof(E);
+  if (!m.kdst) return;
   if constexpr (kNT)
-    stream_store16(kdst, kv);
+    stream_store16(m.kdst, m.k);
   else
-    *reinterpret_cast<uint4*>(kdst) = kv;
-
+    *reinterpret_cast<uint4*>(m.kdst) = m.k;
   union {
     uint4 v;
     E e[X];
   } vv;
-  vv.v = *reinterpret_cast<const uint4*>(w.value + src);
-  E* vdst = w.v_cache + head_base + static_cast<int64_t>(c) * X * kBlock + r;
+  vv.v = m.v;
 #pragma unroll
   for (int i = 0; i < X; ++i) {
     if constexpr (kNT)
-      stream_store(vdst + i * kBlock, vv.e[i]);
+      stream_store(m.vdst + i * kBlock, vv.e[i]);
     else
-      vdst[i * kBlock] = vv.e[i];
+      m.vdst[i * kBlock] = vv.e[i];
   }
 }
 
 template <typename E>
 template <bool kNT>
 __device__ __forceinline__ void CacheWriteArgs<E>::write(int64_t gid) const {
-  write_token_chunk<E, kNT>(*this, gid);
+  store_token_chunk<E, kNT>(load_token_chunk(*this, gid));
+}
+
+// Chunks gid0 + i * stride, i < N: every load before any store.
+template <typename E>
+template <bool kNT, int N>
+__device__ __forceinline__ void CacheWriteArgs<E>::write_many(int64_t gid0, int64_t stride) const {
+  ChunkMove<E> m[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) m[i] = load_token_chunk(*this, gid0 + i * stride);
+#pragma unroll
+  for (int i = 0; i < N; ++i) store_token_chunk<E, kNT>(m[i]);
 }
 
 // ---- INT8 cache ("KV Cache for the intermediate", section "KV Cache
@@ -150,6 +180,11 @@ struct CacheWriteI8Args {
   }
   template <bool kNT>
   __device__ void write(int64_t gid) const;
+  template <bool kNT, int N>
+  __device__ void write_many(int64_t gid0, int64_t stride) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) write<kNT>(gid0 + i * stride);
+  }
 };
 
 // Thread gid quantizes one 16-dimension chunk of one (token, head), in the

@@ -438,6 +438,20 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
 // others write the step's new tokens into the cache (both only read their
 // inputs, so they can run side by side); the decode kernels follow on the
 // stream.
+//
+// The plan's registers set this kernel's occupancy (2 waves per SIMD), so a
+// run of tokens (kNT false: more tokens than sequences) is written kStepBatch
+// chunks per thread, all loaded before any is stored, to keep as many loads
+// in flight as the plain writer does at full occupancy (a 39K-token step:
+// 105 -> ~80 us).  A decode step's tokens, one per sequence, keep one chunk
+// per thread.
+constexpr int kStepBatch = 4;
+
+template <bool kNT>
+__host__ __device__ constexpr int step_batch() {
+  return kNT ? 1 : kStepBatch;
+}
+
 template <typename W, bool kNT>
 __global__ __launch_bounds__(kThreads) void decode_prep_kernel(PlanArgs a, W w) {
   __shared__ int wave_tot[kWaves * kPlanVals];
@@ -445,7 +459,9 @@ __global__ __launch_bounds__(kThreads) void decode_prep_kernel(PlanArgs a, W w) 
     plan_body(a, wave_tot);
     return;
   }
-  w.template write<kNT>(static_cast<int64_t>(blockIdx.x - 1) * kThreads + threadIdx.x);
+  const int64_t writers = static_cast<int64_t>(gridDim.x - 1) * kThreads;
+  w.template write_many<kNT, step_batch<kNT>()>(
+      static_cast<int64_t>(blockIdx.x - 1) * kThreads + threadIdx.x, writers);
 }
 
 // Merge of a split sequence's partials by the last of its work-groups to
@@ -1033,13 +1049,15 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
     }
     pa_status ps;
     if (write) {  // the step's cache writes ride along with the plan
-      const dim3 g(static_cast<uint32_t>(1 + (write->threads() + kThreads - 1) / kThreads));
-      // one token per sequence: stored past the caches (see write_token_chunk)
-      ps = write->window == 1
-               ? launch_kernel(PA_KERNEL_DECODE_PLAN, decode_prep_kernel<W, true>, g,
-                               dim3(kThreads), 0, st, pa, *write)
-               : launch_kernel(PA_KERNEL_DECODE_PLAN, decode_prep_kernel<W, false>, g,
-                               dim3(kThreads), 0, st, pa, *write);
+      // one token per sequence: stored past the caches (see store_token_chunk)
+      const bool nt = write->window == 1;
+      const int64_t per_group = static_cast<int64_t>(kThreads) * (nt ? step_batch<true>()
+                                                                      : step_batch<false>());
+      const dim3 g(static_cast<uint32_t>(1 + (write->threads() + per_group - 1) / per_group));
+      ps = nt ? launch_kernel(PA_KERNEL_DECODE_PLAN, decode_prep_kernel<W, true>, g,
+                              dim3(kThreads), 0, st, pa, *write)
+              : launch_kernel(PA_KERNEL_DECODE_PLAN, decode_prep_kernel<W, false>, g,
+                              dim3(kThreads), 0, st, pa, *write);
     } else {
       ps = launch_kernel(PA_KERNEL_DECODE_PLAN, decode_plan_kernel, dim3(1), dim3(kThreads), 0, st,
                          pa);
