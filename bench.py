@@ -581,7 +581,7 @@ def main():
     ec = 1 if int8 else w.elem_bytes
     pool_bytes = 2 * (w.num_blocks + 1) * w.num_kv_heads * 16 * w.head_dim * ec
     copies = args.copies or max(1, int(np.ceil(1.5e9 / pool_bytes)))
-    shared = (not args.no_shared and not int8 and bool(np.any(np.asarray(w.prompt_of) >= 0)))
+    shared = not args.no_shared and bool(np.any(np.asarray(w.prompt_of) >= 0))
     db = runner.DeviceBatch(w, copies=copies, int8=int8, shared_prefix=shared)
     db.prefill()
     torch.cuda.synchronize()

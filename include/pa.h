@@ -493,6 +493,41 @@ pa_status pa_decode_step_int8(const void* key, const void* value, const int64_t*
                               int32_t max_context_len, int32_t partition_size, void* workspace,
                               size_t workspace_bytes, pa_dtype dtype, void* stream);
 
+/* pa_paged_attention_decode_int8 for a batch whose sequences share leading
+ * blocks: each group's shared positions are read from the INT8 cache once for
+ * all its sequences, as pa_paged_attention_decode_shared does for a 16-bit
+ * cache ("KV Cache and PagedAttention: why your LLM server slows down",
+ * section "How PagedAttention fixes this"; "KV Cache for the intermediate",
+ * section "KV Cache Quantization").  The group arguments, their limits and
+ * the treatment of malformed listings are those of
+ * pa_paged_attention_decode_shared; the other arguments and errors those of
+ * pa_paged_attention_decode_int8.  The workspace is sized by
+ * pa_decode_shared_workspace_bytes with the same arguments (an INT8 cache
+ * needs no more).  With more than 16 query heads per KV head the groups are
+ * not used. */
+pa_status pa_paged_attention_decode_int8_shared(
+    const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* prefix_seqs, const int32_t* prefix_start, const int32_t* prefix_blocks,
+    int32_t num_groups, int32_t num_members, float scale, void* out, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    pa_dtype dtype, void* stream);
+
+/* pa_decode_step_int8 with shared prefixes: the step's quantizing token
+ * writes, then pa_paged_attention_decode_int8_shared (arguments as there and
+ * as pa_decode_step_int8), the writes running in the launch that builds the
+ * work list. */
+pa_status pa_decode_step_int8_shared(
+    const void* key, const void* value, const int64_t* slot_mapping, int32_t num_new_tokens,
+    int32_t num_blocks, const void* q, void* k_cache, void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* prefix_seqs, const int32_t* prefix_start, const int32_t* prefix_blocks,
+    int32_t num_groups, int32_t num_members, float scale, void* out, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    pa_dtype dtype, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Kernel timing.  Between pa_timing_begin and pa_timing_end every kernel the
  * library launches carries two HIP events attached to its dispatch on its own

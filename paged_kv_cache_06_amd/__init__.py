@@ -28,7 +28,8 @@ __all__ = [
     "shared_prefix_groups", "paged_attention_decode_shared", "decode_step_shared",
     "decode_shared_workspace_bytes",
     "decode_workspace_bytes", "decode_auto_partition",
-    "reshape_and_cache_int8", "paged_attention_decode_int8",
+    "reshape_and_cache_int8", "paged_attention_decode_int8", "paged_attention_decode_int8_shared",
+    "decode_step_int8_shared",
     "swap_blocks", "transfer_blocks", "release_finished_transfers", "new_host_kv_cache",
     "paged_attention_prefill",
     "decode_step", "decode_step_int8",
@@ -97,6 +98,11 @@ _SIGNATURES = {
     "pa_decode_step_shared": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32] + [_c_p] * 8 +
                               [_c_i32, _c_i32, _c_f, _c_p] + [_c_i32] * 7 +
                               [_c_p, _c_sz, _c_i32, _c_p]),
+    "pa_paged_attention_decode_int8_shared": (_c_i32, [_c_p] * 10 + [_c_i32, _c_i32, _c_f, _c_p] +
+                                              [_c_i32] * 7 + [_c_p, _c_sz, _c_i32, _c_p]),
+    "pa_decode_step_int8_shared": (_c_i32, [_c_p] * 3 + [_c_i32] * 2 + [_c_p] * 10 +
+                                   [_c_i32, _c_i32, _c_f, _c_p] + [_c_i32] * 7 +
+                                   [_c_p, _c_sz, _c_i32, _c_p]),
     "pa_reshape_and_cache_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "pa_paged_attention_decode_int8": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f,
@@ -799,6 +805,74 @@ def decode_step_int8(key, value, slot_mapping, q, k_cache, v_cache, k_scale, v_s
         _ptr(block_tables), _ptr(context_lens.contiguous()), float(scale), _ptr(out), s, hq, hkv,
         d, mb, mcl, int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q)),
         "pa_decode_step_int8")
+
+
+def _int8_decode_args(q, k_cache, v_cache, block_tables, context_lens, out, max_context_len):
+    torch = _torch()
+    _need(k_cache.dtype == torch.int8, "INT8 caches expected")
+    nb, hkv, d = _cache_dims(k_cache, v_cache)
+    s, hq, dq = q.shape
+    _need(dq == d and tuple(out.shape) == (s, hq, d), "q/out must be [S, Hq, D]")
+    _need(q.is_contiguous() and out.is_contiguous(), "q/out must be contiguous")
+    _need(q.dtype == out.dtype, "q/out dtypes differ")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == s and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == s and
+          context_lens.is_contiguous(), "context_lens must be contiguous int32 [S]")
+    mb = block_tables.shape[1]
+    mcl = mb * BLOCK_SIZE if max_context_len is None else int(max_context_len)
+    return nb, hkv, d, s, hq, mb, mcl
+
+
+def paged_attention_decode_int8_shared(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                       context_lens, prefix_seqs, prefix_start, prefix_blocks,
+                                       scale, out, *, max_context_len: int | None = None,
+                                       partition_size: int = PARTITION_AUTO,
+                                       workspace=None) -> None:
+    """paged_attention_decode_int8 reading each group's shared leading blocks
+    once (``pa_paged_attention_decode_int8_shared``); prefix_* as for
+    ``paged_attention_decode_shared``."""
+    nb, hkv, d, s, hq, mb, mcl = _int8_decode_args(q, k_cache, v_cache, block_tables,
+                                                   context_lens, out, max_context_len)
+    ng, nm = _shared_args(prefix_seqs, prefix_start, prefix_blocks)
+    ws_ptr, ws_bytes = _workspace(q, s, hq, d, mcl, partition_size, workspace,
+                                  decode_shared_workspace_bytes(s, hq, d, mcl, partition_size, ng,
+                                                                nm))
+    _check(load().pa_paged_attention_decode_int8_shared(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _scales(k_scale, hkv, d, "k_scale"),
+        _scales(v_scale, hkv, d, "v_scale"), _ptr(block_tables), _ptr(context_lens),
+        _ptr(prefix_seqs), _ptr(prefix_start), _ptr(prefix_blocks), ng, nm, float(scale),
+        _ptr(out), s, hq, hkv, d, mb, mcl, int(partition_size), ws_ptr, ws_bytes, _dtype_code(q),
+        _stream(q)), "pa_paged_attention_decode_int8_shared")
+
+
+def decode_step_int8_shared(key, value, slot_mapping, q, k_cache, v_cache, k_scale, v_scale,
+                            block_tables, context_lens, prefix_seqs, prefix_start, prefix_blocks,
+                            scale, out, *, max_context_len: int | None = None,
+                            partition_size: int = PARTITION_AUTO, workspace=None) -> None:
+    """decode_step_int8 with shared prefixes (``pa_decode_step_int8_shared``)."""
+    torch = _torch()
+    nb, hkv, d, s, hq, mb, mcl = _int8_decode_args(q, k_cache, v_cache, block_tables,
+                                                   context_lens, out, max_context_len)
+    t = key.shape[0]
+    _need(tuple(key.shape) == (t, hkv, d) and tuple(value.shape) == (t, hkv, d),
+          "key/value must be [T, Hkv, D]")
+    _need(key.is_contiguous() and value.is_contiguous(), "key/value must be contiguous")
+    _need(key.dtype == value.dtype == q.dtype, "key/value/q dtypes differ")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == t and
+          slot_mapping.is_contiguous(), "slot_mapping must be contiguous int64 [T]")
+    ng, nm = _shared_args(prefix_seqs, prefix_start, prefix_blocks)
+    ws_ptr, ws_bytes = _workspace(q, s, hq, d, mcl, partition_size, workspace,
+                                  decode_shared_workspace_bytes(s, hq, d, mcl, partition_size, ng,
+                                                                nm))
+    _check(load().pa_decode_step_int8_shared(
+        _ptr(key), _ptr(value), _ptr(slot_mapping), t, nb, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _scales(k_scale, hkv, d, "k_scale"), _scales(v_scale, hkv, d, "v_scale"),
+        _ptr(block_tables), _ptr(context_lens), _ptr(prefix_seqs), _ptr(prefix_start),
+        _ptr(prefix_blocks), ng, nm, float(scale), _ptr(out), s, hq, hkv, d, mb, mcl,
+        int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q)),
+        "pa_decode_step_int8_shared")
 
 
 def paged_attention_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_tables,

@@ -617,7 +617,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int4 it, int gh
 // products is member c / G, head c % G -- instead of once per sequence.
 // Each member's partial goes to slot it.w of its rows and is merged with its
 // private partials like any other.  Only for query-head groups G <= 16.
-template <typename Tag, int D, int W>
+// kInt8: an INT8 cache (the K scale folded into each column's query, the V
+// scale applied to each partial, as in decode_item).
+template <typename Tag, int D, int W, bool kInt8>
 __device__ __forceinline__ void decode_prefix_tile(const DecodeArgs& a, int4 it, int g,
                                                    float* comb) {
   __shared__ int s_mem[16], s_np[16], s_last[16];
@@ -651,18 +653,25 @@ __device__ __forceinline__ void decode_prefix_tile(const DecodeArgs& a, int4 it,
   const int m = n / G, hh = n % G;
   const int seq = m < k ? s_mem[m] : -1;
   uint4 qf[D / 32];
-  if (seq >= 0) {
-    const uint4* qrow = reinterpret_cast<const uint4*>(
-        a.q + (static_cast<size_t>(seq) * a.hq_total + g * G + hh) * D + kg * 8);
-#pragma unroll
-    for (int step = 0; step < D / 32; ++step) qf[step] = qrow[step * 4];
-  } else {
-#pragma unroll
-    for (int step = 0; step < D / 32; ++step) qf[step] = make_uint4(0, 0, 0, 0);
-  }
   WaveState<D> st;
   st.reset();
-  attend_blocks<Tag, D, W>(a, trow, ids, b_first, count, end, g, qf, st);
+  if constexpr (kInt8) {
+    const uint16_t* qrow =
+        seq >= 0 ? a.q + (static_cast<size_t>(seq) * a.hq_total + g * G + hh) * D : nullptr;
+    const float back = load_q_i8_cols<Tag, D>(a, qrow, g, qf);
+    attend_blocks_i8<D, W>(a, trow, ids, b_first, count, end, g, qf, a.scale_log2 * back, st);
+  } else {
+    if (seq >= 0) {
+      const uint4* qrow = reinterpret_cast<const uint4*>(
+          a.q + (static_cast<size_t>(seq) * a.hq_total + g * G + hh) * D + kg * 8);
+#pragma unroll
+      for (int step = 0; step < D / 32; ++step) qf[step] = qrow[step * 4];
+    } else {
+#pragma unroll
+      for (int step = 0; step < D / 32; ++step) qf[step] = make_uint4(0, 0, 0, 0);
+    }
+    attend_blocks<Tag, D, W>(a, trow, ids, b_first, count, end, g, qf, st);
+  }
   stage_partials<D, W>(comb, 16, 16, st);
   __syncthreads();
   for (int e = threadIdx.x; e < 16 * D; e += W * kWave) {
@@ -671,6 +680,7 @@ __device__ __forceinline__ void decode_prefix_tile(const DecodeArgs& a, int4 it,
     if (mc >= k || s_mem[mc] < 0) continue;
     float M, L, A;
     combine_waves<W>(comb, 16, D, c, d, M, L, A);
+    if constexpr (kInt8) A *= a.v_scale[static_cast<size_t>(g) * D + d];
     const size_t row = static_cast<size_t>(s_mem[mc]) * a.hq_total + g * G + c % G;
     store_result<Tag, D>(a, row, d, slot, s_np[mc], M, L, A);
   }
@@ -705,7 +715,7 @@ __global__ __launch_bounds__(item_threads(W), 4) void decode_items_kernel(
   const int4 it = items[blockIdx.x / heads];
   if (it.x == -1) return;
   if (it.x < -1) {
-    if (a.pfx_seqs) decode_prefix_tile<Tag, D, W>(a, it, blockIdx.x % heads, comb);
+    if (a.pfx_seqs) decode_prefix_tile<Tag, D, W, false>(a, it, blockIdx.x % heads, comb);
     return;
   }
   decode_item<Tag, D, false, W>(a, it, blockIdx.x % heads, comb);
@@ -719,7 +729,11 @@ __global__ __launch_bounds__(item_threads(W), 4) void decode_items_i8_kernel(
   extern __shared__ float comb[];
   const int heads = a.hkv * a.head_blocks;
   const int4 it = items[blockIdx.x / heads];
-  if (it.x < 0) return;
+  if (it.x < 0) {  // the end of the list, or a prefix item
+    if (it.x < -1 && a.pfx_seqs)
+      decode_prefix_tile<Tag, D, W, true>(a, it, blockIdx.x % heads, comb);
+    return;
+  }
   decode_item<Tag, D, true, W>(a, it, blockIdx.x % heads, comb);
 }
 
@@ -1260,7 +1274,8 @@ pa_status decode_int8_impl(const void* q, const void* k_cache, const void* v_cac
                            void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
                            int32_t partition_size, void* workspace, size_t workspace_bytes,
-                           pa_dtype dtype, void* stream, const StepWrite& wr) {
+                           pa_dtype dtype, void* stream, const StepWrite& wr,
+                           const SharedPrefix* shared = nullptr) {
   if (dtype != PA_BF16 && dtype != PA_F16) return PA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
@@ -1276,7 +1291,13 @@ pa_status decode_int8_impl(const void* q, const void* k_cache, const void* v_cac
   Split sp;
   if (!resolve_split(partition_size, num_seqs, num_kv_heads, max_context_len, &sp, 1))
     return PA_ERR_INVALID_ARG;
-  const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp).total;
+  // shared prefixes as in decode_impl (this path is always the matrix-core one)
+  const SharedPrefix* sh =
+      shared && shared->num_groups > 0 && num_q_heads / num_kv_heads <= 16 ? shared : nullptr;
+  if (sh && partition_size == PA_PARTITION_AUTO && sp.np > 1 &&
+      !resolve_split(2 * sp.part, num_seqs, num_kv_heads, max_context_len, &sp, 1))
+    return PA_ERR_INVALID_ARG;
+  const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, sp, sh).total;
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
     return PA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -1294,7 +1315,7 @@ pa_status decode_int8_impl(const void* q, const void* k_cache, const void* v_cac
     w.window = step_window(wr.num_tokens, num_seqs);
     return launch<BF16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out,
                          num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp,
-                         ws, true, st, k_scale, v_scale, fused ? &w : nullptr);
+                         ws, true, st, k_scale, v_scale, fused ? &w : nullptr, sh);
   }
   CacheWriteI8Args<F16T> w{static_cast<const uint16_t*>(wr.key),
                            static_cast<const uint16_t*>(wr.value), kc, vc, wr.slots, k_scale,
@@ -1302,7 +1323,7 @@ pa_status decode_int8_impl(const void* q, const void* k_cache, const void* v_cac
   w.window = step_window(wr.num_tokens, num_seqs);
   return launch<F16T>(q, k_cache, v_cache, block_tables, context_lens, scale_log2, out, num_seqs,
                       num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sp, ws, true, st,
-                      k_scale, v_scale, fused ? &w : nullptr);
+                      k_scale, v_scale, fused ? &w : nullptr, sh);
 }
 
 }  // namespace
@@ -1509,6 +1530,56 @@ pa_status pa_decode_step_shared(
                      num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, max_context_len,
                      partition_size, workspace, workspace_bytes, dtype, stream,
                      StepWrite{key, value, slot_mapping, num_new_tokens, num_blocks}, &sh);
+}
+
+pa_status pa_paged_attention_decode_int8_shared(
+    const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* prefix_seqs, const int32_t* prefix_start, const int32_t* prefix_blocks,
+    int32_t num_groups, int32_t num_members, float scale, void* out, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    pa_dtype dtype, void* stream) {
+  pa::SharedPrefix sh;
+  const pa_status st =
+      shared_args(prefix_seqs, prefix_start, prefix_blocks, num_groups, num_members, &sh);
+  if (st != PA_OK) return st;
+  return pa::decode_int8_impl(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                              scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              max_blocks_per_seq, max_context_len, partition_size, workspace,
+                              workspace_bytes, dtype, stream,
+                              pa::StepWrite{nullptr, nullptr, nullptr, 0, 0}, &sh);
+}
+
+pa_status pa_decode_step_int8_shared(
+    const void* key, const void* value, const int64_t* slot_mapping, int32_t num_new_tokens,
+    int32_t num_blocks, const void* q, void* k_cache, void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* prefix_seqs, const int32_t* prefix_start, const int32_t* prefix_blocks,
+    int32_t num_groups, int32_t num_members, float scale, void* out, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    pa_dtype dtype, void* stream) {
+  using namespace pa;
+  pa::SharedPrefix sh;
+  const pa_status st =
+      shared_args(prefix_seqs, prefix_start, prefix_blocks, num_groups, num_members, &sh);
+  if (st != PA_OK) return st;
+  // the write's own checks, as pa_decode_step_int8 makes them
+  if (num_new_tokens < 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (num_new_tokens > 0 && (!key || !value || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  if ((static_cast<int64_t>(num_new_tokens) * num_kv_heads * head_dim / 16 + 255) / 256 >
+      0x7fffffff)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0)  // nothing to attend: only the write
+    return pa_reshape_and_cache_int8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale,
+                                     num_new_tokens, num_blocks, num_kv_heads, head_dim, dtype,
+                                     stream);
+  return decode_int8_impl(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                          scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          max_blocks_per_seq, max_context_len, partition_size, workspace,
+                          workspace_bytes, dtype, stream,
+                          StepWrite{key, value, slot_mapping, num_new_tokens, num_blocks}, &sh);
 }
 
 }  // extern "C"

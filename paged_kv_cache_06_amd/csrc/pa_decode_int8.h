@@ -129,6 +129,50 @@ __device__ __forceinline__ float load_q_i8(const DecodeArgs& a, int s, int g, in
   return ldexpf(1.f, ex - 15);
 }
 
+// load_q_i8 for the columns of a prefix tile, whose query rows belong to
+// different sequences: qrow is this lane's column's row (every lane of a
+// column passes the same one), nullptr for an empty column (reads 0).
+template <typename Tag, int D>
+__device__ __forceinline__ float load_q_i8_cols(const DecodeArgs& a, const uint16_t* qrow, int g,
+                                                uint4* qh) {
+  const uint32_t kg = (threadIdx.x & (kWave - 1)) >> 4;
+  const float* sk = a.k_scale + static_cast<size_t>(g) * D;
+  float x[D / 32][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+    const uint32_t d0 = 64 * (m >> 1) + 16 * kg + 8 * (m & 1);
+    const uint4 qv = qrow ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
+    const uint4 s0 = *reinterpret_cast<const uint4*>(sk + d0);
+    const uint4 s1 = *reinterpret_cast<const uint4*>(sk + d0 + 4);
+    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t bits = static_cast<uint16_t>(qw[e / 2] >> (16 * (e & 1)));
+      x[m][e] = Tag::to_f32(bits) * __uint_as_float(sw[e]);
+      amax = fmaxf(amax, fabsf(x[m][e]));
+    }
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  int ex;
+  (void)frexpf(amax, &ex);  // amax < 2^ex (ex = 0 for amax = 0)
+  const float up = ldexpf(1.f, 15 - ex);
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+    uint32_t hw[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const f16x2_t v = {static_cast<_Float16>(x[m][e] * up),
+                         static_cast<_Float16>(x[m][e + 1] * up)};
+      hw[e / 2] = __builtin_bit_cast(uint32_t, v);
+    }
+    qh[m] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  }
+  return ldexpf(1.f, ex - 15);
+}
+
 // attend_blocks over an INT8 cache: sl2 is the per-lane score factor (the
 // softmax scale in log2 units times load_q_i8's return value).
 template <int D, int W>

@@ -20,10 +20,11 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import (BLOCK_SIZE, PARTITION_AUTO, BlockManager, Pool, copy_blocks, decode_step,
-               decode_step_int8, decode_step_shared, new_kv_cache,
+               decode_step_int8, decode_step_int8_shared, decode_step_shared, new_kv_cache,
                new_kv_cache_int8, paged_attention_decode, paged_attention_decode_int8,
-               paged_attention_decode_shared, paged_attention_prefill, reshape_and_cache,
-               reshape_and_cache_int8, shared_prefix_groups)
+               paged_attention_decode_int8_shared, paged_attention_decode_shared,
+               paged_attention_prefill, reshape_and_cache, reshape_and_cache_int8,
+               shared_prefix_groups)
 
 _TORCH_DTYPE = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
 NAN_FILL = float("nan")
@@ -209,6 +210,13 @@ class DeviceBatch:
         if ph["pairs"].shape[0]:
             copy_blocks(kc, vc, ph["pairs"])
         o = self.out if out is None else out
+        if self.int8 and self.shared is not None:
+            decode_step_int8_shared(ph["key"], ph["value"], ph["slots"], self.q, kc, vc,
+                                    self.k_scale, self.v_scale, self.tables, self.context_lens,
+                                    *self.shared, self.w.scale, o,
+                                    max_context_len=self.max_context_len,
+                                    partition_size=partition_size)
+            return
         if self.int8:
             decode_step_int8(ph["key"], ph["value"], ph["slots"], self.q, kc, vc, self.k_scale,
                              self.v_scale, self.tables, self.context_lens, self.w.scale, o,
@@ -226,6 +234,13 @@ class DeviceBatch:
 
     def decode(self, copy: int = 0, partition_size: int = PARTITION_AUTO, out=None):
         kc, vc = self.caches[copy]
+        if self.int8 and self.shared is not None:
+            paged_attention_decode_int8_shared(self.q, kc, vc, self.k_scale, self.v_scale,
+                                               self.tables, self.context_lens, *self.shared,
+                                               self.w.scale, self.out if out is None else out,
+                                               max_context_len=self.max_context_len,
+                                               partition_size=partition_size)
+            return
         if self.int8:
             paged_attention_decode_int8(self.q, kc, vc, self.k_scale, self.v_scale, self.tables,
                                         self.context_lens, self.w.scale,

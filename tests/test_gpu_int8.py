@@ -63,6 +63,34 @@ def test_special_values_quantize_like_the_oracle():
     assert kc[0, 0, 0, :8].tolist() == [0, 127, -127, 0, 2, -2, 127, 0]
 
 
+def test_near_ties_at_general_scales_quantize_like_the_oracle():
+    # scales that are not powers of two: the writer's fast quotient x * rcp(s)
+    # decides far from a tie and the exact fp32 division near one; planted
+    # values are the fp32 ties (k + 1/2) * s and their neighbours one ulp away
+    import torch
+    print("[gpu] int8 near-ties at general scales", flush=True)
+    hkv, d, t = 2, 128, 64
+    rng = np.random.default_rng(17)
+    sk = ((3.5 + rng.random((hkv, d))) / 127).astype(np.float32)
+    sv = rng.uniform(1e-3, 0.2, (hkv, d)).astype(np.float32)
+    k = rng.integers(-130, 130, (t, hkv, d)).astype(np.float32)
+    tie = ((k + np.float32(0.5)) * sk).astype(np.float32)
+    step_ = rng.integers(-1, 2, (t, hkv, d))  # the tie, or one ulp below or above it
+    x = np.where(step_ == 0, tie, np.nextafter(tie, np.where(step_ > 0, np.inf, -np.inf)))
+    x = x.astype(np.float32)
+    y = (rng.standard_normal((t, hkv, d)) * 10).astype(np.float32)
+    kq, vq = pa.new_kv_cache_int8(8, hkv, d, "cuda", 33)
+    slots = rng.permutation(8 * 16)[:t].astype(np.int64)
+    pa.reshape_and_cache_int8(torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda(), kq, vq,
+                              torch.from_numpy(slots).cuda(), torch.from_numpy(sk).cuda(),
+                              torch.from_numpy(sv).cuda())
+    kc = np.full((8, hkv, 16, d), 33, np.int8)
+    vc = kc.copy()
+    quant.reshape_and_cache(x, y, "f32", kc, vc, slots, sk, sv)
+    kg, vg = pa.logical_view(kq, vq)
+    assert np.array_equal(kg.cpu().numpy(), kc) and np.array_equal(vg.cpu().numpy(), vc)
+
+
 CASES = [
     # (lens, hq, hkv, d, dtype)
     ([1, 15, 16, 17, 33, 100, 257, 600], 8, 2, 128, "bf16"),

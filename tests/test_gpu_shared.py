@@ -185,3 +185,73 @@ def test_full_size_shared_prefix_workloads_every_output(config):
     again = torch.empty_like(shared.out)
     shared.decode(out=again)
     assert np.array_equal(bits_of(again), shared.out_bits())  # run to run
+
+
+# ---- the same over an INT8 cache ----
+
+def _both_int8(w, partition_size):
+    ref = step.run_int8(w)[3]
+    shared = runner.DeviceBatch(w, int8=True, shared_prefix=True)
+    plain = runner.DeviceBatch(w, int8=True)
+    for db in (shared, plain):
+        db.prefill()
+        db.step(partition_size=partition_size)
+    torch.cuda.synchronize()
+    return shared, plain, ref
+
+
+INT8_SHAPES = [
+    (8, 2, 128, "bf16"),    # G = 4
+    (16, 2, 128, "f16"),    # G = 8
+    (4, 4, 64, "bf16"),     # G = 1: 16 samples per pass
+    (32, 2, 64, "f16"),     # G = 16
+]
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", INT8_SHAPES)
+@pytest.mark.parametrize("partition_size", [pa.PARTITION_AUTO, pa.PARTITION_NONE, 64, 1024])
+def test_int8_small_groups_against_oracle(hq, hkv, d, dtype, partition_size):
+    print(f"[gpu] int8 shared decode {hq}/{hkv} d={d} {dtype} P={partition_size}", flush=True)
+    prompt_of = [0, 0, 0, -1, 1, 1, 1, 1, 1, 2, 2, 3, 3, 3, 3, 3, 3, -1]
+    lens = [1, 5, 20, 2, 3, 40, 7, 9, 70, 1, 33, 2, 17, 16, 1, 64, 5, 100]
+    w = workloads.make_custom(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=hq + d + 1,
+                              prompt_lens=[21, 32, 45, 300], prompt_of=prompt_of)
+    shared, plain, ref = _both_int8(w, partition_size)
+    assert shared.shared[2].numel() == 4
+    assert_close(shared.out_bits(), ref, dtype, f"int8 shared {hq}/{hkv} P={partition_size}")
+    _close_to_plain(shared.out_bits(), plain.out_bits(), dtype)
+
+
+def test_int8_fused_shared_step_equals_write_then_decode():
+    print("[gpu] int8 shared step fused vs unfused", flush=True)
+    w = workloads.make_custom([1, 5, 20, 2, 3, 40, 7, 9], hq=8, hkv=2, d=128, dtype="bf16",
+                              seed=32, prompt_lens=[21, 32, 45],
+                              prompt_of=[0, 0, 0, 1, 1, 1, 2, 2])
+    a = runner.DeviceBatch(w, int8=True, shared_prefix=True)
+    b = runner.DeviceBatch(w, int8=True, shared_prefix=True)
+    for db, fused in ((a, True), (b, False)):
+        db.prefill()
+        db.step(fused=fused)
+    torch.cuda.synchronize()
+    for x, y in zip(a.caches[0], b.caches[0]):
+        assert torch.equal(x, y)
+    assert np.array_equal(a.out_bits(), b.out_bits())
+
+
+@pytest.mark.parametrize("config", [4, "4b"])
+def test_int8_full_size_shared_prefix_workloads_every_output(config):
+    print(f"[gpu] full-size workload {config}, INT8 cache, through the shared-prefix decode",
+          flush=True)
+    w = workloads.make(config)
+    shared = runner.DeviceBatch(w, int8=True, shared_prefix=True)
+    shared.prefill()
+    shared.step()
+    torch.cuda.synchronize()
+    assert shared.shared[2].numel() == (64 if config == 4 else 1)
+    ref = step.run_int8(w)[3]
+    info = assert_close(shared.out_bits(), ref, "bf16", f"workload {config}, int8, shared")
+    print(f"  {info}", flush=True)
+    plain = runner.DeviceBatch(w, int8=True)
+    plain.prefill()
+    plain.step()
+    _close_to_plain(shared.out_bits(), plain.out_bits(), "bf16")
