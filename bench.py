@@ -617,11 +617,9 @@ def main():
     dec = kt["decode"]
     dec_ms = dec["ms"] / max(1, dec["launches"])
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
-    ps = args.partition if args.partition != -1 else pa.decode_auto_partition(
-        w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, db.max_context_len,
-        3 if int8 else {"f32": 0, "f16": 1, "bf16": 2}[w.dtype])
-    if db.shared is not None and args.partition == -1 and 0 < ps < db.max_context_len:
-        ps *= 2  # the shared-prefix decode doubles the automatic partition
+    # the partition the plan used: the automatic one may be doubled, for shared
+    # prefixes on the host and for an even batch by the plan itself
+    ps = pa.last_plan_partition()
     if int8:
         main_kernel = "decode_items_i8_kernel"
     elif w.dtype != "f32" and w.head_dim in (64, 128):

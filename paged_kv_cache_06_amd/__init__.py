@@ -27,7 +27,7 @@ __all__ = [
     "paged_attention_decode", "paged_attention_decode_noalloc", "DECODE_SCRATCH_BYTES",
     "shared_prefix_groups", "paged_attention_decode_shared", "decode_step_shared",
     "decode_shared_workspace_bytes",
-    "decode_workspace_bytes", "decode_auto_partition",
+    "decode_workspace_bytes", "decode_auto_partition", "last_plan_partition",
     "reshape_and_cache_int8", "paged_attention_decode_int8", "paged_attention_decode_int8_shared",
     "decode_step_int8_shared",
     "swap_blocks", "transfer_blocks", "release_finished_transfers", "new_host_kv_cache",
@@ -755,6 +755,19 @@ def decode_step_shared(key, value, slot_mapping, q, k_cache, v_cache, block_tabl
         _ptr(prefix_blocks), ng, nm, float(scale), _ptr(out), s, hq, hkv, d, mb, mcl,
         int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q)),
         "pa_decode_step_shared")
+
+
+def last_plan_partition() -> int:
+    """The partition size the last decode through a workspace of this module
+    planned with (word 2 of the plan's header in that workspace): the given
+    or automatic one, or the automatic one doubled by the plan for an even
+    batch.  0 if no decode has run."""
+    torch = _torch()
+    if not _workspaces:
+        return 0
+    ws = next(iter(_workspaces.values()))
+    torch.cuda.synchronize(ws.device)
+    return int(ws[:12].view(torch.int32)[2].item())
 
 
 def _workspace(q, s, hq, d, mcl, partition_size, workspace, need=None):

@@ -102,14 +102,16 @@ __device__ __forceinline__ ChunkMove<E> load_token_chunk(const CacheWriteArgs<E>
   const int h = tc.h, c = tc.c;
   if (t >= w.num_tokens) return m;
   const int64_t th = t * w.hkv + h;  // token * hkv + head
+  // the token's K and V chunks do not depend on its slot: they are loaded
+  // together with it, so one memory latency precedes the stores, not two
+  const int64_t src = th * w.head_dim + static_cast<int64_t>(c) * X;
+  m.k = *reinterpret_cast<const uint4*>(w.key + src);
+  m.v = *reinterpret_cast<const uint4*>(w.value + src);
   const int64_t slot = w.slots[t];
   if (slot < 0 || slot >= w.num_slots) return m;
   const int64_t b = slot / kBlock;
   const int r = static_cast<int>(slot % kBlock);
-  const int64_t src = th * w.head_dim + static_cast<int64_t>(c) * X;
   const int64_t head_base = (b * w.hkv + h) * static_cast<int64_t>(w.head_dim) * kBlock;
-  m.k = *reinterpret_cast<const uint4*>(w.key + src);
-  m.v = *reinterpret_cast<const uint4*>(w.value + src);
   m.kdst = w.k_cache + head_base + (static_cast<int64_t>(c) * kBlock + r) * X;
   m.vdst = w.v_cache + head_base + static_cast<int64_t>(c) * X * kBlock + r;
   return m;
@@ -220,13 +222,8 @@ __device__ __forceinline__ void CacheWriteI8Args<Tag>::write(int64_t gid) const 
   const int h = tc.h, c = tc.c;
   if (t >= num_tokens) return;
   const int64_t th = t * hkv + h;  // token * hkv + head
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t b = slot / kBlock;
-  const int r = static_cast<int>(slot % kBlock);
   const int64_t src = th * head_dim + static_cast<int64_t>(c) * 16;
   const int64_t sc = static_cast<int64_t>(h) * head_dim + c * 16;
-  const int64_t slab = (b * hkv + h) * static_cast<int64_t>(head_dim) * kBlock + (c / 4) * 1024;
 
   union Values {
     uint4 u[kPieces];
@@ -248,6 +245,12 @@ __device__ __forceinline__ void CacheWriteI8Args<Tag>::write(int64_t gid) const 
     ks.u[q] = reinterpret_cast<const float4*>(k_scale + sc)[q];
     vs.u[q] = reinterpret_cast<const float4*>(v_scale + sc)[q];
   }
+  // values and scales do not depend on the slot: loaded together with it
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t b = slot / kBlock;
+  const int r = static_cast<int>(slot % kBlock);
+  const int64_t slab = (b * hkv + h) * static_cast<int64_t>(head_dim) * kBlock + (c / 4) * 1024;
   uint32_t kw[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < 16; ++e)

@@ -123,6 +123,8 @@ struct PlanArgs {
   int* grp_tokens;            // workspace [num_groups]: shared positions of each group
   int* grp_leader;            // workspace [num_groups]: a member whose row holds them
   int capacity;               // entries of the item list
+  int heads = 0;              // head groups per item (work-groups per list entry)
+  int even_doubling = 0;      // the partition is automatic: double it for even batches
 };
 
 // A length beyond the call's bound is cut to it, so that no sequence has more
@@ -254,6 +256,10 @@ __device__ __forceinline__ int plan_shared(const PlanArgs& a, int i) {
 // for a sequence with more than one partial.
 constexpr int kFull = kClasses, kSplit = kClasses + 1;
 constexpr int kPlanVals = kClasses + 2;
+// two more values in the plan's first scan: items and rounds at twice the
+// partition (even_batch)
+constexpr int kEvenItems = kPlanVals, kEvenRounds = kPlanVals + 1;
+constexpr int kScanVals = kPlanVals + 2;
 
 struct SeqPlan {
   int len, shared, np_pre, np_priv;  // np_priv: private partitions (0: none)
@@ -340,12 +346,55 @@ __device__ __forceinline__ int plan_partition(const PlanArgs& a, int i0, int i1,
   return a.max_blocks * kBlock;
 }
 
+// Items and rounds (blocks per wave, summed over items) of sequences i0..i1
+// at partition part2, for the choice below.
+__device__ __forceinline__ void even_counts(const PlanArgs& a, int part2, int i0, int i1,
+                                            int* items, int* rounds) {
+  const int r_full = ceil_div(ceil_div(part2, kBlock), a.waves);
+  int n = 0, r = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int len = plan_len(a, i);
+    const int full = len / part2, rest = len - full * part2;
+    n += max(1, ceil_div(len, part2));
+    r += full * r_full + (rest > 0 ? ceil_div(ceil_div(rest, kBlock), a.waves) : 0);
+  }
+  *items = n;
+  *rounds = r;
+}
+
+// An automatic partition is doubled once for a batch of evenly long
+// sequences: when at twice the size the list still gives every CU two
+// work-groups and its longest item streams at most 1.5x the rounds of the
+// mean one.  Fewer, longer items then lose no parallelism and save the
+// per-item start-up and merges (Llama-3-8B layer, 64 sequences of
+// U{128..4096}: 104.6 -> 98.5 us at 2048; 8 x 32K: 181.6 -> 173.9 us at
+// 4096), while a skewed batch, whose longest items would then trail the
+// rest, keeps its partition (70B mixed batch: 96.6 us at 1024, 98.1 at 2048).
+__device__ __forceinline__ bool even_batch(const PlanArgs& a, int part2, int items2,
+                                           int rounds2) {
+  const int max_rounds = ceil_div(ceil_div(min(part2, a.max_len), kBlock), a.waves);
+  return static_cast<int64_t>(items2) * a.heads >= 512 &&
+         2 * static_cast<int64_t>(max_rounds) * items2 <= 3 * static_cast<int64_t>(rounds2);
+}
+
 // The item list, largest first (see the file header).  One work-group; each
 // thread takes a run of consecutive sequences and a run of consecutive
 // groups, so one exclusive scan of its per-class counts places every item
 // (sequences before groups within a thread's share of a class).
-__device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
-  constexpr int kVals = kPlanVals;
+// The plan reads every length several times (counts, the even-batch test,
+// the emission; the group pass): batches of up to kLensLds sequences read
+// them from LDS after one pass over global memory.
+constexpr int kLensLds = 4096;
+
+__device__ __forceinline__ void plan_body(const PlanArgs& args, int* wave_tot) {
+  __shared__ int s_lens[kLensLds];
+  PlanArgs a = args;
+  if (args.num_seqs <= kLensLds) {
+    for (int i = threadIdx.x; i < args.num_seqs; i += kThreads) s_lens[i] = args.lens[i];
+    __syncthreads();
+    a.lens = s_lens;
+  }
+  constexpr int kVals = kScanVals;
   const int S = a.num_seqs;
   const int per = ceil_div(S, kThreads);
   const int i0 = min(S, threadIdx.x * per), i1 = min(S, i0 + per);
@@ -356,6 +405,15 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
   int part = a.part_size;
   int cnt[kVals], excl[kVals], all[kVals];
   plan_count(a, part, i0, i1, j0, j1, cnt);
+  // uniform: the candidate for an even batch (no shared prefixes; lengths
+  // whose block count fits an int)
+  const int part2 = static_cast<int>(
+      min(static_cast<int64_t>(part) * 2, static_cast<int64_t>(a.max_blocks) * kBlock));
+  const bool even_try = a.even_doubling && a.num_groups == 0 && part < a.max_len &&
+                        part2 > part &&
+                        static_cast<int64_t>(S) * ceil_div(a.max_len, kBlock) < (1 << 30);
+  cnt[kEvenItems] = cnt[kEvenRounds] = 0;
+  if (even_try) even_counts(a, part2, i0, i1, &cnt[kEvenItems], &cnt[kEvenRounds]);
   block_scan<kVals>(cnt, excl, all, wave_tot);
   int listed = all[kFull];
 #pragma unroll
@@ -364,6 +422,13 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
     __syncthreads();  // the scan's totals are read before they are rewritten
     part = plan_partition(a, i0, i1, j0, j1, wave_tot);
     plan_count(a, part, i0, i1, j0, j1, cnt);
+    cnt[kEvenItems] = cnt[kEvenRounds] = 0;
+    block_scan<kVals>(cnt, excl, all, wave_tot);
+  } else if (even_try && even_batch(a, part2, all[kEvenItems], all[kEvenRounds])) {
+    __syncthreads();
+    part = part2;
+    plan_count(a, part, i0, i1, j0, j1, cnt);
+    cnt[kEvenItems] = cnt[kEvenRounds] = 0;
     block_scan<kVals>(cnt, excl, all, wave_tot);
   }
   // item positions: full partitions from 0, then classes in order
@@ -430,7 +495,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, int* wave_tot) {
 }
 
 __global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanArgs a) {
-  __shared__ int wave_tot[kWaves * kPlanVals];
+  __shared__ int wave_tot[kWaves * kScanVals];
   plan_body(a, wave_tot);
 }
 
@@ -454,7 +519,7 @@ __host__ __device__ constexpr int step_batch() {
 
 template <typename W, bool kNT>
 __global__ __launch_bounds__(kThreads) void decode_prep_kernel(PlanArgs a, W w) {
-  __shared__ int wave_tot[kWaves * kPlanVals];
+  __shared__ int wave_tot[kWaves * kScanVals];
   if (blockIdx.x == 0) {
     plan_body(a, wave_tot);
     return;
@@ -956,6 +1021,7 @@ bool resolve_split(int partition_size, int num_seqs, int hkv, int max_len, Split
   out->np = max(1, (max_len + ps - 1) / ps);
   out->long_context = max_len >= kLongContext;
   out->max_len = max_len;
+  out->auto_part = partition_size == PA_PARTITION_AUTO;
   return true;
 }
 
@@ -1049,6 +1115,10 @@ pa_status launch(const void* q, const void* k_cache, const void* v_cache, const 
                 fused_merge ? num_seqs * hkv * head_blocks : 0,  // one per (sequence, head group)
                 item_grid, waves};
     pa.capacity = cap;
+    pa.heads = heads;
+    // the fused merge takes any partition; the merge kernel of the other
+    // paths reads partitions of sp.part, and shared prefixes keep theirs
+    pa.even_doubling = fused_merge && sp.auto_part && !sh;
     if (sh) {
       pa.pfx_seqs = sh->seqs;
       pa.pfx_start = sh->start;

@@ -347,6 +347,22 @@ __device__ __forceinline__ void combine_waves(const float* comb, int nhm, int D,
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave from DPP moves, which are
+// ALU operations, where a shuffle is a round trip through the LDS crossbar:
+// Hillis-Steele steps of 1, 2, 4 and 8 lanes within each row of 16, then
+// lane 15 of rows 0 and 2 added into rows 1 and 3 (row_bcast:15) and lane 31
+// into rows 2 and 3 (row_bcast:31).  A lane whose source lies outside its
+// row, or whose row the mask leaves out, adds the 0 passed as the old value.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+  return x;
+}
+
 // Exclusive scan over the 256 threads of a work-group of kVals counters at
 // once; all[] receives the totals.  `tot` is LDS of kWaves * kVals ints.
 template <int kVals>
@@ -355,12 +371,7 @@ __device__ __forceinline__ void block_scan(const int* cnt, int* excl, int* all, 
   const int wv = threadIdx.x / kWave;
 #pragma unroll
   for (int c = 0; c < kVals; ++c) {
-    int x = cnt[c];
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
+    const int x = wave_inclusive_sum(cnt[c]);
     excl[c] = x - cnt[c];
     if (lane == kWave - 1) tot[wv * kVals + c] = x;
   }
@@ -395,6 +406,7 @@ struct Split {
   bool long_context = false;  // the longest context has >= 16K positions
   int waves = kItemWaves;     // waves per work-group of the matrix-core items kernels
   int max_len = 0;            // the call's bound on every length
+  bool auto_part = false;     // part is the automatic choice (the plan may double it)
 };
 
 // Shared prefixes of a decode call: groups of sequences whose tables begin

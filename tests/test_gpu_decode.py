@@ -138,6 +138,22 @@ def test_many_sequences():
     assert_close(db.out_bits(), ref, "bf16", "1100 sequences")
 
 
+@pytest.mark.parametrize("config,expect", [("2", 2048), ("5", 4096), ("3", 1024)])
+def test_even_batches_double_the_automatic_partition(config, expect):
+    # the plan doubles an automatic partition for a batch of evenly long
+    # sequences (8B layer 1024 -> 2048, 32K context 2048 -> 4096) and keeps
+    # it for the skewed mixed batch; a partition the caller passes is kept.
+    # The outputs at the doubled partition are checked against the oracle by
+    # the full-size tests.
+    print(f"[gpu] even-batch partition, workload {config}", flush=True)
+    db = runner.DeviceBatch(workloads.make(config))
+    db.prefill()
+    db.step()
+    assert pa.last_plan_partition() == expect
+    db.step(partition_size=1024)
+    assert pa.last_plan_partition() == 1024
+
+
 def test_stale_workspace_does_not_matter():
     # the workspace is scratch: a NaN-filled one and a reused one give the same bits
     import torch
