@@ -138,6 +138,17 @@ def test_many_sequences():
     assert_close(db.out_bits(), ref, "bf16", "1100 sequences")
 
 
+@pytest.mark.parametrize("partition_size", [pa.PARTITION_AUTO, 16])
+def test_more_sequences_than_the_plan_stages_in_lds(partition_size):
+    # above 4096 sequences the plan reads the lengths from global memory
+    # instead of its LDS copy, 20 sequences per plan thread
+    print(f"[gpu] 5000 sequences P={partition_size}", flush=True)
+    lens = (np.arange(5000) * 7 % 61) + 1
+    w = workloads.make_custom(lens, hq=4, hkv=1, d=64, dtype="bf16", seed=11)
+    db, ref = _run_small(w, partition_size)
+    assert_close(db.out_bits(), ref, "bf16", "5000 sequences")
+
+
 @pytest.mark.parametrize("config,expect", [("2", 2048), ("5", 4096), ("3", 1024)])
 def test_even_batches_double_the_automatic_partition(config, expect):
     # the plan doubles an automatic partition for a batch of evenly long
