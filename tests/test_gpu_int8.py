@@ -183,7 +183,7 @@ def _oracle_full(config):
     return _ORACLE[config]
 
 
-@pytest.mark.parametrize("config", [3, 5])
+@pytest.mark.parametrize("config", [2, 3, 5])
 def test_full_size_every_output_and_code_against_oracle(config):
     print(f"[gpu] int8 full-size workload {config}: every output and every code", flush=True)
     w, db = _full(config)
