@@ -277,7 +277,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 
 /* The partition size PA_PARTITION_AUTO resolves to for these sizes
  * (PA_PARTITION_NONE or a positive multiple of 16); dtype PA_I8 gives the
- * choice of pa_paged_attention_decode_int8. */
+ * choice of pa_paged_attention_decode_int8.  The decode may double it once
+ * for a batch of evenly long sequences (see pa_paged_attention_decode). */
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
 
@@ -306,7 +307,12 @@ int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 sequence);
  *                 PA_PARTITION_NONE: one pass over each whole sequence;
  *                 PA_PARTITION_AUTO: the partition size
- *                 pa_decode_auto_partition gives
+ *                 pa_decode_auto_partition gives; on the matrix-core path
+ *                 the device's work-list pass doubles it once for a batch of
+ *                 evenly long sequences: when at twice the size the list
+ *                 still holds >= 512 (item, head group) work-groups and its
+ *                 longest item streams at most 1.5 x the blocks per wave of
+ *                 the mean item (the workspace for the given size covers it)
  *   workspace     device, >= pa_decode_workspace_bytes(...) bytes, 256-byte
  *                 aligned; scratch that each call rewrites before reading.
  *                 Calls that share a workspace must not overlap (same stream,
